@@ -1,0 +1,415 @@
+"""Benchmark of IBP batched gather + decompress on one MI355X.
+
+A step is one gather + decompress launch (participation scan, payload fetch,
+decode, dense store) over one fresh batch of ids drawn from the workload's id
+law.  The default workload is the sparse GNN feature table (2^20 rows of 1,433
+fp32, 1 KB chunks, Mask from a 1 % sample, 8,192 uniform ids per batch) held
+compressed in pinned host memory: every step reads the compressed payloads
+over PCIe with GPU-initiated loads.
+
+Prints ONE JSON line.  `value` is decompressed GB/s (ids x tensor bytes per
+second of wall time over the timed steps, inputs already resident).  Extra
+objects: `roofline` (the gather kernel against the host-link peak),
+`cpu_baseline` (the CPU oracle on a bounded sample of the same batches),
+`hbm_path` (the same kernel reading a compressed cache in HBM), probes of the
+link, and the transfer speedup over an uncompressed GPU gather of the same
+rows ([JH] Table 1 discussion: transfer speedup against plain transfers).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sparse_gnn]
+       [--hbm-workload dense_gnn|dlrm_1k|none] [--host-flags default|coherent|noncoherent]
+       [--no-cpu-baseline] [--threshold T]
+"""
+import argparse
+import json
+import os
+import platform
+import statistics
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PCIE5_X16_GBPS = 63.0      # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes x 128/130 / 8
+HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="sparse_gnn")
+    p.add_argument("--hbm-workload", default="dense_gnn")
+    p.add_argument("--host-flags", default="default", choices=["default", "coherent", "noncoherent"])
+    p.add_argument("--threshold", type=float, default=None)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+def host_info():
+    info = {"cpu": platform.processor() or "", "cores": os.cpu_count(),
+            "affinity": len(os.sched_getaffinity(0))}
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            k, _, v = line.partition(":")
+            if k.strip() in ("Model name", "Socket(s)", "NUMA node(s)", "Thread(s) per core"):
+                info[k.strip()] = v.strip()
+    except Exception:
+        pass
+    return info
+
+
+class Timer:
+    """HIP events on torch's current stream (the stream the kernels use)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, s):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.append((s, e))
+
+    def ms(self):
+        self.torch.cuda.synchronize()
+        return [s.elapsed_time(e) for s, e in self.pairs]
+
+
+class Table:
+    """One workload compressed on the GPU into a store (pinned host or HBM)."""
+
+    def __init__(self, torch, ibp, W, w, T, where, host_flags, keep_raw=True):
+        import numpy as np
+        self.w, self.T, self.where = w, T, where
+        B, C, S, N = w.tensor_bytes, w.chunk_bytes, w.slot_bytes, w.n_tensors
+        self.n_c = ibp.num_chunks(B, C)
+        t0 = time.time()
+        # raw rows in pinned host memory, slot-strided (also the raw-gather source)
+        self.raw = ibp.HostBuffer(N * S, host_flags)
+        view = self.raw.array.reshape(N, S)
+        W.rows(w, 0, N, out=view[:, :B])
+        log(f"{w.key}: generated {N} x {B} B in {time.time() - t0:.1f} s")
+        # metadata from the sample (rows read by the GPU from pinned memory)
+        sid = W.sample_ids(w)
+        n_s = N if sid is None else len(sid)
+        d_sid = None if sid is None else torch.from_numpy(sid).cuda()
+        self.mask = torch.zeros(B // 4, dtype=torch.int32, device="cuda")
+        self.bitval = torch.zeros_like(self.mask)
+        counts = torch.zeros(8 * B, dtype=torch.int32, device="cuda")
+        ev = Timer(torch)
+        s = ev.start()
+        ibp.build_metadata(self.raw, S, d_sid, n_s, B, T, self.mask, self.bitval, counts)
+        ev.stop(s)
+        # compress into the store
+        if where == "pinned":
+            self.store = ibp.HostBuffer(N * S, host_flags)
+        else:
+            self.store = torch.empty(N * S, dtype=torch.uint8, device="cuda")
+        self.part = torch.zeros((N * self.n_c + 31) // 32, dtype=torch.int32, device="cuda")
+        self.lengths = torch.zeros(N, dtype=torch.int32, device="cuda")
+        s = ev.start()
+        ibp.compress(self.raw, S, N, 0, N, B, C, self.mask, self.bitval, self.store, S, self.part,
+                     self.lengths)
+        ev.stop(s)
+        self.offsets = None
+        self.cache = None
+        self.store_bytes = N * S
+        if where == "hbm":
+            # compacted cache in HBM
+            self.offsets = torch.zeros(N + 1, dtype=torch.int64, device="cuda")
+            s = ev.start()
+            ibp.compact_offsets(self.lengths, N, self.offsets)
+            ev.stop(s)
+            total = int(self.offsets[-1].item())
+            self.cache = torch.empty(max(total, 16), dtype=torch.uint8, device="cuda")
+            s = ev.start()
+            ibp.compact(self.store, S, N, self.offsets, self.cache, total)
+            ev.stop(s)
+            self.store_bytes = total
+            del self.store
+            self.store = self.cache
+        ms = ev.ms()
+        self.meta_ms, self.compress_ms = ms[0], ms[1]
+        self.compact_ms = sum(ms[2:]) if where == "hbm" else None
+        self.len_host = self.lengths.cpu().numpy().view(np.uint32)
+        self.mask_host = self.mask.cpu().numpy().view(np.uint32)
+        self.bitval_host = self.bitval.cpu().numpy().view(np.uint32)
+        if not keep_raw:
+            self.raw.free()
+            self.raw = None
+        log(f"{w.key}: metadata {self.meta_ms:.2f} ms, compress {self.compress_ms:.2f} ms, "
+            f"mean payload {self.len_host.mean() / B:.4f} of {B} B")
+
+    def gather(self, ibp, d_ids, n_ids, out):
+        w = self.w
+        ibp.gather_decompress(self.store, self.store_bytes, w.slot_bytes, self.offsets, self.part,
+                              w.n_tensors, d_ids, n_ids, w.tensor_bytes, w.chunk_bytes, self.mask,
+                              self.bitval, out)
+
+
+def time_gather(torch, ibp, table, batches, warmup, steps, out, raw_baseline=False):
+    """Warm-up, then `steps` launches bracketed by synchronisations.
+    Returns (wall seconds, per-launch kernel ms list)."""
+    w = table.w
+    n = w.batch
+    for k in range(warmup):
+        d = batches[k]
+        if raw_baseline:
+            ibp.raw_gather(table.raw, w.slot_bytes, w.n_tensors, d, n, w.tensor_bytes, out)
+        else:
+            table.gather(ibp, d, n, out)
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    t0 = time.perf_counter()
+    for k in range(warmup, warmup + steps):
+        d = batches[k]
+        s = tm.start()
+        if raw_baseline:
+            ibp.raw_gather(table.raw, w.slot_bytes, w.n_tensors, d, n, w.tensor_bytes, out)
+        else:
+            table.gather(ibp, d, n, out)
+        tm.stop(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, tm.ms()
+
+
+def check_rows(table, ids_host, out):
+    """The gathered rows are the original rows (lossless), on a sample."""
+    import numpy as np
+    w = table.w
+    got = out.cpu().numpy().view(np.uint8).reshape(-1, w.tensor_bytes)
+    view = table.raw.array.reshape(w.n_tensors, w.slot_bytes)[:, :w.tensor_bytes]
+    pick = np.linspace(0, len(ids_host) - 1, 64).astype(np.int64)
+    if not (got[pick] == view[ids_host[pick]]).all():
+        raise SystemExit("bench: gathered rows differ from the original rows")
+
+
+def probes(torch, ibp, host_flags):
+    """Host-link read peak: DMA copy and zero-copy streaming read of 1 GiB."""
+    GiB = 1 << 30
+    src = torch.empty(GiB, dtype=torch.uint8).pin_memory()
+    dst = torch.empty(GiB, dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        dst.copy_(src, non_blocking=True)
+    tm = Timer(torch)
+    for _ in range(10):
+        s = tm.start()
+        dst.copy_(src, non_blocking=True)
+        tm.stop(s)
+    dma = GiB / (statistics.median(tm.ms()) * 1e-3) / 1e9
+    del src
+    hb = ibp.HostBuffer(GiB, host_flags)
+    hb.array[:] = 1
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        ibp.stream_read(hb, GiB, 0x9E3779B9, sink)
+    tm = Timer(torch)
+    for _ in range(10):
+        s = tm.start()
+        ibp.stream_read(hb, GiB, 0x9E3779B9, sink)
+        tm.stop(s)
+    zc = GiB / (statistics.median(tm.ms()) * 1e-3) / 1e9
+    hb.free()
+    # HBM streaming read, 4 GiB (far beyond the 256 MB last-level cache)
+    big = torch.ones(4 * GiB, dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        ibp.stream_read(big, 4 * GiB, 0x9E3779B9, sink)
+    tm = Timer(torch)
+    for _ in range(10):
+        s = tm.start()
+        ibp.stream_read(big, 4 * GiB, 0x9E3779B9, sink)
+        tm.stop(s)
+    hbm = 4 * GiB / (statistics.median(tm.ms()) * 1e-3) / 1e9
+    del big, dst
+    torch.cuda.empty_cache()
+    return {"h2d_dma_GBps": round(dma, 2), "h2d_zero_copy_read_GBps": round(zc, 2),
+            "hbm_stream_read_GBps": round(hbm, 1)}
+
+
+def cpu_baseline(table, batches_host, seconds):
+    """The oracle's gather + decompress of the same batches from the same
+    (host-resident) store, timed on the host cores; bounded to ~`seconds`."""
+    import numpy as np
+    from oracle import oracle as O
+    w = table.w
+    part = table.part.cpu().numpy().view(np.uint32)
+    if table.where == "pinned":
+        store = table.store.array
+        offs = None
+    else:
+        store = table.cache.cpu().numpy()
+        offs = table.offsets.cpu().numpy().view(np.uint64)
+    out = np.empty((w.batch, w.tensor_bytes), np.uint8)
+    rows = 0
+    t0 = time.perf_counter()
+    k = 0
+    while True:
+        ids = batches_host[k % len(batches_host)]
+        O.gather_decompress(store, part, w.n_tensors, ids, w.tensor_bytes, w.chunk_bytes,
+                            table.mask_host, table.bitval_host, slot_bytes=w.slot_bytes,
+                            offsets=offs, out=out)
+        rows += len(ids)
+        k += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or k >= 4 * len(batches_host):
+            break
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(rows * w.tensor_bytes / el / 1e9, 4), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"{k} batches of {w.batch} ids ({rows} rows) of the timed id sequence, "
+                      f"{el:.1f} s"}
+
+
+def measure_workload(torch, ibp, W, key, T, where, host_flags, steps, warmup, with_raw):
+    import numpy as np
+    w = W.WORKLOADS[key]
+    T = w.threshold if T is None else T
+    table = Table(torch, ibp, W, w, T, where, host_flags, keep_raw=True)
+    nb = warmup + steps
+    ids_host = [W.batch_ids(w, k) for k in range(nb)]
+    batches = [torch.from_numpy(i).cuda() for i in ids_host]
+    out = torch.empty(w.batch * w.tensor_bytes, dtype=torch.uint8, device="cuda")
+    wall, ms = time_gather(torch, ibp, table, batches, warmup, steps, out)
+    check_rows(table, ids_host[-1], out)
+    comp = [int(table.len_host[i].sum()) for i in ids_host[warmup:]]
+    res = {"table": table, "ids_host": ids_host, "wall": wall, "kernel_ms": ms,
+           "comp_bytes": comp, "T": T}
+    if with_raw:
+        rwall, rms = time_gather(torch, ibp, table, batches, warmup, steps, out, raw_baseline=True)
+        res["raw_kernel_ms"] = rms
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the gathered tensors are independent, see the design notes on sharding)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from host_transfer_amd import ibp
+    from host_transfer_amd import workloads as W
+
+    torch.cuda.set_device(0)
+    flags = {"default": ibp.HOST_DEFAULT, "coherent": ibp.HOST_COHERENT,
+             "noncoherent": ibp.HOST_NONCOHERENT}[args.host_flags]
+    log(f"device {torch.cuda.get_device_name(0)}; host {host_info()}")
+    pr = probes(torch, ibp, flags)
+    log(f"probes {pr}")
+
+    # --- headline: the workload from pinned host memory
+    key = args.workload
+    m = measure_workload(torch, ibp, W, key, args.threshold, "pinned", flags, args.steps,
+                         args.warmup, with_raw=True)
+    w, table = W.WORKLOADS[key], m["table"]
+    K = args.steps
+    dense_bytes = w.batch * w.tensor_bytes
+    value = dense_bytes * K / m["wall"] / 1e9
+    kern_ms = statistics.mean(m["kernel_ms"])
+    comp = statistics.mean(m["comp_bytes"])
+    achieved = comp / (kern_ms * 1e-3) / 1e9
+    raw_ms = statistics.mean(m["raw_kernel_ms"])
+    link_peak = max(pr["h2d_dma_GBps"], pr["h2d_zero_copy_read_GBps"])
+    log(f"{key}: {value:.1f} GB/s decompressed, kernel {kern_ms * 1e3:.1f} us, "
+        f"{achieved:.1f} GB/s compressed over the link, raw gather {raw_ms * 1e3:.1f} us")
+
+    result = {
+        "metric": "decompressed GB/s for batched gather+decompress; % of PCIe/HBM roofline",
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(m["wall"] * 1e3 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic (seeded generators shaped like the pages' workloads)",
+        "config": {
+            "workload": f"{key}: {w.n_tensors} tensors x {w.tensor_bytes} B, {w.chunk_bytes} B "
+                        f"chunks, T={m['T']}, Mask from "
+                        f"{'all' if w.sample_fraction >= 1 else f'{w.sample_fraction:.0%}'} of "
+                        f"the tensors, store in pinned host memory ({args.host_flags}), "
+                        f"{w.batch} ids per batch ({w.id_law})",
+            "batch": w.batch, "tensor_bytes": w.tensor_bytes, "chunk_bytes": w.chunk_bytes,
+            "store": "pinned-host", "host_flags": args.host_flags,
+        },
+        "roofline": {
+            "bound": "pcie",
+            "achieved": round(achieved, 3),
+            "peak": PCIE5_X16_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PCIE5_X16_GBPS, 4),
+            "traffic": None,
+            "peak_measured": round(link_peak, 2),
+            "frac_of_measured": round(achieved / link_peak, 4),
+            "kernel": "k_gather_decompress",
+            "kernel_us": round(kern_ms * 1e3, 2),
+            "bytes_per_launch": round(comp, 1),
+        },
+        "compression": {
+            "mean_payload_over_tensor": round(float(table.len_host.mean()) / w.tensor_bytes, 5),
+            "batch_payload_over_dense": round(comp / dense_bytes, 5),
+        },
+        "transfer_speedup_vs_raw_gpu_gather": round(raw_ms / kern_ms, 3),
+        "raw_gather_GBps": round(dense_bytes / (raw_ms * 1e-3) / 1e9, 2),
+        "offline": {"metadata_ms": round(table.meta_ms, 3),
+                    "compress_ms": round(table.compress_ms, 3)},
+        "probes": pr,
+        "host": host_info(),
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(table, m["ids_host"][args.warmup:], args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    table.raw.free()
+    table.store.free()
+    del table, m
+    torch.cuda.empty_cache()
+
+    # --- the same kernel on a compressed cache in HBM
+    if args.hbm_workload != "none":
+        hk = args.hbm_workload
+        h = measure_workload(torch, ibp, W, hk, None, "hbm", flags, args.steps, args.warmup,
+                             with_raw=False)
+        hw, ht = W.WORKLOADS[hk], h["table"]
+        hk_ms = statistics.mean(h["kernel_ms"])
+        hbytes = statistics.mean(h["comp_bytes"]) + hw.batch * (hw.tensor_bytes + 16)
+        ach = hbytes / (hk_ms * 1e-3) / 1e9
+        result["hbm_path"] = {
+            "workload": f"{hk}: {hw.n_tensors} x {hw.tensor_bytes} B compacted cache "
+                        f"({ht.store_bytes / 1e9:.2f} GB) in HBM, {hw.batch} ids ({hw.id_law})",
+            "decompressed_GBps": round(hw.batch * hw.tensor_bytes / (hk_ms * 1e-3) / 1e9, 2),
+            "kernel_us": round(hk_ms * 1e3, 2),
+            "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
+                         "frac_of_measured": round(ach / pr["hbm_stream_read_GBps"], 4)},
+            "compact_ms": round(ht.compact_ms, 3),
+        }
+        ht.raw.free()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

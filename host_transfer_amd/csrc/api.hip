@@ -1,0 +1,304 @@
+// api.hip -- the extern "C" entry points of libibp.so (include/ibp.h).
+// Validates every argument before any HIP call, then hands over to the
+// launchers of the kernel files.  Errors are reported through the return code
+// and a thread-local message; nothing throws across the ABI.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <atomic>
+#include <mutex>
+
+#include "ibp.h"
+#include "ibp_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return IBP_OK;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(IBP_ERR_HIP, "%s: HIP error %d (%s)", where, (int)e, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Confirms a usable current device before anything is launched.
+int require_device(const char* where) {
+  ibp::DeviceInfo di;
+  hipError_t e = ibp::device_info(&di);
+  if (e != hipSuccess) return hip_fail(e, where);
+  return IBP_OK;
+}
+
+int check_tensor(uint32_t tensor_bytes) {
+  if (tensor_bytes == 0 || tensor_bytes % 4 != 0 || tensor_bytes > IBP_MAX_TENSOR_BYTES)
+    return fail(IBP_ERR_SIZE, "tensor_bytes %u must be a multiple of 4 in [4, %u]", tensor_bytes,
+                IBP_MAX_TENSOR_BYTES);
+  return IBP_OK;
+}
+
+int check_chunk(uint32_t chunk_bytes) {
+  if (chunk_bytes != 256 && chunk_bytes != 1024 && chunk_bytes != 4096)
+    return fail(IBP_ERR_CHUNK, "chunk_bytes %u must be 256, 1024 or 4096", chunk_bytes);
+  return IBP_OK;
+}
+
+// Bitmap words for n tensors of n_c chunks, or 0 on overflow.
+uint64_t bitmap_bits(uint64_t n_tensors, uint32_t n_c) {
+  if (n_tensors > (UINT64_MAX - 31) / n_c) return 0;
+  return n_tensors * n_c;
+}
+
+struct DevCache {
+  std::once_flag once;
+  ibp::DeviceInfo info;
+  hipError_t err;
+};
+constexpr int kMaxDevices = 64;
+DevCache g_dev[kMaxDevices];
+
+}  // namespace
+
+namespace ibp {
+
+hipError_t device_info(DeviceInfo* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  DevCache& c = g_dev[dev];
+  std::call_once(c.once, [&] {
+    c.info.device = dev;
+    c.err = hipDeviceGetAttribute(&c.info.cus, hipDeviceAttributeMultiprocessorCount, dev);
+    int lds = 0;
+    if (c.err == hipSuccess)
+      c.err = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    c.info.lds_per_block = (size_t)lds;
+  });
+  *out = c.info;
+  return c.err;
+}
+
+Geometry make_geometry(uint32_t tensor_bytes, uint32_t chunk_bytes) {
+  Geometry g;
+  g.tensor_bytes = tensor_bytes;
+  g.chunk_bytes = chunk_bytes;
+  g.W = tensor_bytes / 4;
+  g.n_c = (tensor_bytes + chunk_bytes - 1) / chunk_bytes;
+  g.wpc_log2 = 0;
+  while ((1u << g.wpc_log2) < chunk_bytes / 4) ++g.wpc_log2;
+  g.last_bits = 8u * (tensor_bytes - (g.n_c - 1) * chunk_bytes);
+  // smallest group (threads per tensor) that keeps <= 8 words per thread
+  g.group = 64;
+  while (g.group * 8 < g.W) g.group *= 2;
+  g.J = (g.W + g.group - 1) / g.group;
+  g.groups = g.group == 64 ? 4 : 1;
+  return g;
+}
+
+}  // namespace ibp
+
+extern "C" {
+
+int ibp_version(void) { return IBP_VERSION; }
+
+const char* ibp_last_error(void) { return g_err; }
+
+int ibp_num_chunks(uint32_t tensor_bytes, uint32_t chunk_bytes) {
+  int r = check_tensor(tensor_bytes);
+  if (r) return r;
+  if ((r = check_chunk(chunk_bytes))) return r;
+  ok();
+  return (int)((tensor_bytes + chunk_bytes - 1) / chunk_bytes);
+}
+
+int ibp_build_metadata(const void* rows, uint64_t row_stride, const int64_t* sample_ids,
+                       uint64_t n_samples, uint32_t tensor_bytes, double threshold,
+                       uint32_t* mask, uint32_t* bitval, uint32_t* counts, void* stream) {
+  if (!rows || !mask || !bitval || !counts)
+    return fail(IBP_ERR_NULL, "ibp_build_metadata: rows, mask, bitval and counts are required");
+  int r = check_tensor(tensor_bytes);
+  if (r) return r;
+  if (n_samples == 0 || n_samples > 0xFFFFFFFFull)
+    return fail(IBP_ERR_SIZE, "ibp_build_metadata: n_samples %llu must be in [1, 2^32-1]",
+                (unsigned long long)n_samples);
+  if (row_stride < tensor_bytes || row_stride % 4 != 0)
+    return fail(IBP_ERR_SIZE, "ibp_build_metadata: row_stride %llu must be >= tensor_bytes and %% 4",
+                (unsigned long long)row_stride);
+  if (!(threshold >= 0.5 && threshold <= 1.0))
+    return fail(IBP_ERR_THRESHOLD, "ibp_build_metadata: threshold must be in [0.5, 1]");
+  if (!aligned(rows, 4) || !aligned(mask, 4) || !aligned(bitval, 4) || !aligned(counts, 4) ||
+      (sample_ids && !aligned(sample_ids, 8)))
+    return fail(IBP_ERR_ALIGN, "ibp_build_metadata: misaligned pointer");
+  // cutoff m = ceil(T * n) in binary64
+  const uint64_t cutoff = (uint64_t)ceil(threshold * (double)n_samples);
+  if ((r = require_device("ibp_build_metadata"))) return r;
+  hipError_t e = ibp::launch_build_metadata((const uint8_t*)rows, row_stride, sample_ids,
+                                            n_samples, tensor_bytes, cutoff, mask, bitval, counts,
+                                            (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "ibp_build_metadata");
+  return ok();
+}
+
+int ibp_compress(const void* rows, uint64_t row_stride, uint64_t n_rows, uint64_t first_tensor,
+                 uint64_t n_tensors, uint32_t tensor_bytes, uint32_t chunk_bytes,
+                 const uint32_t* mask, const uint32_t* bitval, void* store, uint64_t slot_bytes,
+                 uint32_t* part_bits, uint32_t* lengths, void* stream) {
+  if (!rows || !mask || !bitval || !store || !part_bits)
+    return fail(IBP_ERR_NULL, "ibp_compress: rows, mask, bitval, store and part_bits are required");
+  int r = check_tensor(tensor_bytes);
+  if (r) return r;
+  if ((r = check_chunk(chunk_bytes))) return r;
+  if (first_tensor > n_tensors || n_rows > n_tensors - first_tensor)
+    return fail(IBP_ERR_SIZE, "ibp_compress: first_tensor + n_rows exceeds n_tensors");
+  if (row_stride < tensor_bytes || row_stride % 4 != 0)
+    return fail(IBP_ERR_SIZE, "ibp_compress: row_stride must be >= tensor_bytes and %% 4");
+  if (slot_bytes < tensor_bytes || slot_bytes % 16 != 0)
+    return fail(IBP_ERR_SIZE, "ibp_compress: slot_bytes must be >= tensor_bytes and %% 16");
+  const uint32_t n_c = (tensor_bytes + chunk_bytes - 1) / chunk_bytes;
+  if (n_tensors && (!bitmap_bits(n_tensors, n_c) || n_tensors > UINT64_MAX / slot_bytes))
+    return fail(IBP_ERR_SIZE, "ibp_compress: n_tensors too large");
+  if (!aligned(rows, 4) || !aligned(mask, 4) || !aligned(bitval, 4) || !aligned(store, 16) ||
+      !aligned(part_bits, 4) || (lengths && !aligned(lengths, 4)))
+    return fail(IBP_ERR_ALIGN, "ibp_compress: misaligned pointer");
+  if ((r = require_device("ibp_compress"))) return r;
+  const ibp::Geometry g = ibp::make_geometry(tensor_bytes, chunk_bytes);
+  hipError_t e = ibp::launch_compress(g, (const uint8_t*)rows, row_stride, n_rows, first_tensor,
+                                      mask, bitval, (uint8_t*)store, slot_bytes, part_bits,
+                                      lengths, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "ibp_compress");
+  return ok();
+}
+
+int ibp_compact_offsets(const uint32_t* lengths, uint64_t n_tensors, uint64_t* offsets,
+                        void* stream) {
+  if (!lengths || !offsets)
+    return fail(IBP_ERR_NULL, "ibp_compact_offsets: lengths and offsets are required");
+  if (!aligned(lengths, 4) || !aligned(offsets, 8))
+    return fail(IBP_ERR_ALIGN, "ibp_compact_offsets: misaligned pointer");
+  int r;
+  if ((r = require_device("ibp_compact_offsets"))) return r;
+  hipError_t e = ibp::launch_compact_offsets(lengths, n_tensors, offsets, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "ibp_compact_offsets");
+  return ok();
+}
+
+int ibp_compact(const void* store, uint64_t slot_bytes, uint64_t n_tensors,
+                const uint64_t* offsets, void* cache, uint64_t cache_bytes, void* stream) {
+  if (!store || !offsets || !cache)
+    return fail(IBP_ERR_NULL, "ibp_compact: store, offsets and cache are required");
+  if (slot_bytes == 0 || slot_bytes % 16 != 0)
+    return fail(IBP_ERR_SIZE, "ibp_compact: slot_bytes must be a positive multiple of 16");
+  if (n_tensors > UINT64_MAX / slot_bytes)
+    return fail(IBP_ERR_SIZE, "ibp_compact: n_tensors too large");
+  if (!aligned(store, 16) || !aligned(cache, 16) || !aligned(offsets, 8))
+    return fail(IBP_ERR_ALIGN, "ibp_compact: misaligned pointer");
+  int r;
+  if ((r = require_device("ibp_compact"))) return r;
+  hipError_t e = ibp::launch_compact((const uint8_t*)store, slot_bytes, n_tensors, offsets,
+                                     (uint8_t*)cache, cache_bytes, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "ibp_compact");
+  return ok();
+}
+
+int ibp_gather_decompress(const void* store, uint64_t store_bytes, uint64_t slot_bytes,
+                          const uint64_t* offsets, const uint32_t* part_bits, uint64_t n_tensors,
+                          const int64_t* ids, uint64_t n_ids, uint32_t tensor_bytes,
+                          uint32_t chunk_bytes, const uint32_t* mask, const uint32_t* bitval,
+                          void* out, void* stream) {
+  if (!store || !part_bits || !ids || !mask || !bitval || !out)
+    return fail(IBP_ERR_NULL,
+                "ibp_gather_decompress: store, part_bits, ids, mask, bitval and out are required");
+  int r = check_tensor(tensor_bytes);
+  if (r) return r;
+  if ((r = check_chunk(chunk_bytes))) return r;
+  const uint32_t n_c = (tensor_bytes + chunk_bytes - 1) / chunk_bytes;
+  if (n_tensors && !bitmap_bits(n_tensors, n_c))
+    return fail(IBP_ERR_SIZE, "ibp_gather_decompress: n_tensors too large");
+  if (!offsets) {
+    if (slot_bytes < tensor_bytes || slot_bytes % 16 != 0)
+      return fail(IBP_ERR_SIZE,
+                  "ibp_gather_decompress: slot_bytes must be >= tensor_bytes and %% 16");
+    if (n_tensors > UINT64_MAX / slot_bytes || store_bytes < n_tensors * slot_bytes)
+      return fail(IBP_ERR_SIZE, "ibp_gather_decompress: store_bytes < n_tensors * slot_bytes");
+  }
+  if (n_ids > UINT64_MAX / tensor_bytes)
+    return fail(IBP_ERR_SIZE, "ibp_gather_decompress: n_ids too large");
+  if (!aligned(store, 16) || !aligned(out, 16) || !aligned(ids, 8) || !aligned(mask, 4) ||
+      !aligned(bitval, 4) || !aligned(part_bits, 4) || (offsets && !aligned(offsets, 8)))
+    return fail(IBP_ERR_ALIGN, "ibp_gather_decompress: misaligned pointer");
+  if ((r = require_device("ibp_gather_decompress"))) return r;
+  const ibp::Geometry g = ibp::make_geometry(tensor_bytes, chunk_bytes);
+  hipError_t e = ibp::launch_gather(g, (const uint8_t*)store, store_bytes, slot_bytes, offsets,
+                                    part_bits, n_tensors, ids, n_ids, mask, bitval,
+                                    (uint32_t*)out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "ibp_gather_decompress");
+  return ok();
+}
+
+int ibp_host_alloc(uint64_t bytes, unsigned flags, void** ptr) {
+  if (!ptr) return fail(IBP_ERR_NULL, "ibp_host_alloc: ptr is required");
+  *ptr = nullptr;
+  if (bytes == 0) return fail(IBP_ERR_SIZE, "ibp_host_alloc: bytes must be > 0");
+  if (flags > IBP_HOST_NONCOHERENT) return fail(IBP_ERR_FLAGS, "ibp_host_alloc: unknown flags");
+  unsigned hf = hipHostMallocMapped | hipHostMallocPortable;
+  if (flags == IBP_HOST_COHERENT) hf |= hipHostMallocCoherent;
+  if (flags == IBP_HOST_NONCOHERENT) hf |= hipHostMallocNonCoherent;
+  hipError_t e = hipHostMalloc(ptr, (size_t)bytes, hf);
+  if (e != hipSuccess) {
+    *ptr = nullptr;
+    return hip_fail(e, "ibp_host_alloc");
+  }
+  return ok();
+}
+
+int ibp_host_free(void* ptr) {
+  if (!ptr) return ok();
+  hipError_t e = hipHostFree(ptr);
+  if (e != hipSuccess) return hip_fail(e, "ibp_host_free");
+  return ok();
+}
+
+int ibp_raw_gather(const void* src, uint64_t row_stride, uint64_t n_rows, const int64_t* ids,
+                   uint64_t n_ids, uint32_t row_bytes, void* out, void* stream) {
+  if (!src || !ids || !out) return fail(IBP_ERR_NULL, "ibp_raw_gather: src, ids and out are required");
+  if (row_bytes == 0 || row_bytes % 4 != 0 || row_stride < row_bytes || row_stride % 16 != 0)
+    return fail(IBP_ERR_SIZE, "ibp_raw_gather: row_bytes %% 4, row_stride >= row_bytes and %% 16");
+  if (!aligned(src, 16) || !aligned(out, 16) || !aligned(ids, 8))
+    return fail(IBP_ERR_ALIGN, "ibp_raw_gather: misaligned pointer");
+  int r;
+  if ((r = require_device("ibp_raw_gather"))) return r;
+  hipError_t e = ibp::launch_raw_gather((const uint8_t*)src, row_stride, n_rows, ids, n_ids,
+                                        row_bytes, (uint8_t*)out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "ibp_raw_gather");
+  return ok();
+}
+
+int ibp_stream_read(const void* src, uint64_t bytes, uint32_t never, uint32_t* sink,
+                    void* stream) {
+  if (!src || !sink) return fail(IBP_ERR_NULL, "ibp_stream_read: src and sink are required");
+  if (bytes % 16 != 0) return fail(IBP_ERR_SIZE, "ibp_stream_read: bytes must be %% 16");
+  if (!aligned(src, 16) || !aligned(sink, 4))
+    return fail(IBP_ERR_ALIGN, "ibp_stream_read: misaligned pointer");
+  int r;
+  if ((r = require_device("ibp_stream_read"))) return r;
+  hipError_t e = ibp::launch_stream_read((const uint8_t*)src, bytes, never, sink,
+                                         (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "ibp_stream_read");
+  return ok();
+}
+
+}  // extern "C"

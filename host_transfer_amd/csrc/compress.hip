@@ -1,0 +1,281 @@
+// compress.hip -- IBP compression and compaction (off the critical path).
+//
+// [G-EN] Core Algorithm, Compression: chunk by chunk, the invariant positions
+// are checked against Bitval; a matching chunk drops them and closes the gaps,
+// a chunk that does not match (or would not shrink) is kept whole, and its
+// participation bit records which.  The GPU writes the result straight into
+// the (possibly host-mapped) store.  [G-EN] System Integration: in-place
+// fixed-size slots and a GPU-memory bitmask; cache compression keeps the
+// compressed tensors packed in GPU memory (ibp_compact).
+//
+// One group of G threads per tensor, with the same word ownership and
+// registers as the decompressor (ibp_plan.h):
+//   1. each thread loads its words (coalesced) and flags its chunk in LDS if
+//      a Mask bit differs from Bitval;
+//   2. the first wave decides P per chunk (lane c owns chunk c), scans the
+//      chunk sizes into bit offsets, and updates the bitmap bits of the
+//      tensor (atomic AND/OR, so neighbouring tensors sharing a bitmap word
+//      can be compressed concurrently);
+//   3. each thread packs its words and ORs them into an LDS buffer at their
+//      bit offsets (LDS atomics; a word can straddle two buffer words);
+//   4. the group writes the buffer to the slot in 16 B stores and clears it.
+#include "ibp_internal.h"
+#include "ibp_plan.h"
+
+namespace ibp {
+
+struct CompressArgs {
+  const uint8_t* rows;
+  uint64_t row_stride;
+  uint64_t n_rows;
+  uint64_t first;
+  const uint32_t* mask;
+  const uint32_t* bitval;
+  uint8_t* store;
+  uint64_t slot_bytes;
+  uint32_t* part_bits;
+  uint32_t* lengths;
+  Shape sh;
+  uint32_t groups;
+  uint32_t pbuf_bytes;
+};
+
+struct CompressLds {
+  uint32_t pref, kc, wsum, group0, group_stride;
+  __host__ __device__ CompressLds(uint32_t W, uint32_t pbuf_bytes) {
+    pref = 0;
+    kc = ((4u * (W + 1)) + 15u) & ~15u;
+    wsum = kc + 256;
+    group0 = wsum + 64;
+    // header, chunk offsets, chunk mismatch flags, payload buffer
+    group_stride = (uint32_t)sizeof(GroupHdr) + 256 + 256 + pbuf_bytes;
+  }
+  __host__ __device__ uint32_t total(uint32_t groups) const { return group0 + groups * group_stride; }
+};
+
+template <int J>
+__global__ __launch_bounds__(1024) void k_compress(CompressArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const CompressLds L(a.sh.W, a.pbuf_bytes);
+  uint32_t* s_pref = (uint32_t*)(smem + L.pref);
+  uint32_t* s_kc = (uint32_t*)(smem + L.kc);
+  uint32_t* s_wsum = (uint32_t*)(smem + L.wsum);
+
+  const uint32_t G = a.sh.group;
+  const uint32_t g = threadIdx.x / G;
+  const uint32_t gl = threadIdx.x - g * G;
+  uint8_t* gbase = smem + L.group0 + g * L.group_stride;
+  GroupHdr* hdr = (GroupHdr*)gbase;
+  uint32_t* s_obuf = (uint32_t*)(gbase + sizeof(GroupHdr));
+  uint32_t* s_fail = (uint32_t*)(gbase + sizeof(GroupHdr) + 256);
+  uint8_t* pbuf = gbase + sizeof(GroupHdr) + 512;
+  uint32_t* pb32 = (uint32_t*)pbuf;
+  uint4* pb128 = (uint4*)pbuf;
+
+  // clean buffer and flags before the first tensor
+  for (uint32_t q = gl; q < a.pbuf_bytes / 16; q += G) pb128[q] = make_uint4(0, 0, 0, 0);
+  if (gl < kWave) s_fail[gl] = 0;
+
+  WordRegs<J> R;
+  load_plan<J>(a.mask, a.bitval, a.sh, s_pref, s_kc, s_wsum, gl, R);
+
+  const bool single = G == kWave;
+  const uint32_t W = a.sh.W, n_c = a.sh.n_c;
+  const uint64_t step = (uint64_t)gridDim.x * a.groups;
+  for (uint64_t row = (uint64_t)blockIdx.x * a.groups + g; row < a.n_rows; row += step) {
+    const uint64_t t = a.first + row;
+    const uint32_t* x32 = (const uint32_t*)(a.rows + row * a.row_stride);
+
+    // 1. load words, flag mismatching chunks
+    uint32_t x[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const uint32_t w = gl + G * j;
+      x[j] = w < W ? x32[w] : 0u;
+      if (w < W && ((x[j] ^ R.bitval[j]) & R.mask[j]) != 0u) s_fail[w >> a.sh.wpc_log2] = 1u;
+    }
+    group_sync(single);
+
+    // 2. participation, offsets, length, bitmap (first wave)
+    if (gl < kWave) {
+      uint32_t size = 0;
+      bool p = false;
+      if (gl < n_c) {
+        const uint32_t bits = chunk_bits(a.sh, gl);
+        p = s_fail[gl] == 0u && s_kc[gl] < bits;
+        size = p ? s_kc[gl] : bits;
+        s_fail[gl] = 0u;
+        const uint64_t bit = t * n_c + gl;
+        const uint32_t b = 1u << (bit & 31);
+        if (p)
+          atomicOr(a.part_bits + (bit >> 5), b);
+        else
+          atomicAnd(a.part_bits + (bit >> 5), ~b);
+      }
+      const uint32_t incl = wave_inclusive_sum(size);
+      if (gl < n_c) s_obuf[gl] = incl - size;
+      const uint64_t pm = __ballot(p);
+      const uint32_t total = __shfl(incl, kWave - 1, kWave);
+      if (gl == 0) {
+        hdr->pmask = pm;
+        hdr->len = (total + 7u) >> 3;
+      }
+    }
+    group_sync(single);
+    const uint64_t pmask = hdr->pmask;
+    const uint32_t len = hdr->len;
+
+    // 3. pack and deposit at the bit offsets
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const uint32_t w = gl + G * j;
+      if (w < W) {
+        const uint32_t c = w >> a.sh.wpc_log2;
+        const bool p = (pmask >> c) & 1u;
+        const uint32_t off = s_obuf[c] + (p ? (R.info[j] & 0xFFFFu) : (R.info[j] >> 16));
+        const uint32_t v = p ? pack_bits(x[j], ~R.mask[j], R.mv[j]) : x[j];
+        const uint32_t sh = off & 31u;
+        const uint32_t lo = v << sh;
+        const uint32_t hi = sh ? (v >> (32u - sh)) : 0u;
+        if (lo) atomicOr(pb32 + (off >> 5), lo);
+        if (hi) atomicOr(pb32 + (off >> 5) + 1, hi);
+      }
+    }
+    group_sync(single);
+
+    // 4. buffer -> slot (16 B units up to the payload's end), then clear it
+    uint4* dst = (uint4*)(a.store + t * a.slot_bytes);
+    const uint32_t n16 = (len + 15u) >> 4;
+    for (uint32_t q = gl; q < n16; q += G) {
+      dst[q] = pb128[q];
+      pb128[q] = make_uint4(0, 0, 0, 0);
+    }
+    if (gl == 0 && a.lengths) a.lengths[t] = len;
+    group_sync(single);
+  }
+}
+
+template <int J>
+static hipError_t launch_j(const Geometry& g, const CompressArgs& a, hipStream_t s) {
+  const CompressLds L(g.W, a.pbuf_bytes);
+  const uint32_t lds = L.total(g.groups);
+  const uint32_t threads = g.group * g.groups;
+  DeviceInfo di;
+  hipError_t e = device_info(&di);
+  if (e != hipSuccess) return e;
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_compress<J>, threads, lds);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) return hipErrorInvalidConfiguration;
+  const uint64_t want = (a.n_rows + g.groups - 1) / g.groups;
+  const uint64_t cap = (uint64_t)per_cu * (uint64_t)di.cus;
+  const uint32_t blocks = (uint32_t)(want < cap ? want : cap);
+  hipLaunchKernelGGL(k_compress<J>, dim3(blocks), dim3(threads), lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_compress(const Geometry& g, const uint8_t* rows, uint64_t row_stride,
+                           uint64_t n_rows, uint64_t first, const uint32_t* mask,
+                           const uint32_t* bitval, uint8_t* store, uint64_t slot_bytes,
+                           uint32_t* part_bits, uint32_t* lengths, hipStream_t s) {
+  if (n_rows == 0) return hipSuccess;
+  CompressArgs a;
+  a.rows = rows;
+  a.row_stride = row_stride;
+  a.n_rows = n_rows;
+  a.first = first;
+  a.mask = mask;
+  a.bitval = bitval;
+  a.store = store;
+  a.slot_bytes = slot_bytes;
+  a.part_bits = part_bits;
+  a.lengths = lengths;
+  a.sh = Shape{g.W, g.n_c, g.wpc_log2, g.last_bits, g.group};
+  a.groups = g.groups;
+  a.pbuf_bytes = ((g.tensor_bytes + 15u) & ~15u) + 16u;
+  switch (g.J) {
+    case 1: return launch_j<1>(g, a, s);
+    case 2: return launch_j<2>(g, a, s);
+    case 3: return launch_j<3>(g, a, s);
+    case 4: return launch_j<4>(g, a, s);
+    case 5: return launch_j<5>(g, a, s);
+    case 6: return launch_j<6>(g, a, s);
+    case 7: return launch_j<7>(g, a, s);
+    case 8: return launch_j<8>(g, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// ---------------------------------------------------------------- compaction
+
+// offsets[t] = sum of roundup(lengths[u], 16) over u < t; offsets[n] = total.
+// One workgroup walks the array in tiles of 4 x 1024 entries (off the
+// critical path: a few milliseconds for millions of tensors).
+__global__ __launch_bounds__(1024) void k_compact_offsets(const uint32_t* __restrict__ lengths,
+                                                           uint64_t n, uint64_t* __restrict__ offsets) {
+  __shared__ uint32_t s_wsum[16];
+  const uint32_t tid = threadIdx.x;
+  uint64_t carry = 0;
+  for (uint64_t base = 0; base < n; base += 4096) {
+    uint32_t v[4];
+    uint32_t local = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint64_t t = base + 4u * tid + i;
+      v[i] = t < n ? ((lengths[t] + 15u) & ~15u) : 0u;
+      local += v[i];
+    }
+    uint32_t tot;
+    const uint32_t incl = block_inclusive_sum(local, s_wsum, &tot);
+    uint64_t o = carry + (incl - local);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint64_t t = base + 4u * tid + i;
+      if (t < n) offsets[t] = o;
+      o += v[i];
+    }
+    carry += tot;
+  }
+  if (tid == 0) offsets[n] = carry;
+}
+
+// One wave per entry: copies offsets[t+1] - offsets[t] bytes from slot t.
+__global__ __launch_bounds__(256) void k_compact_copy(const uint8_t* __restrict__ store,
+                                                       uint64_t slot_bytes, uint64_t n,
+                                                       const uint64_t* __restrict__ offsets,
+                                                       uint8_t* __restrict__ cache,
+                                                       uint64_t cache_bytes) {
+  const uint32_t lane = lane_id();
+  const uint64_t wave = (uint64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const uint64_t waves = (uint64_t)gridDim.x * (blockDim.x / kWave);
+  for (uint64_t t = wave; t < n; t += waves) {
+    const uint64_t o0 = offsets[t], o1 = offsets[t + 1];
+    if (o1 < o0 || o1 > cache_bytes || ((o0 | o1) & 15u) != 0 || o1 - o0 > slot_bytes) continue;
+    const uint4* src = (const uint4*)(store + t * slot_bytes);
+    uint4* dst = (uint4*)(cache + o0);
+    const uint32_t n16 = (uint32_t)((o1 - o0) >> 4);
+    for (uint32_t q = lane; q < n16; q += kWave) dst[q] = src[q];
+  }
+}
+
+hipError_t launch_compact_offsets(const uint32_t* lengths, uint64_t n, uint64_t* offsets,
+                                  hipStream_t s) {
+  hipLaunchKernelGGL(k_compact_offsets, dim3(1), dim3(1024), 0, s, lengths, n, offsets);
+  return hipGetLastError();
+}
+
+hipError_t launch_compact(const uint8_t* store, uint64_t slot_bytes, uint64_t n,
+                          const uint64_t* offsets, uint8_t* cache, uint64_t cache_bytes,
+                          hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  DeviceInfo di;
+  hipError_t e = device_info(&di);
+  if (e != hipSuccess) return e;
+  const uint64_t want = (n + 3) / 4;
+  const uint64_t cap = (uint64_t)di.cus * 8;
+  hipLaunchKernelGGL(k_compact_copy, dim3((uint32_t)(want < cap ? want : cap)), dim3(256), 0, s,
+                     store, slot_bytes, n, offsets, cache, cache_bytes);
+  return hipGetLastError();
+}
+
+}  // namespace ibp

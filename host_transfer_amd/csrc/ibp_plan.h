@@ -1,0 +1,122 @@
+// ibp_plan.h -- per-kernel preparation of the Mask/Bitval metadata (gfx950).
+//
+// A "group" of G threads (G = 64, 128, 256 or 512) handles one tensor at a
+// time.  Thread gl of a group owns the output words w = gl + G*j, j < J, for
+// every tensor it touches, so everything that depends only on the metadata is
+// computed once per workgroup and kept in that thread's registers:
+//   - the five move masks of its words (ibp_device.h),
+//   - Mask and Bitval of its words,
+//   - `info`: the bit offset of the word's kept bits inside its chunk when the
+//     chunk participates (low 16 bits) and inside its chunk when the chunk is
+//     raw (high 16 bits, = 32 * word index in the chunk).
+// The per-chunk payload sizes K_c (kept bits of a participating chunk) go to
+// LDS, read by the lanes that own chunks ([G-EN] Core Algorithm: metadata is
+// global, reused for every tensor; [JH]: one thread per chunk).
+#pragma once
+
+#include "ibp_device.h"
+
+namespace ibp {
+
+struct Shape {
+  uint32_t W;          // 32-bit words per tensor
+  uint32_t n_c;        // chunks per tensor (<= 64)
+  uint32_t wpc_log2;   // log2(words per chunk)
+  uint32_t last_bits;  // bits in the last chunk (the others have 32 << wpc_log2)
+  uint32_t group;      // threads per tensor (multiple of 64)
+};
+
+__device__ __forceinline__ uint32_t chunk_bits(const Shape& sh, uint32_t c) {
+  return c + 1 < sh.n_c ? (32u << sh.wpc_log2) : sh.last_bits;
+}
+
+template <int J>
+struct WordRegs {
+  uint32_t mv[J][5];
+  uint32_t mask[J];
+  uint32_t bitval[J];
+  uint32_t info[J];
+};
+
+// Workgroup-wide inclusive sum (blockDim.x a multiple of 64, <= 1024).
+// s_wsum: 16 words of LDS.  Contains barriers: every thread must call it.
+__device__ __forceinline__ uint32_t block_inclusive_sum(uint32_t v, uint32_t* s_wsum,
+                                                        uint32_t* total) {
+  const uint32_t incl = wave_inclusive_sum(v);
+  const uint32_t wid = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  if (lane_id() == kWave - 1) s_wsum[wid] = incl;
+  __syncthreads();
+  uint32_t off = 0, tot = 0;
+  for (uint32_t i = 0; i < nw; ++i) {
+    const uint32_t s = s_wsum[i];
+    off += i < wid ? s : 0u;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return incl + off;
+}
+
+// Builds the registers of thread gl and the K_c table.  Every thread of the
+// workgroup must call it.  s_pref: W+1 words of LDS (scratch), s_kc: 64 words.
+template <int J>
+__device__ void load_plan(const uint32_t* __restrict__ mask, const uint32_t* __restrict__ bitval,
+                          const Shape& sh, uint32_t* s_pref, uint32_t* s_kc, uint32_t* s_wsum,
+                          uint32_t gl, WordRegs<J>& R) {
+  const uint32_t nt = blockDim.x, tid = threadIdx.x;
+  // exclusive prefix over all words of the number of kept (non-Mask) bits
+  uint32_t carry = 0;
+  for (uint32_t base = 0; base < sh.W; base += nt) {
+    const uint32_t w = base + tid;
+    const uint32_t k = w < sh.W ? (uint32_t)__popc(~mask[w]) : 0u;
+    uint32_t tot;
+    const uint32_t incl = block_inclusive_sum(k, s_wsum, &tot);
+    if (w < sh.W) s_pref[w] = carry + incl - k;
+    carry += tot;
+  }
+  if (tid == 0) s_pref[sh.W] = carry;
+  __syncthreads();
+  for (uint32_t c = tid; c < sh.n_c; c += nt) {
+    const uint32_t lo = c << sh.wpc_log2;
+    const uint32_t hi = min((c + 1) << sh.wpc_log2, sh.W);
+    s_kc[c] = s_pref[hi] - s_pref[lo];
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const uint32_t w = gl + sh.group * j;
+    if (w < sh.W) {
+      const uint32_t m = mask[w];
+      move_masks(~m, R.mv[j]);
+      R.mask[j] = m;
+      R.bitval[j] = bitval[w] & m;
+      const uint32_t first = (w >> sh.wpc_log2) << sh.wpc_log2;
+      R.info[j] = (s_pref[w] - s_pref[first]) | ((32u * (w - first)) << 16);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 5; ++s) R.mv[j][s] = 0;
+      R.mask[j] = 0;
+      R.bitval[j] = 0;
+      R.info[j] = 0;
+    }
+  }
+  __syncthreads();
+}
+
+// Synchronises the threads of one group: a wave, or the whole workgroup.
+__device__ __forceinline__ void group_sync(bool single_wave) {
+  if (single_wave)
+    wave_sync();
+  else
+    __syncthreads();
+}
+
+// Per-group state shared between the chunk-owning wave and the others.
+struct GroupHdr {
+  uint64_t pmask;  // participation bits of the current tensor's chunks
+  uint64_t base;   // byte offset of its payload in the store
+  uint32_t len;    // payload bytes
+  uint32_t valid;  // id in range
+  uint32_t pad[2];
+};
+
+}  // namespace ibp

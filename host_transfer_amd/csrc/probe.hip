@@ -1,0 +1,81 @@
+// probe.hip -- measurement baselines ([JH] Table 1 and Figure 5 discussions):
+//   k_raw_gather   uncompressed GPU-initiated gather of the same rows (what
+//                  the compressed gather is compared against);
+//   k_stream_read  streaming 16 B loads over a buffer (host-mapped: the rate
+//                  of GPU-initiated reads over the host link; device: HBM).
+#include "ibp_internal.h"
+#include "ibp_device.h"
+
+namespace ibp {
+
+// One wave per output row.  16 B units when the row size allows it, else 4 B.
+__global__ __launch_bounds__(256) void k_raw_gather(const uint8_t* __restrict__ src,
+                                                     uint64_t row_stride, uint64_t n_rows,
+                                                     const int64_t* __restrict__ ids,
+                                                     uint64_t n_ids, uint32_t row_bytes,
+                                                     uint8_t* __restrict__ out) {
+  const uint32_t lane = lane_id();
+  const uint64_t wave = (uint64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const uint64_t waves = (uint64_t)gridDim.x * (blockDim.x / kWave);
+  const bool wide = (row_bytes & 15u) == 0;
+  for (uint64_t r = wave; r < n_ids; r += waves) {
+    const int64_t id = ids[r];
+    const bool valid = id >= 0 && (uint64_t)id < n_rows;
+    const uint8_t* s = src + (valid ? (uint64_t)id * row_stride : 0);
+    uint8_t* d = out + r * row_bytes;
+    if (wide) {
+      for (uint32_t q = lane; q < row_bytes / 16; q += kWave)
+        ((uint4*)d)[q] = valid ? ((const uint4*)s)[q] : make_uint4(0, 0, 0, 0);
+    } else {
+      for (uint32_t q = lane; q < row_bytes / 4; q += kWave)
+        ((uint32_t*)d)[q] = valid ? ((const uint32_t*)s)[q] : 0u;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_stream_read(const uint4* __restrict__ src, uint64_t n16,
+                                                      uint32_t never, uint32_t* __restrict__ sink) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  uint32_t acc = 0;
+  uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^
+           d.z ^ d.w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = src[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  if (acc == never) sink[0] = acc;
+}
+
+hipError_t launch_raw_gather(const uint8_t* src, uint64_t row_stride, uint64_t n_rows,
+                             const int64_t* ids, uint64_t n_ids, uint32_t row_bytes, uint8_t* out,
+                             hipStream_t s) {
+  if (n_ids == 0) return hipSuccess;
+  DeviceInfo di;
+  hipError_t e = device_info(&di);
+  if (e != hipSuccess) return e;
+  const uint64_t want = (n_ids + 3) / 4;
+  const uint64_t cap = (uint64_t)di.cus * 8;
+  hipLaunchKernelGGL(k_raw_gather, dim3((uint32_t)(want < cap ? want : cap)), dim3(256), 0, s,
+                     src, row_stride, n_rows, ids, n_ids, row_bytes, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_read(const uint8_t* src, uint64_t bytes, uint32_t never, uint32_t* sink,
+                              hipStream_t s) {
+  const uint64_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  DeviceInfo di;
+  hipError_t e = device_info(&di);
+  if (e != hipSuccess) return e;
+  const uint64_t want = (n16 + 255) / 256;
+  const uint64_t cap = (uint64_t)di.cus * 8;
+  hipLaunchKernelGGL(k_stream_read, dim3((uint32_t)(want < cap ? want : cap)), dim3(256), 0, s,
+                     (const uint4*)src, n16, never, sink);
+  return hipGetLastError();
+}
+
+}  // namespace ibp

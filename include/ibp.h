@@ -1,0 +1,234 @@
+/*
+ * ibp.h -- C ABI of libibp.so: Invariant Bit Packing (IBP) on AMD Instinct
+ * MI355X (gfx950).  Batched gather + decompress of IBP-compressed fixed-size
+ * tensors into dense device buffers, plus the two off-critical-path steps
+ * that produce the compressed form (metadata build, compression) and the
+ * compaction into a GPU-resident compressed cache.
+ *
+ * The method is the one described on web pages about the paper "Reducing the
+ * GPU Memory Bottleneck with Lossless Compression for ML -- Extended"
+ * (Kamath, Krishnamurthy, Canini, Peter).  Citations below name the page and
+ * the part of it:
+ *   [G-EN]  gist.science English explainer, "Technical Summary": Core
+ *           Algorithm (Preprocessing, Compression, Decompression) and System
+ *           Integration (cache compression, PCIe transfer compression);
+ *   [JH]    juhe.plus Chinese review of the same paper (its paragraphs on the
+ *           Mask/Bitval metadata, on warp-per-tensor decompression, on
+ *           128 B-aligned GPU-initiated transfers and on sampling).
+ *
+ * ---------------------------------------------------------------- FORMAT
+ * The pages fix no byte format; this library fixes the following one.
+ *   tensor     B bytes (B % 4 == 0, 4 <= B <= IBP_MAX_TENSOR_BYTES); bit i is
+ *              bit (i % 8) of byte (i / 8), i.e. bit (i % 32) of the
+ *              little-endian 32-bit word i / 32.  W = B / 4 words.
+ *   Mask       W words; bit i set = position i is invariant.
+ *   Bitval     W words; the invariant value of each Mask position, 0 elsewhere.
+ *   chunk      C bytes, C in {256, 1024, 4096} (the chunk sizes the pages
+ *              evaluate, [JH] Figure 7 discussion); chunk c of a tensor is
+ *              bytes [c*C, min((c+1)*C, B)); n_c = ceil(B / C) <= 64.
+ *   P[t][c]    participation of chunk c of tensor t: 1 iff every Mask bit of
+ *              the chunk equals its Bitval bit and the chunk holds at least one
+ *              Mask bit (otherwise packing it would save nothing).
+ *   bitmap     P[t][c] is bit (t*n_c + c) of a uint32 array, LSB first.  It
+ *              lives in GPU memory, apart from the payloads ([G-EN] System
+ *              Integration: a GPU-memory bitmask says which tensors are
+ *              compressed; here one bit per chunk, so a tensor is compressed
+ *              iff any of its bits is set).
+ *   payload    chunk streams back to back, no padding: a participating chunk
+ *              contributes its non-Mask bits in ascending position, another
+ *              chunk all its bits; stream bit j is bit (j % 8) of byte j / 8;
+ *              unused bits of the last byte are 0.  len_t = ceil(bits / 8)
+ *              <= B bytes.
+ *   slot store the payload of tensor t starts at store + t*slot_bytes
+ *              (in-place fixed-size buffers, [G-EN] System Integration, PCIe
+ *              transfer compression); slot bytes [len_t, slot_bytes) are
+ *              don't-care (the compressor writes zeros up to the next 16 B).
+ *   cache      compacted layout: payload of t at cache + offsets[t],
+ *              offsets[0] = 0, offsets[t+1] = offsets[t] + roundup(len_t, 16)
+ *              ([G-EN] System Integration, cache compression).
+ *
+ * -------------------------------------------------------------- CONVENTIONS
+ *   - Every function returns IBP_OK (0) or a negative ibp_status.  Arguments
+ *     are validated synchronously before anything is enqueued; on failure
+ *     nothing is enqueued and ibp_last_error() describes why (thread-local).
+ *     Nothing throws across this interface.
+ *   - GPU work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream) of the current HIP device; results are valid once the stream
+ *     has been synchronized.  A HIP launch failure returns IBP_ERR_HIP.
+ *   - The caller owns every buffer and keeps it alive until the stream has
+ *     finished with it.  "device" buffers are GPU memory; "host-mapped" means
+ *     pinned host memory from ibp_host_alloc (the GPU reads and writes it
+ *     directly over PCIe).  The library keeps no allocation between calls.
+ *   - Pointer alignment: rows and word arrays 4 B; store, cache and out 16 B.
+ *   - Output is deterministic: the same inputs give the same bytes.
+ */
+#ifndef IBP_H
+#define IBP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    IBP_OK = 0,
+    IBP_ERR_NULL = -1,       /* a required pointer is NULL                     */
+    IBP_ERR_SIZE = -2,       /* a size, count or stride is out of range         */
+    IBP_ERR_CHUNK = -3,      /* chunk_bytes not in {256, 1024, 4096}            */
+    IBP_ERR_THRESHOLD = -4,  /* threshold not in [0.5, 1] (or NaN)             */
+    IBP_ERR_ALIGN = -5,      /* a pointer or stride breaks its alignment rule   */
+    IBP_ERR_HIP = -6,        /* the HIP runtime reported an error               */
+    IBP_ERR_FLAGS = -7       /* unknown flag bits                               */
+} ibp_status;
+
+#define IBP_VERSION 1
+#define IBP_MAX_TENSOR_BYTES 16384u
+#define IBP_MAX_CHUNKS 64u
+
+/* Library version (IBP_VERSION). */
+int ibp_version(void);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char *ibp_last_error(void);
+
+/* n_c = ceil(tensor_bytes / chunk_bytes), or a negative ibp_status if the
+ * pair is not accepted by the other calls. */
+int ibp_num_chunks(uint32_t tensor_bytes, uint32_t chunk_bytes);
+
+/*
+ * ibp_build_metadata -- [G-EN] Core Algorithm, Preprocessing; [JH] paragraph
+ * on Mask/Bitval and paragraph on sampling 1/5/10 % of the data.
+ * Over the n_samples sampled tensors, counts per bit position i the number n1
+ * of tensors with bit i set (n0 = n_samples - n1), then writes
+ *     Mask[i]   = max(n0, n1) >= m,   m = ceil(threshold * n_samples)
+ *     Bitval[i] = Mask[i] && n1 > n0
+ * m is computed on the host in IEEE binary64.
+ *   rows         tensor r at rows + r*row_stride (device or host-mapped).
+ *   sample_ids   device int64[n_samples] of tensor indices, or NULL for
+ *                tensors 0..n_samples-1.  Precondition: each id < the number
+ *                of tensors behind `rows` (not checked on the GPU).
+ *   threshold    T in [0.5, 1].
+ *   mask, bitval device uint32[tensor_bytes / 4] outputs.
+ *   counts       device uint32[8 * tensor_bytes] workspace; on completion it
+ *                holds n1 of every bit position i at counts[i].
+ * Errors: NULL pointer, tensor_bytes out of range or not % 4, n_samples == 0
+ * or > 2^32 - 1, row_stride < tensor_bytes or not % 4, bad threshold.
+ */
+int ibp_build_metadata(const void *rows, uint64_t row_stride,
+                       const int64_t *sample_ids, uint64_t n_samples,
+                       uint32_t tensor_bytes, double threshold,
+                       uint32_t *mask, uint32_t *bitval, uint32_t *counts,
+                       void *stream);
+
+/*
+ * ibp_compress -- [G-EN] Core Algorithm, Compression; System Integration,
+ * PCIe transfer compression (in-place fixed-size buffers, GPU bitmask); the
+ * GPU writes the store directly, also when it is host-mapped.
+ * Compresses rows 0..n_rows-1 as tensors t = first_tensor + i of a store of
+ * n_tensors slots: writes the payload of t to its slot (bytes
+ * [0, roundup(len_t, 16)) of the slot; zeros after len_t), sets/clears bits
+ * t*n_c + c of part_bits, and writes len_t to lengths[t] if lengths != NULL.
+ * Other tensors' slots, bits and lengths are untouched.
+ *   rows        row i at rows + i*row_stride (device or host-mapped).
+ *   mask,bitval device uint32[tensor_bytes / 4] (from ibp_build_metadata).
+ *   store       device or host-mapped, n_tensors*slot_bytes bytes, 16 B aligned.
+ *   slot_bytes  >= tensor_bytes, % 16 == 0 (128 recommended for host stores).
+ *   part_bits   device uint32[ceil(n_tensors*n_c / 32)].
+ *   lengths     device uint32[n_tensors] or NULL.
+ * Calls that write the same tensors, or run concurrently on one store, race.
+ * Errors: NULL pointer, sizes, first_tensor + n_rows > n_tensors, alignment.
+ */
+int ibp_compress(const void *rows, uint64_t row_stride, uint64_t n_rows,
+                 uint64_t first_tensor, uint64_t n_tensors,
+                 uint32_t tensor_bytes, uint32_t chunk_bytes,
+                 const uint32_t *mask, const uint32_t *bitval,
+                 void *store, uint64_t slot_bytes,
+                 uint32_t *part_bits, uint32_t *lengths, void *stream);
+
+/*
+ * ibp_compact_offsets -- [G-EN] System Integration, cache compression.
+ * offsets[0] = 0, offsets[t+1] = offsets[t] + roundup(lengths[t], 16) for
+ * t < n_tensors (so offsets[n_tensors] is the cache size in bytes).
+ *   lengths  device uint32[n_tensors];  offsets  device uint64[n_tensors + 1].
+ */
+int ibp_compact_offsets(const uint32_t *lengths, uint64_t n_tensors,
+                        uint64_t *offsets, void *stream);
+
+/*
+ * ibp_compact -- copies entry t (offsets[t+1] - offsets[t] bytes from the
+ * start of slot t) to cache + offsets[t] for every t < n_tensors.  Entries
+ * that would end past cache_bytes are not copied.
+ *   store  device or host-mapped slots (as written by ibp_compress).
+ *   cache  device, cache_bytes bytes, 16 B aligned.
+ */
+int ibp_compact(const void *store, uint64_t slot_bytes, uint64_t n_tensors,
+                const uint64_t *offsets, void *cache, uint64_t cache_bytes,
+                void *stream);
+
+/*
+ * ibp_gather_decompress -- [G-EN] Core Algorithm, Decompression; [JH]
+ * paragraphs on warp-per-tensor decompression with chunk offsets from a scan
+ * inside the warp, and on 128 B-aligned GPU-initiated reads of host memory
+ * overlapped with decoding.
+ * out row r (tensor_bytes bytes at out + r*tensor_bytes) = the decompressed
+ * tensor ids[r]: participating chunks take Bitval at Mask positions and the
+ * next payload bits elsewhere; other chunks take payload bits everywhere.
+ *   store        payloads: slots (offsets == NULL; store holds
+ *                n_tensors*slot_bytes bytes, host-mapped or device) or a
+ *                compacted cache (offsets != NULL; device uint64 offsets as
+ *                from ibp_compact_offsets).
+ *   store_bytes  readable bytes at store.  Reads never go past it (a corrupt
+ *                bitmap or offset yields wrong rows, never an access fault).
+ *   part_bits    device bitmap of the n_tensors tensors.
+ *   ids          device int64[n_ids]; repeats allowed.  An id outside
+ *                [0, n_tensors) yields a row of zero bytes.
+ *   mask,bitval  device uint32[tensor_bytes / 4].
+ *   out          device, n_ids*tensor_bytes bytes, 16 B aligned.
+ * Errors: NULL pointer, sizes (store_bytes < n_tensors*slot_bytes in slot
+ * mode), chunk size, alignment.
+ */
+int ibp_gather_decompress(const void *store, uint64_t store_bytes,
+                          uint64_t slot_bytes, const uint64_t *offsets,
+                          const uint32_t *part_bits, uint64_t n_tensors,
+                          const int64_t *ids, uint64_t n_ids,
+                          uint32_t tensor_bytes, uint32_t chunk_bytes,
+                          const uint32_t *mask, const uint32_t *bitval,
+                          void *out, void *stream);
+
+/* ------------------------------------------------------------ host memory
+ * Pinned host memory that the GPU reads and writes directly (zero-copy),
+ * [G-EN] Core Algorithm, Compression (zero-copy access to CPU memory).
+ *   IBP_HOST_DEFAULT      mapped, portable; coherence per HIP's default
+ *   IBP_HOST_COHERENT     + fine-grained (coherent) memory
+ *   IBP_HOST_NONCOHERENT  + coarse-grained (non-coherent) memory
+ * ibp_host_free releases memory from ibp_host_alloc (NULL is accepted). */
+#define IBP_HOST_DEFAULT 0u
+#define IBP_HOST_COHERENT 1u
+#define IBP_HOST_NONCOHERENT 2u
+int ibp_host_alloc(uint64_t bytes, unsigned flags, void **ptr);
+int ibp_host_free(void *ptr);
+
+/* ------------------------------------------------------------ measurement
+ * Baselines the pages compare against ([JH] Table 1 and Figure 5
+ * discussions): an uncompressed GPU-initiated gather of the same rows, and a
+ * streaming read that measures the link or HBM read rate. */
+
+/* out row r = row_bytes bytes at src + ids[r]*row_stride.  Ids outside
+ * [0, n_rows) give zero rows.  src device or host-mapped; row_stride and
+ * src 16 B aligned; out 16 B aligned; row_bytes % 4 == 0. */
+int ibp_raw_gather(const void *src, uint64_t row_stride, uint64_t n_rows,
+                   const int64_t *ids, uint64_t n_ids, uint32_t row_bytes,
+                   void *out, void *stream);
+
+/* Reads bytes (a multiple of 16) at src with 16 B loads spread over the whole
+ * GPU.  sink: device uint32[1]; written only if the XOR of all data equals
+ * `never` (so the reads cannot be optimised away).  src 16 B aligned. */
+int ibp_stream_read(const void *src, uint64_t bytes, uint32_t never,
+                    uint32_t *sink, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IBP_H */

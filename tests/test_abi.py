@@ -1,0 +1,126 @@
+"""The C ABI on the CPU: libibp.so loads, exports every function include/ibp.h
+declares, and rejects bad arguments synchronously with the documented status
+and a message, before any HIP call.  No compute call is made here."""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ibp.h")
+
+
+@pytest.fixture(scope="module")
+def ibp():
+    from host_transfer_amd import ibp as mod
+    return mod
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ibp_\w+)\s*\(", text, flags=re.M))
+
+
+def test_every_declared_function_is_exported(ibp):
+    names = declared_functions()
+    assert len(names) == 12, names
+    out = subprocess.run(["nm", "-D", "--defined-only", ibp.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (ibp_\w+)$", out, flags=re.M))
+    assert names <= exported, names - exported
+    assert names == set(ibp.EXPORTED)
+
+
+def test_version_and_chunks(ibp):
+    assert ibp.version() == 1
+    assert ibp.num_chunks(5732, 1024) == 6
+    assert ibp.num_chunks(512, 1024) == 1
+    assert ibp.num_chunks(10240, 256) == 40
+    assert ibp.num_chunks(16384, 256) == 64
+    for tb, cb, code in [(0, 256, ibp.ERR_SIZE), (6, 256, ibp.ERR_SIZE), (16388, 256, ibp.ERR_SIZE),
+                         (512, 512, ibp.ERR_CHUNK), (512, 0, ibp.ERR_CHUNK)]:
+        with pytest.raises(ibp.IbpError) as e:
+            ibp.num_chunks(tb, cb)
+        assert e.value.code == code and ibp.last_error()
+
+
+P = 1 << 20  # a fake, suitably aligned address: validation never dereferences it
+
+
+def _expect(ibp, code, fn, *args):
+    with pytest.raises(ibp.IbpError) as e:
+        fn(*args, stream=0)
+    assert e.value.code == code, (e.value.code, ibp.last_error())
+    assert ibp.last_error()
+
+
+def test_build_metadata_validation(ibp):
+    f = ibp.build_metadata
+    _expect(ibp, ibp.ERR_NULL, f, 0, 512, None, 10, 512, 0.99, P, P, P)
+    _expect(ibp, ibp.ERR_NULL, f, P, 512, None, 10, 512, 0.99, P, P, None)
+    _expect(ibp, ibp.ERR_SIZE, f, P, 512, None, 10, 510, 0.99, P, P, P)
+    _expect(ibp, ibp.ERR_SIZE, f, P, 512, None, 0, 512, 0.99, P, P, P)
+    _expect(ibp, ibp.ERR_SIZE, f, P, 256, None, 10, 512, 0.99, P, P, P)
+    for T in (0.4999, 1.0001, float("nan")):
+        _expect(ibp, ibp.ERR_THRESHOLD, f, P, 512, None, 10, 512, T, P, P, P)
+    _expect(ibp, ibp.ERR_ALIGN, f, P + 2, 512, None, 10, 512, 0.99, P, P, P)
+    _expect(ibp, ibp.ERR_ALIGN, f, P, 512, P + 4, 10, 512, 0.99, P, P, P)
+
+
+def test_compress_validation(ibp):
+    f = ibp.compress
+    ok = [P, 512, 10, 0, 10, 512, 256, P, P, P, 512, P, P]
+
+    def args(**kw):
+        a = list(ok)
+        names = ["rows", "stride", "n", "first", "nt", "tb", "cb", "mask", "bv", "store", "slot",
+                 "pb", "lens"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return a
+    _expect(ibp, ibp.ERR_NULL, f, *args(store=0))
+    _expect(ibp, ibp.ERR_NULL, f, *args(pb=0))
+    _expect(ibp, ibp.ERR_CHUNK, f, *args(cb=128))
+    _expect(ibp, ibp.ERR_SIZE, f, *args(first=5, n=6))
+    _expect(ibp, ibp.ERR_SIZE, f, *args(slot=520))
+    _expect(ibp, ibp.ERR_SIZE, f, *args(slot=496))
+    _expect(ibp, ibp.ERR_SIZE, f, *args(stride=508))
+    _expect(ibp, ibp.ERR_ALIGN, f, *args(store=P + 8))
+
+
+def test_gather_validation(ibp):
+    f = ibp.gather_decompress
+    ok = [P, 10 * 512, 512, None, P, 10, P, 4, 512, 256, P, P, P]
+
+    def args(**kw):
+        a = list(ok)
+        names = ["store", "sbytes", "slot", "offs", "pb", "nt", "ids", "nids", "tb", "cb", "mask",
+                 "bv", "out"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return a
+    _expect(ibp, ibp.ERR_NULL, f, *args(ids=0))
+    _expect(ibp, ibp.ERR_NULL, f, *args(out=0))
+    _expect(ibp, ibp.ERR_SIZE, f, *args(sbytes=10 * 512 - 1))
+    _expect(ibp, ibp.ERR_SIZE, f, *args(tb=20000))
+    _expect(ibp, ibp.ERR_CHUNK, f, *args(cb=2048))
+    _expect(ibp, ibp.ERR_ALIGN, f, *args(out=P + 4))
+    _expect(ibp, ibp.ERR_ALIGN, f, *args(ids=P + 4))
+    _expect(ibp, ibp.ERR_ALIGN, f, *args(offs=P + 4))
+
+
+def test_other_validation(ibp):
+    _expect(ibp, ibp.ERR_NULL, ibp.compact_offsets, 0, 10, P)
+    _expect(ibp, ibp.ERR_NULL, ibp.compact, P, 512, 10, P, 0, 100)
+    _expect(ibp, ibp.ERR_SIZE, ibp.compact, P, 500, 10, P, P, 100)
+    _expect(ibp, ibp.ERR_SIZE, ibp.raw_gather, P, 512, 10, P, 4, 514, P)
+    _expect(ibp, ibp.ERR_SIZE, ibp.stream_read, P, 100, 0, P)
+    with pytest.raises(ibp.IbpError) as e:
+        ibp.host_alloc(1024, 7)
+    assert e.value.code == ibp.ERR_FLAGS
+    with pytest.raises(ibp.IbpError) as e:
+        ibp.host_alloc(0)
+    assert e.value.code == ibp.ERR_SIZE
+    ibp.host_free(0)

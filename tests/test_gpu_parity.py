@@ -1,0 +1,210 @@
+"""GPU parity: every stage of libibp.so against the CPU oracle, bit for bit.
+
+Inputs are the seeded workloads at sizes the oracle finishes in seconds
+(several tiles and a ragged tail each), random tensors covering every thread
+grouping (1..8 words per thread, 64..512 threads per tensor, 1..64 chunks),
+and the degenerate cases of the method.  All GPU work goes through the C ABI.
+"""
+import numpy as np
+import pytest
+import torch
+
+from host_transfer_amd import workloads as W
+from tests import gpu_case as G
+
+pytestmark = pytest.mark.gpu
+
+
+def full_roundtrip(name, rows, C, T, sample_ids=None, slot=None, pinned=False, batches=None,
+                   rng=None):
+    """Metadata -> compress -> gather (slots) -> compact -> gather (cache)."""
+    rng = rng or np.random.default_rng(7)
+    n, B = rows.shape
+    slot = slot or (B + 127) // 128 * 128
+    G.log(f"[parity] {name}: n={n} B={B} C={C} T={T} slot={slot} pinned={pinned}")
+    mask, bitval = G.check_metadata(rows, T, sample_ids)
+    store, part, lengths = G.gpu_compress(rows, mask, bitval, C, slot, pinned=pinned)
+    o_store, o_part, o_len = G.check_store(rows, mask, bitval, C, slot, store, part, lengths)
+    batches = batches or [rng.integers(0, n, 777), np.arange(n)[::-1].copy(), np.array([0, n - 1, 0])]
+    for ids in batches:
+        got = G.gpu_gather(store, n * slot, slot, None, part, n, ids, B, C, mask, bitval)
+        want = G.expected_rows(rows, ids)
+        assert (got == want).all(), f"{name}: gather from slots is not the original rows"
+        ora = O_gather(o_store, o_part, n, ids, B, C, mask, bitval, slot)
+        assert (got == ora).all(), f"{name}: gather differs from the oracle"
+    # compacted HBM cache
+    offsets = torch.zeros(n + 1, dtype=torch.int64, device="cuda")
+    from host_transfer_amd import ibp
+    ibp.compact_offsets(lengths, n, offsets)
+    g_off = G.host(offsets).view(np.uint64)
+    from oracle import oracle as O
+    o_off, o_cache = O.compact(o_store, slot, o_len)
+    assert (g_off == o_off).all(), f"{name}: cache offsets differ"
+    total = int(g_off[-1])
+    cache = torch.full((max(total, 16),), 0x3C, dtype=torch.int8, device="cuda")
+    ibp.compact(store, slot, n, offsets, cache, total)
+    g_cache = G.host(cache).view(np.uint8)[:total]
+    assert (g_cache == o_cache).all(), f"{name}: cache bytes differ"
+    ids = batches[0]
+    got = G.gpu_gather(cache, total, 0, offsets, part, n, ids, B, C, mask, bitval)
+    assert (got == G.expected_rows(rows, ids)).all(), f"{name}: gather from the cache differs"
+    return mask, bitval, o_len
+
+
+def O_gather(store, part, n, ids, B, C, mask, bitval, slot):
+    from oracle import oracle as O
+    return O.gather_decompress(store, part, n, ids, B, C, mask, bitval, slot_bytes=slot)
+
+
+# ------------------------------------------------------------ the workloads
+
+def test_tiny_full():
+    w = W.WORKLOADS["tiny"]
+    rows = W.rows(w)
+    mask, _, lens = full_roundtrip("tiny", rows, w.chunk_bytes, w.threshold,
+                                   batches=[W.batch_ids(w, 0), W.batch_ids(w, 1)[:1000],
+                                            np.arange(w.n_tensors)])
+    assert (mask == 0x78000000).all()
+
+
+@pytest.mark.parametrize("T", [0.99, 0.95])
+def test_sparse_gnn(T):
+    w = W.WORKLOADS["sparse_gnn"].scaled(3000)
+    rows = W.rows(w)
+    full_roundtrip(f"sparse_gnn T={T}", rows, w.chunk_bytes, T, sample_ids=W.sample_ids(
+        W.WORKLOADS["sparse_gnn"].scaled(3000 * 40))[:300] % 3000)
+
+
+def test_dense_gnn_pinned():
+    w = W.WORKLOADS["dense_gnn"].scaled(5000)
+    rows = W.rows(w)
+    full_roundtrip("dense_gnn", rows, w.chunk_bytes, w.threshold, pinned=True)
+
+
+def test_dlrm_pinned():
+    for key, n in (("dlrm_1k", 4000), ("dlrm_2k", 2500)):
+        w = W.WORKLOADS[key].scaled(n)
+        rows = W.rows(w)
+        full_roundtrip(key, rows, w.chunk_bytes, w.threshold, pinned=True)
+
+
+def test_kv_pair():
+    w = W.WORKLOADS["kv_opt13b"]
+    prefill = W.kv_prefill_rows(w, 5, 3000)
+    rows = W.rows(w, 5 * 2560, 2560)
+    # Mask from the prefill sample, applied to the pair's decode rows
+    mask, bitval = G.check_metadata(prefill, w.threshold)
+    slot = w.slot_bytes
+    store, part, lengths = G.gpu_compress(rows, mask, bitval, w.chunk_bytes, slot, pinned=True)
+    o_store, o_part, _ = G.check_store(rows, mask, bitval, w.chunk_bytes, slot, store, part,
+                                       lengths)
+    ids = np.arange(2560)
+    got = G.gpu_gather(store, 2560 * slot, slot, None, part, 2560, ids, w.tensor_bytes,
+                       w.chunk_bytes, mask, bitval)
+    assert (got == rows).all()
+
+
+# ------------------------------------------------------------ geometry sweep
+
+SHAPES = [(4, 256), (12, 256), (260, 256), (508, 1024), (1028, 256), (2052, 1024),
+          (4100, 4096), (5732, 1024), (8196, 256), (10240, 256), (16384, 256), (16384, 4096)]
+
+
+@pytest.mark.parametrize("B,C", SHAPES)
+def test_geometry_sweep(B, C):
+    rng = np.random.default_rng(B * 7 + C)
+    n = 300 if B <= 4096 else 120
+    x = (rng.standard_normal((n, B // 4)) * rng.uniform(0.05, 3.0, B // 4)).astype(np.float32)
+    x[rng.random((n, B // 4)) < 0.01] = 0.0
+    rows = x.view(np.uint8)
+    full_roundtrip(f"sweep B={B} C={C}", rows, C, 0.9, batches=[rng.integers(0, n, 257),
+                                                                np.array([n - 1])])
+
+
+# ------------------------------------------------------------ degenerate cases
+
+def test_mask_zero_and_all_ones():
+    from host_transfer_amd import ibp
+    rng = np.random.default_rng(3)
+    B, C, n = 1024, 256, 200
+    rows = rng.integers(0, 256, (n, B), dtype=np.uint8)
+    zero = np.zeros(B // 4, np.uint32)
+    store, part, lens = G.gpu_compress(rows, zero, zero, C, B)
+    G.check_store(rows, zero, zero, C, B, store, part, lens)
+    assert (G.host(lens) == B).all() and not G.host(part).any()
+    ids = rng.integers(0, n, 99)
+    got = G.gpu_gather(store, n * B, B, None, part, n, ids, B, C, zero, zero)
+    assert (got == rows[ids]).all()
+    # identical tensors: Mask all ones, empty payloads, Bitval restores them
+    same = np.tile(rows[:1], (50, 1))
+    mask, bitval = G.check_metadata(same, 0.99)
+    assert (mask == 0xFFFFFFFF).all()
+    store, part, lens = G.gpu_compress(same, mask, bitval, C, B)
+    assert not G.host(lens).any()
+    got = G.gpu_gather(store, 50 * B, B, None, part, 50, [0, 49, 7], B, C, mask, bitval)
+    assert (got == same[:3]).all()
+
+
+def test_batch_edges_and_invalid_ids():
+    w = W.WORKLOADS["tiny"].scaled(1000)
+    rows = W.rows(w)
+    B, C, slot = w.tensor_bytes, w.chunk_bytes, w.slot_bytes
+    mask, bitval = G.check_metadata(rows, w.threshold)
+    store, part, lens = G.gpu_compress(rows, mask, bitval, C, slot)
+    for nb in (0, 1, 63, 64, 65, 255, 256, 257):
+        ids = (np.arange(nb) * 37) % 1000
+        got = G.gpu_gather(store, 1000 * slot, slot, None, part, 1000, ids, B, C, mask, bitval)
+        assert (got == rows[ids]).all(), nb
+    ids = np.array([5, -1, 1000, 999, 1 << 40, 5, 5])
+    got = G.gpu_gather(store, 1000 * slot, slot, None, part, 1000, ids, B, C, mask, bitval)
+    assert (got == G.expected_rows(rows, ids)).all()
+    assert not got[[1, 2, 4]].any()
+
+
+def test_deterministic_and_store_bound():
+    w = W.WORKLOADS["dense_gnn"].scaled(2000)
+    rows = W.rows(w)
+    B, C, slot = w.tensor_bytes, w.chunk_bytes, w.slot_bytes
+    mask, bitval = G.check_metadata(rows, w.threshold)
+    store, part, lens = G.gpu_compress(rows, mask, bitval, C, slot)
+    ids = np.random.default_rng(1).integers(0, 2000, 5000)
+    a = G.gpu_gather(store, 2000 * slot, slot, None, part, 2000, ids, B, C, mask, bitval)
+    b = G.gpu_gather(store, 2000 * slot, slot, None, part, 2000, ids, B, C, mask, bitval)
+    assert (a == b).all() and (a == rows[ids]).all()
+
+
+def test_compress_in_pieces_matches_whole():
+    """Tensors compressed in separate calls (first_tensor) equal one call."""
+    w = W.WORKLOADS["kv_opt13b"]
+    rows = W.rows(w, 0, 600)
+    mask, bitval = G.check_metadata(W.kv_prefill_rows(w, 0, 800), w.threshold)
+    slot, C = w.slot_bytes, w.chunk_bytes
+    s1, p1, l1 = G.gpu_compress(rows, mask, bitval, C, slot)
+    s2, p2, l2 = G.gpu_compress(rows[:250], mask, bitval, C, slot, n_tensors=600)
+    s2, p2, l2 = G.gpu_compress(rows[250:], mask, bitval, C, slot, n_tensors=600, first=250,
+                                store=s2, part=p2, lengths=l2)
+    G.check_store(rows[250:], mask, bitval, C, slot, s2, p2, l2, first=250, n_tensors=600)
+    assert (G.host(p1) == G.host(p2)).all() and (G.host(l1) == G.host(l2)).all()
+    ln = G.host(l1).view(np.uint32)
+    a = G.store_bytes(s1).reshape(600, slot)
+    b = G.store_bytes(s2).reshape(600, slot)
+    valid = np.arange(slot)[None, :] < ln[:, None].astype(np.int64)
+    assert (a[valid] == b[valid]).all()
+
+
+def test_raw_gather_and_stream_read():
+    from host_transfer_amd import ibp
+    rng = np.random.default_rng(11)
+    n, B, stride = 500, 5732, 5760
+    raw = rng.integers(0, 256, (n, stride), dtype=np.uint8)
+    hb = ibp.HostBuffer(n * stride)
+    hb.array[:] = raw.ravel()
+    ids = rng.integers(-2, n + 2, 300)
+    out = torch.zeros(300 * B, dtype=torch.int8, device="cuda")
+    ibp.raw_gather(hb, stride, n, G.dev(ids), 300, B, out)
+    got = G.host(out).view(np.uint8).reshape(300, B)
+    assert (got == G.expected_rows(raw[:, :B].copy(), ids)).all()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ibp.stream_read(hb, n * stride, 0x9E3779B9, sink)
+    torch.cuda.synchronize()
+    hb.free()
