@@ -101,9 +101,11 @@ Geometry make_geometry(uint32_t tensor_bytes, uint32_t chunk_bytes) {
   g.wpc_log2 = 0;
   while ((1u << g.wpc_log2) < chunk_bytes / 4) ++g.wpc_log2;
   g.last_bits = 8u * (tensor_bytes - (g.n_c - 1) * chunk_bytes);
-  // smallest group (threads per tensor) that keeps <= 8 words per thread
+  // smallest group (threads per tensor) that keeps <= 6 words per thread, so
+  // the per-word registers fit without spilling (and a payload of at most
+  // B <= 24*G bytes fits in two 16 B registers per thread)
   g.group = 64;
-  while (g.group * 8 < g.W) g.group *= 2;
+  while (g.group * 6 < g.W) g.group *= 2;
   g.J = (g.W + g.group - 1) / g.group;
   g.groups = g.group == 64 ? 4 : 1;
   return g;

@@ -200,8 +200,6 @@ hipError_t launch_compress(const Geometry& g, const uint8_t* rows, uint64_t row_
     case 4: return launch_j<4>(g, a, s);
     case 5: return launch_j<5>(g, a, s);
     case 6: return launch_j<6>(g, a, s);
-    case 7: return launch_j<7>(g, a, s);
-    case 8: return launch_j<8>(g, a, s);
     default: return hipErrorInvalidValue;
   }
 }

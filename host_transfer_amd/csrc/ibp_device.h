@@ -74,6 +74,35 @@ __host__ __device__ __forceinline__ uint32_t unpack_bits(uint32_t x, const uint3
   return x;
 }
 
+// One v_bfi_b32 (left to itself the compiler splits the insert into four
+// operations once several stages are chained).
+__device__ __forceinline__ uint32_t bfi_op(uint32_t m, uint32_t a, uint32_t b) {
+  uint32_t r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(a), "v"(b));
+  return r;
+}
+
+// unpack_bits restricted to the stages set in `stages` (bit s = stage of
+// 2^s positions).  `stages` must be uniform across the wave: a stage whose
+// move mask is zero on every lane leaves x unchanged and is skipped.
+__device__ __forceinline__ uint32_t unpack_stages(uint32_t x, const uint32_t mv[5],
+                                                  uint32_t stages) {
+  if (stages & 16u) x = bfi_op(mv[4], x << 16, x);
+  if (stages & 8u) x = bfi_op(mv[3], x << 8, x);
+  if (stages & 4u) x = bfi_op(mv[2], x << 4, x);
+  if (stages & 2u) x = bfi_op(mv[1], x << 2, x);
+  if (stages & 1u) x = bfi_op(mv[0], x << 1, x);
+  return x;
+}
+
+// 32 bits of the LDS bit stream starting at bit `off` (two words and a funnel
+// shift); the word after the last one read must be addressable.
+__device__ __forceinline__ uint32_t window32(const uint32_t* pb32, uint32_t off) {
+  const uint32_t d0 = pb32[off >> 5];
+  const uint32_t d1 = pb32[(off >> 5) + 1];
+  return __builtin_amdgcn_alignbit(d1, d0, off & 31u);
+}
+
 __device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
 
 // Orders LDS accesses among the lanes of one wave.

@@ -1,6 +1,6 @@
 // ibp_plan.h -- per-kernel preparation of the Mask/Bitval metadata (gfx950).
 //
-// A "group" of G threads (G = 64, 128, 256 or 512) handles one tensor at a
+// A "group" of G threads (G = 64, 128, ..., 1024) handles one tensor at a
 // time.  Thread gl of a group owns the output words w = gl + G*j, j < J, for
 // every tensor it touches, so everything that depends only on the metadata is
 // computed once per workgroup and kept in that thread's registers:
@@ -36,6 +36,7 @@ struct WordRegs {
   uint32_t mask[J];
   uint32_t bitval[J];
   uint32_t info[J];
+  uint32_t stages[J];  // wave-uniform: unpack stages with a non-zero move mask
 };
 
 // Workgroup-wide inclusive sum (blockDim.x a multiple of 64, <= 1024).
@@ -59,22 +60,25 @@ __device__ __forceinline__ uint32_t block_inclusive_sum(uint32_t v, uint32_t* s_
 
 // Builds the registers of thread gl and the K_c table.  Every thread of the
 // workgroup must call it.  s_pref: W+1 words of LDS (scratch), s_kc: 64 words.
+// The exclusive prefix of kept bits over all words takes one workgroup scan:
+// each thread sums a contiguous run of words, the runs are scanned, then each
+// thread writes the prefixes of its run.
 template <int J>
 __device__ void load_plan(const uint32_t* __restrict__ mask, const uint32_t* __restrict__ bitval,
                           const Shape& sh, uint32_t* s_pref, uint32_t* s_kc, uint32_t* s_wsum,
                           uint32_t gl, WordRegs<J>& R) {
   const uint32_t nt = blockDim.x, tid = threadIdx.x;
-  // exclusive prefix over all words of the number of kept (non-Mask) bits
-  uint32_t carry = 0;
-  for (uint32_t base = 0; base < sh.W; base += nt) {
-    const uint32_t w = base + tid;
-    const uint32_t k = w < sh.W ? (uint32_t)__popc(~mask[w]) : 0u;
-    uint32_t tot;
-    const uint32_t incl = block_inclusive_sum(k, s_wsum, &tot);
-    if (w < sh.W) s_pref[w] = carry + incl - k;
-    carry += tot;
+  const uint32_t per = (sh.W + nt - 1) / nt;
+  const uint32_t w0 = min(tid * per, sh.W), w1 = min(w0 + per, sh.W);
+  uint32_t local = 0;
+  for (uint32_t w = w0; w < w1; ++w) local += (uint32_t)__popc(~mask[w]);
+  uint32_t total;
+  uint32_t run = block_inclusive_sum(local, s_wsum, &total) - local;
+  for (uint32_t w = w0; w < w1; ++w) {
+    s_pref[w] = run;
+    run += (uint32_t)__popc(~mask[w]);
   }
-  if (tid == 0) s_pref[sh.W] = carry;
+  if (tid == 0) s_pref[sh.W] = total;
   __syncthreads();
   for (uint32_t c = tid; c < sh.n_c; c += nt) {
     const uint32_t lo = c << sh.wpc_log2;
@@ -98,6 +102,10 @@ __device__ void load_plan(const uint32_t* __restrict__ mask, const uint32_t* __r
       R.bitval[j] = 0;
       R.info[j] = 0;
     }
+    uint32_t st = 0;
+#pragma unroll
+    for (int s = 0; s < 5; ++s) st |= (__ballot(R.mv[j][s] != 0u) != 0ull ? 1u : 0u) << s;
+    R.stages[j] = uniform(st);
   }
   __syncthreads();
 }
