@@ -16,8 +16,8 @@ link, and the transfer speedup over an uncompressed GPU gather of the same
 rows ([JH] Table 1 discussion: transfer speedup against plain transfers).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sparse_gnn]
-       [--hbm-workload dense_gnn|dlrm_1k|none] [--host-flags default|coherent|noncoherent]
-       [--no-cpu-baseline] [--threshold T]
+       [--hbm-workloads dense_gnn,dlrm_1k|none] [--hbm-large-batch N]
+       [--host-flags default|coherent|noncoherent] [--no-cpu-baseline] [--threshold T]
 """
 import argparse
 import json
@@ -35,6 +35,33 @@ if ROOT not in sys.path:
 PCIE5_X16_GBPS = 63.0      # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes x 128/130 / 8
 HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E
 
+# HBM/host traffic of the headline launch from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE (KiB per dispatch), scaled by what the same counters read for
+# transfers of known size (factors below).  Valid only for the gather sources
+# they were measured on: bench.py reports them while the sources still hash
+# to GATHER_SOURCES_SHA256, else traffic is null.
+GATHER_SOURCES = ("host_transfer_amd/csrc/gather.hip", "host_transfer_amd/csrc/ibp_plan.h",
+                  "host_transfer_amd/csrc/ibp_device.h")
+GATHER_SOURCES_SHA256 = "77fe701e856413d579c6278de9a5f660ee9e4bdd9ebbbc98f77fff9ba36711a0"
+TRAFFIC_FETCH_KIB, TRAFFIC_WRITE_KIB = 6079.2, 46080.3  # sparse_gnn, 8,192 ids
+FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+
+
+def gather_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in GATHER_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def profiled_traffic():
+    """Scaled bytes per launch from the committed counters, or None."""
+    if GATHER_SOURCES_SHA256 is None or gather_sources_sha256() != GATHER_SOURCES_SHA256:
+        return None
+    return round(TRAFFIC_FETCH_KIB * 1024 * FETCH_SCALE + TRAFFIC_WRITE_KIB * 1024 * WRITE_SCALE)
+
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -46,7 +73,9 @@ def parse():
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="sparse_gnn")
-    p.add_argument("--hbm-workload", default="dense_gnn")
+    p.add_argument("--hbm-workloads", default="dense_gnn,dlrm_1k",
+                   help="comma-separated workloads measured as compressed HBM caches, or 'none'")
+    p.add_argument("--hbm-large-batch", type=int, default=1 << 20)
     p.add_argument("--host-flags", default="default", choices=["default", "coherent", "noncoherent"])
     p.add_argument("--threshold", type=float, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -296,6 +325,79 @@ def measure_workload(torch, ibp, W, key, T, where, host_flags, steps, warmup, wi
     return res
 
 
+def measure_hbm(torch, ibp, W, key, flags, args, pr):
+    """The gather kernel on a compacted HBM cache: Table-D batch and a large
+    batch, with the uncompressed HBM gather of the same ids beside it."""
+    import numpy as np
+    w = W.WORKLOADS[key]
+    table = Table(torch, ibp, W, w, w.threshold, "hbm", flags, keep_raw=True)
+    B, S, N = w.tensor_bytes, w.slot_bytes, w.n_tensors
+    raw_dev = torch.from_numpy(table.raw.array).cuda()   # uncompressed rows in HBM
+    table.raw.free()
+    res = {"workload": f"{key}: {N} x {B} B, compacted cache of {table.store_bytes / 1e9:.2f} GB in "
+                       f"HBM (mean payload {table.len_host.mean() / B:.4f} of the tensor)",
+           "batches": []}
+    for nb in (w.batch, args.hbm_large_batch):
+        nbatches = (nb + w.batch - 1) // w.batch
+        steps = max(3, min(args.steps, (64 << 20) // max(1, nb)))
+        seqs = []
+        for k in range(args.warmup + steps):
+            ids = np.concatenate([W.batch_ids(w, k * nbatches + i) for i in range(nbatches)])[:nb]
+            seqs.append(ids)
+        d = [torch.from_numpy(i).cuda() for i in seqs]
+        out = torch.empty(nb * B, dtype=torch.uint8, device="cuda")
+
+        def run_ibp(k):
+            ibp.gather_decompress(table.store, table.store_bytes, S, table.offsets, table.part, N,
+                                  d[k], nb, B, w.chunk_bytes, table.mask, table.bitval, out)
+
+        def run_raw(k):
+            ibp.raw_gather(raw_dev, S, N, d[k], nb, B, out)
+        kms = timed_launches(torch, run_ibp, args.warmup, steps)
+        rms = timed_launches(torch, run_raw, args.warmup, steps)
+        last = seqs[-1]
+        run_ibp(len(seqs) - 1)
+        torch.cuda.synchronize()
+        pick = np.linspace(0, nb - 1, 256).astype(np.int64)
+        got = out.view(nb, B)[torch.from_numpy(pick).cuda()].cpu().numpy()
+        want = raw_dev.view(N, S)[torch.from_numpy(last[pick]).cuda(), :B].cpu().numpy()
+        if not (got == want).all():
+            raise SystemExit(f"bench: {key} HBM gather differs from the original rows")
+        km, rm = statistics.mean(kms), statistics.mean(rms)
+        comp = statistics.mean(float(table.len_host[i].sum()) for i in seqs[args.warmup:])
+        traffic = comp + nb * (B + 16)
+        res["batches"].append({
+            "ids": nb, "kernel_us": round(km * 1e3, 2),
+            "decompressed_GBps": round(nb * B / (km * 1e-3) / 1e9, 1),
+            "roofline": {"bound": "hbm", "achieved": round(traffic / (km * 1e-3) / 1e9, 1),
+                         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(traffic / (km * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                         "frac_of_measured_read": round(traffic / (km * 1e-3) / 1e9 /
+                                                        pr["hbm_stream_read_GBps"], 4)},
+            "raw_hbm_gather_us": round(rm * 1e3, 2),
+            "speedup_vs_raw_hbm_gather": round(rm / km, 3),
+            "unique_ids": int(len(np.unique(last))),
+        })
+        del out, d
+    res["compact_ms"] = round(table.compact_ms, 3)
+    del raw_dev, table
+    torch.cuda.empty_cache()
+    return res
+
+
+def timed_launches(torch, fn, warmup, steps):
+    """HIP-event duration (ms) of each of `steps` launches after `warmup`."""
+    for k in range(warmup):
+        fn(k)
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    for k in range(warmup, warmup + steps):
+        s = tm.start()
+        fn(k)
+        tm.stop(s)
+    return tm.ms()
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -359,9 +461,11 @@ def main():
             "peak": PCIE5_X16_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / PCIE5_X16_GBPS, 4),
-            "traffic": None,
+            "traffic": profiled_traffic(),
             "peak_measured": round(link_peak, 2),
             "frac_of_measured": round(achieved / link_peak, 4),
+            "peak_zero_copy_read": pr["h2d_zero_copy_read_GBps"],
+            "frac_of_zero_copy_read": round(achieved / pr["h2d_zero_copy_read_GBps"], 4),
             "kernel": "k_gather_decompress",
             "kernel_us": round(kern_ms * 1e3, 2),
             "bytes_per_launch": round(comp, 1),
@@ -388,26 +492,12 @@ def main():
     del table, m
     torch.cuda.empty_cache()
 
-    # --- the same kernel on a compressed cache in HBM
-    if args.hbm_workload != "none":
-        hk = args.hbm_workload
-        h = measure_workload(torch, ibp, W, hk, None, "hbm", flags, args.steps, args.warmup,
-                             with_raw=False)
-        hw, ht = W.WORKLOADS[hk], h["table"]
-        hk_ms = statistics.mean(h["kernel_ms"])
-        hbytes = statistics.mean(h["comp_bytes"]) + hw.batch * (hw.tensor_bytes + 16)
-        ach = hbytes / (hk_ms * 1e-3) / 1e9
-        result["hbm_path"] = {
-            "workload": f"{hk}: {hw.n_tensors} x {hw.tensor_bytes} B compacted cache "
-                        f"({ht.store_bytes / 1e9:.2f} GB) in HBM, {hw.batch} ids ({hw.id_law})",
-            "decompressed_GBps": round(hw.batch * hw.tensor_bytes / (hk_ms * 1e-3) / 1e9, 2),
-            "kernel_us": round(hk_ms * 1e3, 2),
-            "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS,
-                         "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
-                         "frac_of_measured": round(ach / pr["hbm_stream_read_GBps"], 4)},
-            "compact_ms": round(ht.compact_ms, 3),
-        }
-        ht.raw.free()
+    # --- the same kernel on compressed caches in HBM: the Table-D batch and a
+    #     large batch (1M ids) that fills the GPU
+    result["hbm_path"] = []
+    if args.hbm_workloads != "none":
+        for hk in args.hbm_workloads.split(","):
+            result["hbm_path"].append(measure_hbm(torch, ibp, W, hk, flags, args, pr))
     print(json.dumps(result), flush=True)
 
 

@@ -44,7 +44,6 @@ struct GatherArgs {
   Shape sh;
   uint32_t groups;      // groups per workgroup
   uint32_t pbuf_bytes;  // LDS payload buffer per group
-  uint32_t lpr;         // tile kernel: lanes per tensor in the load phase
 };
 
 // LDS layout, in bytes from the start of dynamic shared memory.  Per group:
@@ -63,6 +62,13 @@ struct GatherLds {
   __host__ __device__ uint32_t total(uint32_t groups) const { return group0 + groups * group_stride; }
 };
 
+// 16 zero bytes in device memory: lanes with nothing to load read this
+// instead of skipping the load, so every wave issues the same number of
+// vector memory operations on every path and the compiler's in-order wait
+// counts stay exact (a skipped load would force waits for everything in
+// flight, stores and prefetches included).
+__device__ __align__(16) uint4 g_zero16 = {0u, 0u, 0u, 0u};
+
 // What the first wave knows about one tensor before its payload is read.
 struct RowMeta {
   uint64_t base;  // payload offset in the store
@@ -70,23 +76,24 @@ struct RowMeta {
   bool valid;
 };
 
+// The id of row `row`, or -1 past the batch.  The load itself is
+// unconditional (clamped row): see g_zero16.
 __device__ __forceinline__ int64_t load_id(const GatherArgs& a, uint64_t row) {
-  return row < a.n_ids ? a.ids[row] : -1;
+  const int64_t id = a.ids[row < a.n_ids ? row : a.n_ids - 1];
+  return row < a.n_ids ? id : -1;
 }
 
 // Participation word and payload offset of tensor `id` (lane c: chunk c).
+// Unconditional loads: an invalid id reads tensor 0's entries, ignored later.
 __device__ __forceinline__ RowMeta load_meta(const GatherArgs& a, int64_t id, uint32_t lane) {
   RowMeta m;
   m.valid = id >= 0 && (uint64_t)id < a.n_tensors;
-  m.bits = 0;
-  m.base = 0;
-  if (m.valid) {
-    if (lane < a.sh.n_c) {
-      const uint64_t bit = (uint64_t)id * a.sh.n_c + lane;
-      m.bits = a.part_bits[bit >> 5] >> (bit & 31);
-    }
-    m.base = a.offsets ? a.offsets[id] : (uint64_t)id * a.slot_bytes;
-  }
+  const uint64_t t = m.valid ? (uint64_t)id : 0ull;
+  const uint32_t c = min(lane % kWave, a.sh.n_c - 1u);
+  const uint64_t bit = t * a.sh.n_c + c;
+  m.bits = a.part_bits[bit >> 5] >> (bit & 31);
+  m.base = *(a.offsets ? a.offsets + t : (const uint64_t*)&g_zero16) +
+           (a.offsets ? 0ull : t * a.slot_bytes);
   return m;
 }
 
@@ -144,34 +151,30 @@ __global__ __launch_bounds__(1024) void k_gather_decompress(GatherArgs a) {
   // for a payload still in flight (vector loads retire in issue order):
   // ids three tensors ahead, participation words and offsets two ahead, the
   // scan one ahead.
-  int64_t id_a = -1, id_b = -1;
-  if (first_wave) {
-    id_a = load_id(a, row0);
-    id_b = load_id(a, row0 + step);
-  }
+  // (every wave loads the few metadata bytes, so no load sits behind a
+  // branch; only the first wave uses them)
+  const int64_t id_a = load_id(a, row0);
+  const int64_t id_b = load_id(a, row0 + step);
 
   WordRegs<J> R;
   load_plan<J>(a.mask, a.bitval, a.sh, s_pref, s_kc, s_wsum, gl, R);
 
   if (row0 >= a.n_ids) return;  // uniform per group; no workgroup barrier follows for it
-  RowMeta meta_next;             // tensor row+step (first wave)
-  int64_t id_next2 = -1;         // tensor row+2*step (first wave)
-  if (first_wave) {
-    const RowMeta m0 = load_meta(a, id_a, gl);
-    meta_next = load_meta(a, id_b, gl);
-    id_next2 = load_id(a, row0 + 2 * step);
-    scan_row(a, m0, gl, s_kc, &hdrs[0], obufs);
-  }
+  const RowMeta m0 = load_meta(a, id_a, gl);
+  RowMeta meta_next = load_meta(a, id_b, gl);      // tensor row+step
+  int64_t id_next2 = load_id(a, row0 + 2 * step);  // tensor row+2*step
+  if (first_wave) scan_row(a, m0, gl, s_kc, &hdrs[0], obufs);
   group_sync(single);
 
-  // payload registers of the tensor in flight
-  uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
+  // payload registers of the tensor in flight; lanes past the payload read
+  // g_zero16 rather than skip the load (exact wait counts, see g_zero16)
+  uint4 v0, v1;
   {
     const GroupHdr h = hdrs[0];
     const uint32_t n16 = payload_units(a, h);
     const uint4* src = (const uint4*)(a.store + h.base);
-    if (gl < n16) v0 = src[gl];
-    if (gl + G < n16) v1 = src[gl + G];
+    v0 = *(gl < n16 ? src + gl : &g_zero16);
+    v1 = *(gl + G < n16 ? src + gl + G : &g_zero16);
   }
 
   uint32_t cur = 0;
@@ -189,16 +192,14 @@ __global__ __launch_bounds__(1024) void k_gather_decompress(GatherArgs a) {
     group_sync(single);
     // 3. metadata two and three tensors ahead, then the next payload, all
     //    before this tensor is decoded
-    if (first_wave) {
-      meta_next = load_meta(a, id_next2, gl);
-      id_next2 = load_id(a, row + 3 * step);
-    }
-    if (has_next) {
+    meta_next = load_meta(a, id_next2, gl);
+    id_next2 = load_id(a, row + 3 * step);
+    {
       const GroupHdr hn = hdrs[cur ^ 1u];
-      const uint32_t n16 = payload_units(a, hn);
+      const uint32_t n16 = has_next ? payload_units(a, hn) : 0u;
       const uint4* src = (const uint4*)(a.store + hn.base);
-      if (gl < n16) v0 = src[gl];
-      if (gl + G < n16) v1 = src[gl + G];
+      v0 = *(gl < n16 ? src + gl : &g_zero16);
+      v1 = *(gl + G < n16 ? src + gl + G : &g_zero16);
     }
     // 4. decode this tensor's words and store them.  With chunks of at least
     //    64 words, the 64 words a wave handles for one j lie in one chunk, so
@@ -261,7 +262,9 @@ struct TileHdr {
   uint32_t off[3];  // bit offsets of chunks 1..3 (chunk 0 starts at 0)
 };
 
-// Per-lane (lane i < T) metadata of tensor i of a tile, loaded ahead of use.
+// Per-lane metadata of tensor (lane % T) of a tile, loaded ahead of use.
+// Every lane loads (lanes >= T duplicate lane % T) and ids are clamped into
+// range, so the loads are unconditional.
 struct TileMeta {
   uint64_t base;
   uint32_t w0, w1;  // bitmap words holding the tensor's chunk bits
@@ -269,18 +272,23 @@ struct TileMeta {
   bool valid;
 };
 
+__device__ __forceinline__ int64_t tile_row_id(const GatherArgs& a, uint64_t row) {
+  return a.ids[row < a.n_ids ? row : a.n_ids - 1];
+}
+
 __device__ __forceinline__ TileMeta load_tile_meta(const GatherArgs& a, int64_t id) {
   TileMeta m;
   m.valid = id >= 0 && (uint64_t)id < a.n_tensors;
-  m.base = 0;
-  m.w0 = m.w1 = m.sh = 0;
-  if (m.valid) {
-    const uint64_t bit = (uint64_t)id * a.sh.n_c;
-    m.sh = bit & 31;
-    m.w0 = a.part_bits[bit >> 5];
-    if (m.sh + a.sh.n_c > 32) m.w1 = a.part_bits[(bit >> 5) + 1];
-    m.base = a.offsets ? a.offsets[id] : (uint64_t)id * a.slot_bytes;
-  }
+  const uint64_t t = m.valid ? (uint64_t)id : 0ull;
+  const uint64_t bit = t * a.sh.n_c;
+  const uint64_t q = bit >> 5;
+  const uint64_t last_word = (a.n_tensors * a.sh.n_c - 1) >> 5;
+  m.sh = bit & 31;
+  m.w0 = a.part_bits[q];
+  m.w1 = a.part_bits[q < last_word ? q + 1 : q];
+  // one load on both layouts (offset table, or zero plus the slot offset)
+  m.base = *(a.offsets ? a.offsets + t : (const uint64_t*)&g_zero16) +
+           (a.offsets ? 0ull : t * a.slot_bytes);
   return m;
 }
 
@@ -289,30 +297,55 @@ __device__ __forceinline__ TileHdr make_tile_hdr(const GatherArgs& a, const Tile
   TileHdr h;
   h.valid = m.valid;
   h.base = m.base;
-  h.len = 0;
-  h.pmask = 0;
-  h.off[0] = h.off[1] = h.off[2] = 0;
-  if (m.valid) {
-    const uint32_t n_c = a.sh.n_c;
-    const uint64_t word = (uint64_t)m.w0 | ((uint64_t)m.w1 << 32);
-    const uint32_t pm = (uint32_t)(word >> m.sh) & ((1u << n_c) - 1u);
-    uint32_t o = 0, offs[4];
+  const uint32_t n_c = a.sh.n_c;
+  const uint64_t word = (uint64_t)m.w0 | ((uint64_t)m.w1 << 32);
+  const uint32_t pm = m.valid ? (uint32_t)(word >> m.sh) & ((1u << n_c) - 1u) : 0u;
+  uint32_t o = 0, offs[4];
 #pragma unroll
-    for (uint32_t c = 0; c < 4; ++c) {  // n_c <= 4; chunks past n_c add nothing
-      offs[c] = o;
-      if (c < n_c) o += ((pm >> c) & 1u) ? s_kc[c] : chunk_bits(a.sh, c);
-    }
-    h.off[0] = offs[1];
-    h.off[1] = offs[2];
-    h.off[2] = offs[3];
-    h.pmask = pm;
-    h.len = (o + 7u) >> 3;
+  for (uint32_t c = 0; c < 4; ++c) {  // n_c <= 4; chunks past n_c add nothing
+    offs[c] = o;
+    if (c < n_c) o += ((pm >> c) & 1u) ? s_kc[c] : chunk_bits(a.sh, c);
   }
+  h.off[0] = offs[1];
+  h.off[1] = offs[2];
+  h.off[2] = offs[3];
+  h.pmask = pm;
+  h.len = m.valid ? (o + 7u) >> 3 : 0u;
   return h;
 }
 
-template <int J, int T>
+// Number of 16 B units to read for a header: the payload rounded up to 16 B,
+// never past store_bytes.
+__device__ __forceinline__ uint32_t tile_units(const GatherArgs& a, const TileHdr& h) {
+  const uint64_t avail = h.base < a.store_bytes ? (a.store_bytes - h.base) & ~15ull : 0ull;
+  return (uint32_t)(min((uint64_t)((h.len + 15u) & ~15u), avail) >> 4);
+}
+
+// Decodes word j of one tensor of a tile (chunk, participation and offset
+// wave-uniform, see below).
+template <int J>
+__device__ __forceinline__ uint32_t tile_word(const GatherArgs& a, const WordRegs<J>& R, int j,
+                                              const uint32_t* pb32, uint32_t pm, uint32_t o1,
+                                              uint32_t o2, uint32_t o3) {
+  const uint32_t c = ((uint32_t)kWave * j) >> a.sh.wpc_log2;  // uniform
+  const uint32_t o = c == 0 ? 0u : c == 1 ? o1 : c == 2 ? o2 : o3;
+  uint32_t v;
+  if ((pm >> c) & 1u) {
+    v = window32(pb32, o + (R.info[j] & 0xFFFFu));
+    v = bfi_op(R.mask[j], R.bitval[j], unpack_stages(v, R.mv[j], R.stages[j]));
+  } else {
+    v = window32(pb32, o + (R.info[j] >> 16));
+  }
+  return v;
+}
+
+// RPI tensors per load instruction (LPR = 64/RPI lanes each, one 16 B unit
+// per lane: LPR >= the payload's units).  FULL: W == 64*J, so every lane has
+// a word in every j.
+template <int J, int T, int RPI, bool FULL>
 __global__ __launch_bounds__(256) void k_gather_tile(GatherArgs a) {
+  constexpr uint32_t LPR = kWave / RPI;
+  constexpr int NL = T / RPI;  // load instructions per tile
   extern __shared__ __align__(16) uint8_t smem[];
   const GatherLds L(a.sh.W, a.pbuf_bytes);  // pref/kc/wsum as the group kernel
   uint32_t* s_pref = (uint32_t*)(smem + L.pref);
@@ -325,21 +358,16 @@ __global__ __launch_bounds__(256) void k_gather_tile(GatherArgs a) {
   uint8_t* pbufs = wbase + 2 * T * sizeof(TileHdr);
 
   const uint32_t W = a.sh.W;
-  const uint32_t lpr = a.lpr;  // lanes per tensor in the load phase
-  const uint32_t rpi = kWave / lpr;
   const uint64_t n_tiles = (a.n_ids + T - 1) / T;
+  const uint64_t n_full = a.n_ids / T;  // tiles whose T rows all exist
   const uint64_t waves = (uint64_t)gridDim.x * (blockDim.x / kWave);
   const uint64_t tile0 = (uint64_t)blockIdx.x * (blockDim.x / kWave) + wave;
-  const bool meta_lane = lane < (uint32_t)T;
-  auto row_id = [&](uint64_t tile) -> int64_t {
-    const uint64_t row = tile * T + lane;
-    return (meta_lane && tile < n_tiles && row < a.n_ids) ? a.ids[row] : -1;
-  };
+  const uint32_t mrow = lane % T;  // the tile row this lane's metadata is for
 
-  // Tile metadata runs ahead of the payloads (vector loads retire in issue
-  // order): ids three tiles ahead, bitmap words and offsets two ahead, the
-  // headers one ahead.
-  const int64_t id_a = row_id(tile0), id_b = row_id(tile0 + waves);
+  // Tile metadata runs ahead of the payloads: ids three tiles ahead, bitmap
+  // words and offsets two ahead, the headers one ahead.
+  const int64_t id_a = tile_row_id(a, tile0 * T + mrow);
+  const int64_t id_b = tile_row_id(a, (tile0 + waves) * T + mrow);
 
   WordRegs<J> R;
   load_plan<J>(a.mask, a.bitval, a.sh, s_pref, s_kc, s_wsum, lane, R);
@@ -348,32 +376,31 @@ __global__ __launch_bounds__(256) void k_gather_tile(GatherArgs a) {
   TileMeta meta_next = load_tile_meta(a, id_b);
   {
     const TileMeta m0 = load_tile_meta(a, id_a);
-    if (meta_lane) hdrs[lane] = make_tile_hdr(a, m0, s_kc);
+    if (lane < (uint32_t)T) hdrs[lane] = make_tile_hdr(a, m0, s_kc);
   }
-  int64_t id_next2 = row_id(tile0 + 2 * waves);
+  int64_t id_next2 = tile_row_id(a, (tile0 + 2 * waves) * T + mrow);
   wave_sync();
 
-  uint4 v[T];
-  uint32_t n16s[T];
-  auto issue_loads = [&](const TileHdr* hdr) {
-#pragma unroll
-    for (int k = 0; k < T; ++k) {
-      n16s[k] = 0;
-      v[k] = make_uint4(0, 0, 0, 0);
-      if ((uint32_t)k * rpi >= (uint32_t)T) continue;
-      const uint32_t i = k * rpi + lane / lpr;
-      const uint32_t u = lane % lpr;
-      const TileHdr& h = hdr[i];
-      uint32_t n16 = 0;
-      if (h.valid) {
-        const uint64_t avail = h.base < a.store_bytes ? (a.store_bytes - h.base) & ~15ull : 0ull;
-        n16 = (uint32_t)(min((uint64_t)((h.len + 15u) & ~15u), avail) >> 4);
-      }
-      n16s[k] = n16;
-      if (u < n16) v[k] = ((const uint4*)(a.store + h.base))[u];
-    }
-  };
-  issue_loads(hdrs);
+  // payload registers of the tile in flight: NL <= 8 named registers (an
+  // array would be indexed through scratch memory)
+  static_assert(NL <= 8, "at most 8 load instructions per tile");
+  uint4 v0, v1, v2, v3, v4, v5, v6, v7;
+  uint32_t n0 = 0, n1 = 0, n2 = 0, n3 = 0, n4 = 0, n5 = 0, n6 = 0, n7 = 0;
+  const uint32_t lrow = lane / LPR, lunit = lane % LPR;
+#define IBP_TILE_LOAD(k, hdr)                                                                  \
+  if constexpr (k < NL) {                                                                      \
+    const TileHdr& h_ = (hdr)[k * RPI + lrow];                                                 \
+    n##k = tile_units(a, h_);                                                                  \
+    v##k = *(lunit < n##k ? (const uint4*)(a.store + h_.base) + lunit : &g_zero16);            \
+  }
+#define IBP_TILE_ISSUE_LOADS(hdr)                                                              \
+  IBP_TILE_LOAD(0, hdr) IBP_TILE_LOAD(1, hdr) IBP_TILE_LOAD(2, hdr) IBP_TILE_LOAD(3, hdr)      \
+  IBP_TILE_LOAD(4, hdr) IBP_TILE_LOAD(5, hdr) IBP_TILE_LOAD(6, hdr) IBP_TILE_LOAD(7, hdr)
+#define IBP_TILE_STAGE(k)                                                                      \
+  if constexpr (k < NL) {                                                                      \
+    if (lunit < n##k) ((uint4*)(pbufs + (k * RPI + lrow) * a.pbuf_bytes))[lunit] = v##k;       \
+  }
+  IBP_TILE_ISSUE_LOADS(hdrs)
 
   uint32_t cur = 0;
   for (uint64_t tile = tile0; tile < n_tiles; tile += waves, cur ^= 1u) {
@@ -381,67 +408,69 @@ __global__ __launch_bounds__(256) void k_gather_tile(GatherArgs a) {
     TileHdr* hcur = hdrs + cur * T;
     TileHdr* hnext = hdrs + (cur ^ 1u) * T;
     // a. this tile's payloads -> LDS
-#pragma unroll
-    for (int k = 0; k < T; ++k) {
-      if ((uint32_t)k * rpi >= (uint32_t)T) continue;
-      const uint32_t i = k * rpi + lane / lpr;
-      const uint32_t u = lane % lpr;
-      if (u < n16s[k]) ((uint4*)(pbufs + i * a.pbuf_bytes))[u] = v[k];
+    IBP_TILE_STAGE(0) IBP_TILE_STAGE(1) IBP_TILE_STAGE(2) IBP_TILE_STAGE(3)
+    IBP_TILE_STAGE(4) IBP_TILE_STAGE(5) IBP_TILE_STAGE(6) IBP_TILE_STAGE(7)
+    // b. next tile's headers (metadata loaded an iteration ago); past the
+    //    last tile they are invalid, so its loads below read only g_zero16
+    if (lane < (uint32_t)T) {
+      TileHdr h = make_tile_hdr(a, meta_next, s_kc);
+      if (!has_next) h.valid = 0, h.len = 0, h.base = 0;
+      hnext[lane] = h;
     }
-    // b. next tile's headers (metadata loaded an iteration ago)
-    if (has_next && meta_lane) hnext[lane] = make_tile_hdr(a, meta_next, s_kc);
     wave_sync();
     // c. metadata two and three tiles ahead, d. next tile's payload loads
     meta_next = load_tile_meta(a, id_next2);
-    id_next2 = row_id(tile + 3 * waves);
-    if (has_next) issue_loads(hnext);
+    id_next2 = tile_row_id(a, (tile + 3 * waves) * T + mrow);
+    IBP_TILE_ISSUE_LOADS(hnext)
     // e. decode this tile and store it.  Chunks hold at least 64 words, so
     //    the 64 words lane l handles for one j lie in one chunk: chunk,
     //    participation and offset are wave-uniform.
     const uint64_t row0 = tile * T;
-    for (int i = 0; i < T; ++i) {
-      const uint64_t row = row0 + i;
-      if (row >= a.n_ids) break;
-      const TileHdr* hp = hcur + i;
-      uint32_t* orow = a.out + row * W;
-      if (!uniform(hp->valid)) {
+    if (tile < n_full) {
+#pragma unroll 1
+      for (int i = 0; i < T; ++i) {
+        const TileHdr* hp = hcur + i;
+        const bool valid = uniform(hp->valid) != 0u;
+        const uint32_t pm = uniform(hp->pmask);
+        const uint32_t o1 = uniform(hp->off[0]), o2 = uniform(hp->off[1]), o3 = uniform(hp->off[2]);
+        const uint32_t* pb32 = (const uint32_t*)(pbufs + i * a.pbuf_bytes);
+        uint32_t* orow = a.out + (row0 + i) * W;
 #pragma unroll
         for (int j = 0; j < J; ++j) {
           const uint32_t w = lane + kWave * j;
-          if (w < W) orow[w] = 0u;
+          const uint32_t val = tile_word<J>(a, R, j, pb32, pm, o1, o2, o3);
+          if (FULL || w < W) orow[w] = valid ? val : 0u;
         }
-        continue;
       }
-      const uint32_t pm = uniform(hp->pmask);
-      const uint32_t o1 = uniform(hp->off[0]), o2 = uniform(hp->off[1]), o3 = uniform(hp->off[2]);
-      const uint32_t* pb32 = (const uint32_t*)(pbufs + i * a.pbuf_bytes);
+    } else {
+      // the last, partial tile
+      for (int i = 0; i < T; ++i) {
+        const uint64_t row = row0 + i;
+        if (row >= a.n_ids) break;
+        const TileHdr* hp = hcur + i;
+        const bool valid = uniform(hp->valid) != 0u;
+        const uint32_t pm = uniform(hp->pmask);
+        const uint32_t o1 = uniform(hp->off[0]), o2 = uniform(hp->off[1]), o3 = uniform(hp->off[2]);
+        const uint32_t* pb32 = (const uint32_t*)(pbufs + i * a.pbuf_bytes);
+        uint32_t* orow = a.out + row * W;
 #pragma unroll
-      for (int j = 0; j < J; ++j) {
-        const uint32_t w = lane + kWave * j;
-        const uint32_t c = (kWave * j) >> a.sh.wpc_log2;  // uniform
-        const uint32_t o = c == 0 ? 0u : c == 1 ? o1 : c == 2 ? o2 : o3;
-        uint32_t v;
-        if ((pm >> c) & 1u) {
-          v = window32(pb32, o + (R.info[j] & 0xFFFFu));
-          v = bfi_op(R.mask[j], R.bitval[j], unpack_stages(v, R.mv[j], R.stages[j]));
-        } else {
-          v = window32(pb32, o + (R.info[j] >> 16));
+        for (int j = 0; j < J; ++j) {
+          const uint32_t w = lane + kWave * j;
+          const uint32_t val = tile_word<J>(a, R, j, pb32, pm, o1, o2, o3);
+          if (w < W) orow[w] = valid ? val : 0u;
         }
-        if (w < W) orow[w] = v;
       }
+      break;  // it is the last tile
     }
     wave_sync();
   }
+#undef IBP_TILE_ISSUE_LOADS
+#undef IBP_TILE_LOAD
+#undef IBP_TILE_STAGE
 }
 
-template <int J, int T>
+template <int J, int T, int RPI, bool FULL>
 static hipError_t launch_tile(const Geometry& g, GatherArgs a, hipStream_t s) {
-  // lanes per tensor in the load phase: the payload's 16 B units, rounded up
-  // to a power of two, at most 64
-  const uint32_t units = ((g.tensor_bytes + 15u) & ~15u) / 16u;
-  uint32_t lpr = 64;
-  while (lpr / 2 >= units && lpr > 16) lpr /= 2;
-  a.lpr = lpr;
   a.sh.group = kWave;  // lane l owns words l + 64j
   const uint32_t waves = 4;
   const GatherLds L(g.W, a.pbuf_bytes);
@@ -450,15 +479,33 @@ static hipError_t launch_tile(const Geometry& g, GatherArgs a, hipStream_t s) {
   hipError_t e = device_info(&di);
   if (e != hipSuccess) return e;
   int per_cu = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gather_tile<J, T>, waves * 64, lds);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gather_tile<J, T, RPI, FULL>,
+                                                   waves * 64, lds);
   if (e != hipSuccess) return e;
   if (per_cu < 1) return hipErrorInvalidConfiguration;
   const uint64_t tiles = (a.n_ids + T - 1) / T;
   const uint64_t want = (tiles + waves - 1) / waves;
   const uint64_t cap = (uint64_t)per_cu * (uint64_t)di.cus;
   const uint32_t blocks = (uint32_t)(want < cap ? want : cap);
-  hipLaunchKernelGGL((k_gather_tile<J, T>), dim3(blocks), dim3(waves * 64), lds, s, a);
+  hipLaunchKernelGGL((k_gather_tile<J, T, RPI, FULL>), dim3(blocks), dim3(waves * 64), lds, s, a);
   return hipGetLastError();
+}
+
+// Small tensors (W <= 256): rows per load instruction RPI from the payload's
+// 16 B units (J fixes them: J = 1 -> <= 16 units, 2 -> <= 32, 3 and 4 ->
+// <= 64), and NL load instructions per tile: 8 when the batch gives every CU
+// at least 8 waves of such tiles, else 2 (short batches need many waves in
+// flight more than they need the per-tile overhead amortised).
+template <int J, int RPI>
+static hipError_t launch_small(const Geometry& g, const GatherArgs& a, hipStream_t s) {
+  DeviceInfo di;
+  hipError_t e = device_info(&di);
+  if (e != hipSuccess) return e;
+  const bool full = g.W == (uint32_t)kWave * J;
+  const bool big = a.n_ids >= (uint64_t)8 * RPI * 8 * (uint64_t)di.cus;
+  if (big)
+    return full ? launch_tile<J, 8 * RPI, RPI, true>(g, a, s) : launch_tile<J, 8 * RPI, RPI, false>(g, a, s);
+  return full ? launch_tile<J, 2 * RPI, RPI, true>(g, a, s) : launch_tile<J, 2 * RPI, RPI, false>(g, a, s);
 }
 
 template <int J>
@@ -486,6 +533,8 @@ hipError_t launch_gather(const Geometry& g, const uint8_t* store, uint64_t store
                          const uint32_t* mask, const uint32_t* bitval, uint32_t* out,
                          hipStream_t s) {
   if (n_ids == 0) return hipSuccess;
+  // no tensors: every id is out of range and every row is zero
+  if (n_tensors == 0) return launch_fill_u32(out, n_ids * (uint64_t)g.W, 0u, s);
   GatherArgs a;
   a.store = store;
   a.store_bytes = store_bytes;
@@ -502,16 +551,13 @@ hipError_t launch_gather(const Geometry& g, const uint8_t* store, uint64_t store
   a.groups = g.groups;
   // payload rounded to 16 B, plus one word read past the end by the window
   a.pbuf_bytes = ((g.tensor_bytes + 15u) & ~15u) + 16u;
-  a.lpr = 0;
   if (g.W <= 4 * (uint32_t)kWave) {
     // small tensors: tile kernel, lane l owns words l + 64j
-    const uint32_t J = (g.W + kWave - 1) / kWave;
-    const bool t8 = g.tensor_bytes <= 512;
-    switch (J * 2 + (t8 ? 1 : 0)) {
-      case 3: return launch_tile<1, 8>(g, a, s);
-      case 5: return launch_tile<2, 8>(g, a, s);
-      case 6: return launch_tile<3, 4>(g, a, s);
-      case 8: return launch_tile<4, 4>(g, a, s);
+    switch ((g.W + kWave - 1) / kWave) {
+      case 1: return launch_small<1, 4>(g, a, s);  // <= 256 B: <= 16 units
+      case 2: return launch_small<2, 2>(g, a, s);  // <= 512 B: <= 32 units
+      case 3: return launch_small<3, 1>(g, a, s);  // <= 1 KB: <= 64 units
+      case 4: return launch_small<4, 1>(g, a, s);
       default: return hipErrorInvalidValue;
     }
   }
