@@ -153,16 +153,17 @@ __global__ __launch_bounds__(1024) void k_gather_decompress(GatherArgs a) {
   // scan one ahead.
   // (every wave loads the few metadata bytes, so no load sits behind a
   // branch; only the first wave uses them)
+  // the first two tensors' metadata round trips overlap the plan
   const int64_t id_a = load_id(a, row0);
   const int64_t id_b = load_id(a, row0 + step);
+  const RowMeta m0 = load_meta(a, id_a, gl);
+  RowMeta meta_next = load_meta(a, id_b, gl);      // tensor row+step
+  int64_t id_next2 = load_id(a, row0 + 2 * step);  // tensor row+2*step
 
   WordRegs<J> R;
   load_plan<J>(a.mask, a.bitval, a.sh, s_pref, s_kc, s_wsum, gl, R);
 
   if (row0 >= a.n_ids) return;  // uniform per group; no workgroup barrier follows for it
-  const RowMeta m0 = load_meta(a, id_a, gl);
-  RowMeta meta_next = load_meta(a, id_b, gl);      // tensor row+step
-  int64_t id_next2 = load_id(a, row0 + 2 * step);  // tensor row+2*step
   if (first_wave) scan_row(a, m0, gl, s_kc, &hdrs[0], obufs);
   group_sync(single);
 
