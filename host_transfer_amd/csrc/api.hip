@@ -244,10 +244,84 @@ int ibp_gather_decompress(const void* store, uint64_t store_bytes, uint64_t slot
     return fail(IBP_ERR_ALIGN, "ibp_gather_decompress: misaligned pointer");
   if ((r = require_device("ibp_gather_decompress"))) return r;
   const ibp::Geometry g = ibp::make_geometry(tensor_bytes, chunk_bytes);
-  hipError_t e = ibp::launch_gather(g, (const uint8_t*)store, store_bytes, slot_bytes, offsets,
-                                    part_bits, n_tensors, ids, n_ids, mask, bitval,
-                                    (uint32_t*)out, (hipStream_t)stream);
+  // slot mode: store holds the slots; cache mode: store is the compacted cache
+  hipError_t e = offsets
+      ? ibp::launch_gather(g, nullptr, 0, 0, offsets, (const uint8_t*)store, store_bytes,
+                           part_bits, n_tensors, ids, n_ids, mask, bitval, (uint32_t*)out,
+                           (hipStream_t)stream)
+      : ibp::launch_gather(g, (const uint8_t*)store, store_bytes, slot_bytes, nullptr, nullptr, 0,
+                           part_bits, n_tensors, ids, n_ids, mask, bitval, (uint32_t*)out,
+                           (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "ibp_gather_decompress");
+  return ok();
+}
+
+int ibp_cache_offsets(const uint32_t* lengths, const uint32_t* select, uint64_t n_tensors,
+                      uint64_t* cache_offsets, void* stream) {
+  if (!lengths || !select || !cache_offsets)
+    return fail(IBP_ERR_NULL, "ibp_cache_offsets: lengths, select and cache_offsets are required");
+  if (!aligned(lengths, 4) || !aligned(select, 4) || !aligned(cache_offsets, 8))
+    return fail(IBP_ERR_ALIGN, "ibp_cache_offsets: misaligned pointer");
+  int r;
+  if ((r = require_device("ibp_cache_offsets"))) return r;
+  hipError_t e = ibp::launch_cache_offsets(lengths, select, n_tensors, cache_offsets,
+                                           (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "ibp_cache_offsets");
+  return ok();
+}
+
+int ibp_cache_fill(const void* store, uint64_t slot_bytes, const uint32_t* lengths,
+                   uint64_t n_tensors, const uint64_t* cache_offsets, void* cache,
+                   uint64_t cache_bytes, void* stream) {
+  if (!store || !lengths || !cache_offsets || !cache)
+    return fail(IBP_ERR_NULL, "ibp_cache_fill: store, lengths, cache_offsets and cache are required");
+  if (slot_bytes == 0 || slot_bytes % 16 != 0 || n_tensors > UINT64_MAX / slot_bytes)
+    return fail(IBP_ERR_SIZE, "ibp_cache_fill: slot_bytes must be a positive multiple of 16");
+  if (!aligned(store, 16) || !aligned(cache, 16) || !aligned(lengths, 4) ||
+      !aligned(cache_offsets, 8))
+    return fail(IBP_ERR_ALIGN, "ibp_cache_fill: misaligned pointer");
+  int r;
+  if ((r = require_device("ibp_cache_fill"))) return r;
+  hipError_t e = ibp::launch_cache_fill((const uint8_t*)store, slot_bytes, lengths, n_tensors,
+                                        cache_offsets, (uint8_t*)cache, cache_bytes,
+                                        (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "ibp_cache_fill");
+  return ok();
+}
+
+int ibp_gather_decompress_hybrid(const void* store, uint64_t store_bytes, uint64_t slot_bytes,
+                                 const void* cache, uint64_t cache_bytes,
+                                 const uint64_t* cache_offsets, const uint32_t* part_bits,
+                                 uint64_t n_tensors, const int64_t* ids, uint64_t n_ids,
+                                 uint32_t tensor_bytes, uint32_t chunk_bytes,
+                                 const uint32_t* mask, const uint32_t* bitval, void* out,
+                                 void* stream) {
+  if (!store || !cache || !cache_offsets || !part_bits || !ids || !mask || !bitval || !out)
+    return fail(IBP_ERR_NULL, "ibp_gather_decompress_hybrid: a required pointer is null");
+  int r = check_tensor(tensor_bytes);
+  if (r) return r;
+  if ((r = check_chunk(chunk_bytes))) return r;
+  const uint32_t n_c = (tensor_bytes + chunk_bytes - 1) / chunk_bytes;
+  if (n_tensors && !bitmap_bits(n_tensors, n_c))
+    return fail(IBP_ERR_SIZE, "ibp_gather_decompress_hybrid: n_tensors too large");
+  if (slot_bytes < tensor_bytes || slot_bytes % 16 != 0)
+    return fail(IBP_ERR_SIZE,
+                "ibp_gather_decompress_hybrid: slot_bytes must be >= tensor_bytes and %% 16");
+  if (n_tensors > UINT64_MAX / slot_bytes || store_bytes < n_tensors * slot_bytes)
+    return fail(IBP_ERR_SIZE, "ibp_gather_decompress_hybrid: store_bytes < n_tensors * slot_bytes");
+  if (n_ids > UINT64_MAX / tensor_bytes)
+    return fail(IBP_ERR_SIZE, "ibp_gather_decompress_hybrid: n_ids too large");
+  if (!aligned(store, 16) || !aligned(cache, 16) || !aligned(out, 16) || !aligned(ids, 8) ||
+      !aligned(mask, 4) || !aligned(bitval, 4) || !aligned(part_bits, 4) ||
+      !aligned(cache_offsets, 8))
+    return fail(IBP_ERR_ALIGN, "ibp_gather_decompress_hybrid: misaligned pointer");
+  if ((r = require_device("ibp_gather_decompress_hybrid"))) return r;
+  const ibp::Geometry g = ibp::make_geometry(tensor_bytes, chunk_bytes);
+  hipError_t e = ibp::launch_gather(g, (const uint8_t*)store, store_bytes, slot_bytes,
+                                    cache_offsets, (const uint8_t*)cache, cache_bytes, part_bits,
+                                    n_tensors, ids, n_ids, mask, bitval, (uint32_t*)out,
+                                    (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "ibp_gather_decompress_hybrid");
   return ok();
 }
 

@@ -206,21 +206,29 @@ hipError_t launch_compress(const Geometry& g, const uint8_t* rows, uint64_t row_
 
 // ---------------------------------------------------------------- compaction
 
-// offsets[t] = sum of roundup(lengths[u], 16) over u < t; offsets[n] = total.
-// One workgroup walks the array in tiles of 4 x 1024 entries (off the
-// critical path: a few milliseconds for millions of tensors).
+// offsets[t] = sum of roundup(lengths[u], 16) over the selected u < t;
+// offsets[n] = total.  select: null (every tensor) or a flag per tensor; with
+// `mark`, an unselected tensor's entry is kNotCachedEntry.  One workgroup
+// walks the array in tiles of 4 x 1024 entries (off the critical path: a few
+// milliseconds for millions of tensors).
+constexpr uint64_t kNotCachedEntry = ~0ull;
+
 __global__ __launch_bounds__(1024) void k_compact_offsets(const uint32_t* __restrict__ lengths,
-                                                           uint64_t n, uint64_t* __restrict__ offsets) {
+                                                           const uint32_t* __restrict__ select,
+                                                           uint64_t n, uint64_t* __restrict__ offsets,
+                                                           bool mark) {
   __shared__ uint32_t s_wsum[16];
   const uint32_t tid = threadIdx.x;
   uint64_t carry = 0;
   for (uint64_t base = 0; base < n; base += 4096) {
     uint32_t v[4];
+    bool sel[4];
     uint32_t local = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint64_t t = base + 4u * tid + i;
-      v[i] = t < n ? ((lengths[t] + 15u) & ~15u) : 0u;
+      sel[i] = t < n && (select == nullptr || select[t] != 0u);
+      v[i] = sel[i] ? ((lengths[t] + 15u) & ~15u) : 0u;
       local += v[i];
     }
     uint32_t tot;
@@ -229,12 +237,36 @@ __global__ __launch_bounds__(1024) void k_compact_offsets(const uint32_t* __rest
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint64_t t = base + 4u * tid + i;
-      if (t < n) offsets[t] = o;
+      if (t < n) offsets[t] = (mark && !sel[i]) ? kNotCachedEntry : o;
       o += v[i];
     }
     carry += tot;
   }
   if (tid == 0) offsets[n] = carry;
+}
+
+// One wave per cached tensor: copies its payload (rounded up to 16 B) from
+// its slot to cache + offsets[t].  Entries that would end past cache_bytes or
+// read past the slot are skipped.
+__global__ __launch_bounds__(256) void k_cache_fill(const uint8_t* __restrict__ store,
+                                                     uint64_t slot_bytes,
+                                                     const uint32_t* __restrict__ lengths,
+                                                     uint64_t n, const uint64_t* __restrict__ offsets,
+                                                     uint8_t* __restrict__ cache,
+                                                     uint64_t cache_bytes) {
+  const uint32_t lane = lane_id();
+  const uint64_t wave = (uint64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  const uint64_t waves = (uint64_t)gridDim.x * (blockDim.x / kWave);
+  for (uint64_t t = wave; t < n; t += waves) {
+    const uint64_t o = offsets[t];
+    const uint64_t size = ((uint64_t)lengths[t] + 15u) & ~15ull;
+    if (o == kNotCachedEntry || (o & 15u) != 0 || size > slot_bytes || o > cache_bytes ||
+        size > cache_bytes - o)
+      continue;
+    const uint4* src = (const uint4*)(store + t * slot_bytes);
+    uint4* dst = (uint4*)(cache + o);
+    for (uint32_t q = lane; q < (uint32_t)(size >> 4); q += kWave) dst[q] = src[q];
+  }
 }
 
 // One wave per entry: copies offsets[t+1] - offsets[t] bytes from slot t.
@@ -258,7 +290,29 @@ __global__ __launch_bounds__(256) void k_compact_copy(const uint8_t* __restrict_
 
 hipError_t launch_compact_offsets(const uint32_t* lengths, uint64_t n, uint64_t* offsets,
                                   hipStream_t s) {
-  hipLaunchKernelGGL(k_compact_offsets, dim3(1), dim3(1024), 0, s, lengths, n, offsets);
+  hipLaunchKernelGGL(k_compact_offsets, dim3(1), dim3(1024), 0, s, lengths,
+                     (const uint32_t*)nullptr, n, offsets, false);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_offsets(const uint32_t* lengths, const uint32_t* select, uint64_t n,
+                                uint64_t* offsets, hipStream_t s) {
+  hipLaunchKernelGGL(k_compact_offsets, dim3(1), dim3(1024), 0, s, lengths, select, n, offsets,
+                     true);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_fill(const uint8_t* store, uint64_t slot_bytes, const uint32_t* lengths,
+                             uint64_t n, const uint64_t* offsets, uint8_t* cache,
+                             uint64_t cache_bytes, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  DeviceInfo di;
+  hipError_t e = device_info(&di);
+  if (e != hipSuccess) return e;
+  const uint64_t want = (n + 3) / 4;
+  const uint64_t cap = (uint64_t)di.cus * 8;
+  hipLaunchKernelGGL(k_cache_fill, dim3((uint32_t)(want < cap ? want : cap)), dim3(256), 0, s,
+                     store, slot_bytes, lengths, n, offsets, cache, cache_bytes);
   return hipGetLastError();
 }
 

@@ -29,11 +29,17 @@
 
 namespace ibp {
 
+// Where payloads are read from.  A tensor whose offset-table entry is not
+// kNotCached is read from the compacted cache at that offset; any other
+// tensor from its slot of the in-place store.  Slot mode: no offset table;
+// cache mode: no store; hybrid: both.
 struct GatherArgs {
-  const uint8_t* store;
+  const uint8_t* store;     // in-place store (slot t at t*slot_bytes), or null
   uint64_t store_bytes;
   uint64_t slot_bytes;
-  const uint64_t* offsets;
+  const uint64_t* offsets;  // cache entry per tensor, or null
+  const uint8_t* cache;     // compacted cache, or null
+  uint64_t cache_bytes;
   const uint32_t* part_bits;
   uint64_t n_tensors;
   const int64_t* ids;
@@ -69,10 +75,34 @@ struct GatherLds {
 // flight, stores and prefetches included).
 __device__ __align__(16) uint4 g_zero16 = {0u, 0u, 0u, 0u};
 
+constexpr uint64_t kNotCached = ~0ull;
+
+// Address of tensor t's payload and the bytes readable from there (0 when it
+// has no source).  One unconditional load of the offset table entry.
+struct Source {
+  uint64_t addr;
+  uint64_t avail;
+  bool ok;
+};
+
+__device__ __forceinline__ Source row_source(const GatherArgs& a, uint64_t t) {
+  const uint64_t o = *(a.offsets ? a.offsets + t : (const uint64_t*)&g_zero16);
+  const bool hit = a.offsets != nullptr && o != kNotCached;
+  const uint64_t so = t * a.slot_bytes;
+  const uint64_t at = hit ? o : so;
+  const uint64_t lim = hit ? a.cache_bytes : a.store_bytes;
+  Source r;
+  r.addr = hit ? (uint64_t)a.cache + o : (uint64_t)a.store + so;
+  r.avail = at < lim ? (lim - at) & ~15ull : 0ull;
+  r.ok = hit || a.store != nullptr;
+  return r;
+}
+
 // What the first wave knows about one tensor before its payload is read.
 struct RowMeta {
-  uint64_t base;  // payload offset in the store
-  uint32_t bits;  // participation word holding this lane's chunk bit (shifted)
+  uint64_t addr;   // payload address
+  uint64_t avail;  // whole 16 B units readable there, in bytes
+  uint32_t bits;   // participation word holding this lane's chunk bit (shifted)
   bool valid;
 };
 
@@ -92,8 +122,10 @@ __device__ __forceinline__ RowMeta load_meta(const GatherArgs& a, int64_t id, ui
   const uint32_t c = min(lane % kWave, a.sh.n_c - 1u);
   const uint64_t bit = t * a.sh.n_c + c;
   m.bits = a.part_bits[bit >> 5] >> (bit & 31);
-  m.base = *(a.offsets ? a.offsets + t : (const uint64_t*)&g_zero16) +
-           (a.offsets ? 0ull : t * a.slot_bytes);
+  const Source src = row_source(a, t);
+  m.addr = src.addr;
+  m.avail = src.avail;
+  m.valid = m.valid && src.ok;
   return m;
 }
 
@@ -110,17 +142,17 @@ __device__ __forceinline__ void scan_row(const GatherArgs& a, const RowMeta& m, 
     hdr->pmask = pm;
     hdr->valid = m.valid;
     hdr->len = (total + 7u) >> 3;
-    hdr->base = m.base;
+    hdr->addr = m.addr;
+    hdr->avail = m.avail;
   }
 }
 
 // Number of 16 B payload units to read: the payload rounded up to 16 B,
-// never past store_bytes.
+// never past the end of its store or cache.
 __device__ __forceinline__ uint32_t payload_units(const GatherArgs& a, const GroupHdr& h) {
   if (!h.valid) return 0;
-  const uint64_t avail = h.base < a.store_bytes ? (a.store_bytes - h.base) & ~15ull : 0ull;
   const uint32_t want = (h.len + 15u) & ~15u;
-  return (uint32_t)(min((uint64_t)want, avail) >> 4);
+  return (uint32_t)(min((uint64_t)want, h.avail) >> 4);
 }
 
 template <int J>
@@ -173,7 +205,7 @@ __global__ __launch_bounds__(1024) void k_gather_decompress(GatherArgs a) {
   {
     const GroupHdr h = hdrs[0];
     const uint32_t n16 = payload_units(a, h);
-    const uint4* src = (const uint4*)(a.store + h.base);
+    const uint4* src = (const uint4*)h.addr;
     v0 = *(gl < n16 ? src + gl : &g_zero16);
     v1 = *(gl + G < n16 ? src + gl + G : &g_zero16);
   }
@@ -198,7 +230,7 @@ __global__ __launch_bounds__(1024) void k_gather_decompress(GatherArgs a) {
     {
       const GroupHdr hn = hdrs[cur ^ 1u];
       const uint32_t n16 = has_next ? payload_units(a, hn) : 0u;
-      const uint4* src = (const uint4*)(a.store + hn.base);
+      const uint4* src = (const uint4*)hn.addr;
       v0 = *(gl < n16 ? src + gl : &g_zero16);
       v1 = *(gl + G < n16 ? src + gl + G : &g_zero16);
     }
@@ -256,8 +288,8 @@ __global__ __launch_bounds__(1024) void k_gather_decompress(GatherArgs a) {
 // Waves are independent: only wave-level synchronisation inside the loop.
 
 struct TileHdr {
-  uint64_t base;
-  uint32_t len;
+  uint64_t addr;    // payload address
+  uint32_t n16;     // 16 B units to read
   uint32_t pmask;
   uint32_t valid;
   uint32_t off[3];  // bit offsets of chunks 1..3 (chunk 0 starts at 0)
@@ -267,7 +299,8 @@ struct TileHdr {
 // Every lane loads (lanes >= T duplicate lane % T) and ids are clamped into
 // range, so the loads are unconditional.
 struct TileMeta {
-  uint64_t base;
+  uint64_t addr;
+  uint64_t avail;
   uint32_t w0, w1;  // bitmap words holding the tensor's chunk bits
   uint32_t sh;      // bit position of chunk 0 in w0
   bool valid;
@@ -287,9 +320,10 @@ __device__ __forceinline__ TileMeta load_tile_meta(const GatherArgs& a, int64_t 
   m.sh = bit & 31;
   m.w0 = a.part_bits[q];
   m.w1 = a.part_bits[q < last_word ? q + 1 : q];
-  // one load on both layouts (offset table, or zero plus the slot offset)
-  m.base = *(a.offsets ? a.offsets + t : (const uint64_t*)&g_zero16) +
-           (a.offsets ? 0ull : t * a.slot_bytes);
+  const Source src = row_source(a, t);
+  m.addr = src.addr;
+  m.avail = src.avail;
+  m.valid = m.valid && src.ok;
   return m;
 }
 
@@ -297,7 +331,7 @@ __device__ __forceinline__ TileHdr make_tile_hdr(const GatherArgs& a, const Tile
                                                  const uint32_t* s_kc) {
   TileHdr h;
   h.valid = m.valid;
-  h.base = m.base;
+  h.addr = m.addr;
   const uint32_t n_c = a.sh.n_c;
   const uint64_t word = (uint64_t)m.w0 | ((uint64_t)m.w1 << 32);
   const uint32_t pm = m.valid ? (uint32_t)(word >> m.sh) & ((1u << n_c) - 1u) : 0u;
@@ -311,15 +345,11 @@ __device__ __forceinline__ TileHdr make_tile_hdr(const GatherArgs& a, const Tile
   h.off[1] = offs[2];
   h.off[2] = offs[3];
   h.pmask = pm;
-  h.len = m.valid ? (o + 7u) >> 3 : 0u;
+  // 16 B units: the payload rounded up to 16 B, never past the end of its
+  // store or cache
+  const uint32_t len = m.valid ? (o + 7u) >> 3 : 0u;
+  h.n16 = (uint32_t)(min((uint64_t)((len + 15u) & ~15u), m.avail) >> 4);
   return h;
-}
-
-// Number of 16 B units to read for a header: the payload rounded up to 16 B,
-// never past store_bytes.
-__device__ __forceinline__ uint32_t tile_units(const GatherArgs& a, const TileHdr& h) {
-  const uint64_t avail = h.base < a.store_bytes ? (a.store_bytes - h.base) & ~15ull : 0ull;
-  return (uint32_t)(min((uint64_t)((h.len + 15u) & ~15u), avail) >> 4);
 }
 
 // Decodes word j of one tensor of a tile (chunk, participation and offset
@@ -391,8 +421,8 @@ __global__ __launch_bounds__(256) void k_gather_tile(GatherArgs a) {
 #define IBP_TILE_LOAD(k, hdr)                                                                  \
   if constexpr (k < NL) {                                                                      \
     const TileHdr& h_ = (hdr)[k * RPI + lrow];                                                 \
-    n##k = tile_units(a, h_);                                                                  \
-    v##k = *(lunit < n##k ? (const uint4*)(a.store + h_.base) + lunit : &g_zero16);            \
+    n##k = h_.n16;                                                                             \
+    v##k = *(lunit < n##k ? (const uint4*)h_.addr + lunit : &g_zero16);                        \
   }
 #define IBP_TILE_ISSUE_LOADS(hdr)                                                              \
   IBP_TILE_LOAD(0, hdr) IBP_TILE_LOAD(1, hdr) IBP_TILE_LOAD(2, hdr) IBP_TILE_LOAD(3, hdr)      \
@@ -415,7 +445,7 @@ __global__ __launch_bounds__(256) void k_gather_tile(GatherArgs a) {
     //    last tile they are invalid, so its loads below read only g_zero16
     if (lane < (uint32_t)T) {
       TileHdr h = make_tile_hdr(a, meta_next, s_kc);
-      if (!has_next) h.valid = 0, h.len = 0, h.base = 0;
+      if (!has_next) h.valid = 0, h.n16 = 0;
       hnext[lane] = h;
     }
     wave_sync();
@@ -529,18 +559,20 @@ static hipError_t launch_j(const Geometry& g, const GatherArgs& a, hipStream_t s
 }
 
 hipError_t launch_gather(const Geometry& g, const uint8_t* store, uint64_t store_bytes,
-                         uint64_t slot_bytes, const uint64_t* offsets, const uint32_t* part_bits,
-                         uint64_t n_tensors, const int64_t* ids, uint64_t n_ids,
-                         const uint32_t* mask, const uint32_t* bitval, uint32_t* out,
-                         hipStream_t s) {
+                         uint64_t slot_bytes, const uint64_t* offsets, const uint8_t* cache,
+                         uint64_t cache_bytes, const uint32_t* part_bits, uint64_t n_tensors,
+                         const int64_t* ids, uint64_t n_ids, const uint32_t* mask,
+                         const uint32_t* bitval, uint32_t* out, hipStream_t s) {
   if (n_ids == 0) return hipSuccess;
   // no tensors: every id is out of range and every row is zero
   if (n_tensors == 0) return launch_fill_u32(out, n_ids * (uint64_t)g.W, 0u, s);
   GatherArgs a;
   a.store = store;
-  a.store_bytes = store_bytes;
+  a.store_bytes = store ? store_bytes : 0;
   a.slot_bytes = slot_bytes;
   a.offsets = offsets;
+  a.cache = cache;
+  a.cache_bytes = cache ? cache_bytes : 0;
   a.part_bits = part_bits;
   a.n_tensors = n_tensors;
   a.ids = ids;

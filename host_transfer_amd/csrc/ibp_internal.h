@@ -45,11 +45,20 @@ hipError_t launch_compact(const uint8_t* store, uint64_t slot_bytes, uint64_t n,
                           const uint64_t* offsets, uint8_t* cache, uint64_t cache_bytes,
                           hipStream_t s);
 
+// store: in-place slots (or null); offsets + cache: compacted cache entries
+// (kNotCached marks a tensor that is read from its slot instead).
 hipError_t launch_gather(const Geometry& g, const uint8_t* store, uint64_t store_bytes,
-                         uint64_t slot_bytes, const uint64_t* offsets, const uint32_t* part_bits,
-                         uint64_t n_tensors, const int64_t* ids, uint64_t n_ids,
-                         const uint32_t* mask, const uint32_t* bitval, uint32_t* out,
-                         hipStream_t s);
+                         uint64_t slot_bytes, const uint64_t* offsets, const uint8_t* cache,
+                         uint64_t cache_bytes, const uint32_t* part_bits, uint64_t n_tensors,
+                         const int64_t* ids, uint64_t n_ids, const uint32_t* mask,
+                         const uint32_t* bitval, uint32_t* out, hipStream_t s);
+
+hipError_t launch_cache_offsets(const uint32_t* lengths, const uint32_t* select, uint64_t n,
+                                uint64_t* offsets, hipStream_t s);
+
+hipError_t launch_cache_fill(const uint8_t* store, uint64_t slot_bytes, const uint32_t* lengths,
+                             uint64_t n, const uint64_t* offsets, uint8_t* cache,
+                             uint64_t cache_bytes, hipStream_t s);
 
 hipError_t launch_raw_gather(const uint8_t* src, uint64_t row_stride, uint64_t n_rows,
                              const int64_t* ids, uint64_t n_ids, uint32_t row_bytes, uint8_t* out,

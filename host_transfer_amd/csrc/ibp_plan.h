@@ -121,10 +121,10 @@ __device__ __forceinline__ void group_sync(bool single_wave) {
 // Per-group state shared between the chunk-owning wave and the others.
 struct GroupHdr {
   uint64_t pmask;  // participation bits of the current tensor's chunks
-  uint64_t base;   // byte offset of its payload in the store
+  uint64_t addr;   // payload address
   uint32_t len;    // payload bytes
-  uint32_t valid;  // id in range
-  uint32_t pad[2];
+  uint32_t valid;  // id in range and a source for it
+  uint64_t avail;  // whole 16 B units readable at addr, in bytes
 };
 
 }  // namespace ibp

@@ -31,6 +31,7 @@ ERR_NULL, ERR_SIZE, ERR_CHUNK, ERR_THRESHOLD, ERR_ALIGN, ERR_HIP, ERR_FLAGS = -1
 MAX_TENSOR_BYTES = 16384
 MAX_CHUNKS = 64
 HOST_DEFAULT, HOST_COHERENT, HOST_NONCOHERENT = 0, 1, 2
+NOT_CACHED = (1 << 64) - 1
 
 _vp = ctypes.c_void_p
 _u32 = ctypes.c_uint32
@@ -47,6 +48,10 @@ _SIGS = {
     "ibp_compact": [_vp, _u64, _u64, _vp, _vp, _u64, _vp],
     "ibp_gather_decompress": [_vp, _u64, _u64, _vp, _vp, _u64, _vp, _u64, _u32, _u32, _vp, _vp,
                               _vp, _vp],
+    "ibp_cache_offsets": [_vp, _vp, _u64, _vp, _vp],
+    "ibp_cache_fill": [_vp, _u64, _vp, _u64, _vp, _vp, _u64, _vp],
+    "ibp_gather_decompress_hybrid": [_vp, _u64, _u64, _vp, _u64, _vp, _vp, _u64, _vp, _u64, _u32,
+                                     _u32, _vp, _vp, _vp, _vp],
     "ibp_host_alloc": [_u64, ctypes.c_uint, ctypes.POINTER(_vp)],
     "ibp_host_free": [_vp],
     "ibp_raw_gather": [_vp, _u64, _u64, _vp, _u64, _u32, _vp, _vp],
@@ -133,6 +138,26 @@ def gather_decompress(store, store_bytes, slot_bytes, offsets, part_bits, n_tens
                                       _ptr(part_bits), n_tensors, _ptr(ids), n_ids, tensor_bytes,
                                       chunk_bytes, _ptr(mask), _ptr(bitval), _ptr(out),
                                       _stream(stream)))
+
+
+def cache_offsets(lengths, select, n_tensors, offsets, stream=None):
+    _check(_lib.ibp_cache_offsets(_ptr(lengths), _ptr(select), n_tensors, _ptr(offsets),
+                                  _stream(stream)))
+
+
+def cache_fill(store, slot_bytes, lengths, n_tensors, offsets, cache, cache_bytes, stream=None):
+    _check(_lib.ibp_cache_fill(_ptr(store), slot_bytes, _ptr(lengths), n_tensors, _ptr(offsets),
+                               _ptr(cache), cache_bytes, _stream(stream)))
+
+
+def gather_decompress_hybrid(store, store_bytes, slot_bytes, cache, cache_bytes, offsets,
+                             part_bits, n_tensors, ids, n_ids, tensor_bytes, chunk_bytes, mask,
+                             bitval, out, stream=None):
+    _check(_lib.ibp_gather_decompress_hybrid(_ptr(store), store_bytes, slot_bytes, _ptr(cache),
+                                             cache_bytes, _ptr(offsets), _ptr(part_bits),
+                                             n_tensors, _ptr(ids), n_ids, tensor_bytes,
+                                             chunk_bytes, _ptr(mask), _ptr(bitval), _ptr(out),
+                                             _stream(stream)))
 
 
 def raw_gather(src, row_stride, n_rows, ids, n_ids, row_bytes, out, stream=None):

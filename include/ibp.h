@@ -177,7 +177,8 @@ int ibp_compact(const void *store, uint64_t slot_bytes, uint64_t n_tensors,
  *   store        payloads: slots (offsets == NULL; store holds
  *                n_tensors*slot_bytes bytes, host-mapped or device) or a
  *                compacted cache (offsets != NULL; device uint64 offsets as
- *                from ibp_compact_offsets).
+ *                from ibp_compact_offsets; an IBP_NOT_CACHED entry yields a
+ *                row of zero bytes).
  *   store_bytes  readable bytes at store.  Reads never go past it (a corrupt
  *                bitmap or offset yields wrong rows, never an access fault).
  *   part_bits    device bitmap of the n_tensors tensors.
@@ -195,6 +196,51 @@ int ibp_gather_decompress(const void *store, uint64_t store_bytes,
                           uint32_t tensor_bytes, uint32_t chunk_bytes,
                           const uint32_t *mask, const uint32_t *bitval,
                           void *out, void *stream);
+
+/* ------------------------------------------------------ cache + store together
+ * [G-EN] System Integration uses both placements at once: a compressed
+ * software cache in GPU memory for hot tensors, and compressed in-place
+ * buffers in CPU memory for the rest ([JH] Figure 8 paragraph: cache plus
+ * PCIe traffic compression gives the largest GNN speedups).  A partial cache
+ * is described by an offset table with one entry per tensor; IBP_NOT_CACHED
+ * marks a tensor that is only in the in-place store. */
+#define IBP_NOT_CACHED UINT64_MAX
+
+/*
+ * ibp_cache_offsets -- cache_offsets[t] = running sum of roundup(lengths[u],
+ * 16) over the selected u < t if select[t] != 0, else IBP_NOT_CACHED;
+ * cache_offsets[n_tensors] = the cache size in bytes.
+ *   lengths  device uint32[n_tensors];  select  device uint32[n_tensors];
+ *   cache_offsets  device uint64[n_tensors + 1].
+ */
+int ibp_cache_offsets(const uint32_t *lengths, const uint32_t *select, uint64_t n_tensors,
+                      uint64_t *cache_offsets, void *stream);
+
+/*
+ * ibp_cache_fill -- copies the payload of every cached tensor (roundup(len,
+ * 16) bytes from the start of its slot) to cache + cache_offsets[t].  Entries
+ * that would end past cache_bytes are not copied.
+ *   store  in-place slots (device or host-mapped);  cache  device, 16 B aligned.
+ */
+int ibp_cache_fill(const void *store, uint64_t slot_bytes, const uint32_t *lengths,
+                   uint64_t n_tensors, const uint64_t *cache_offsets, void *cache,
+                   uint64_t cache_bytes, void *stream);
+
+/*
+ * ibp_gather_decompress_hybrid -- as ibp_gather_decompress, in one launch,
+ * with each tensor read from the cache when cache_offsets[t] !=
+ * IBP_NOT_CACHED (HBM) and from its slot of `store` otherwise (typically
+ * host-mapped).  Every read stays inside [store, store + store_bytes) or
+ * [cache, cache + cache_bytes).
+ * Errors: as ibp_gather_decompress; store, cache and cache_offsets required.
+ */
+int ibp_gather_decompress_hybrid(const void *store, uint64_t store_bytes, uint64_t slot_bytes,
+                                 const void *cache, uint64_t cache_bytes,
+                                 const uint64_t *cache_offsets, const uint32_t *part_bits,
+                                 uint64_t n_tensors, const int64_t *ids, uint64_t n_ids,
+                                 uint32_t tensor_bytes, uint32_t chunk_bytes,
+                                 const uint32_t *mask, const uint32_t *bitval, void *out,
+                                 void *stream);
 
 /* ------------------------------------------------------------ host memory
  * Pinned host memory that the GPU reads and writes directly (zero-copy),

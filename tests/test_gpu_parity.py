@@ -208,3 +208,56 @@ def test_raw_gather_and_stream_read():
     ibp.stream_read(hb, n * stride, 0x9E3779B9, sink)
     torch.cuda.synchronize()
     hb.free()
+
+
+# ------------------------------------------------------------ cache + store (hybrid)
+
+@pytest.mark.parametrize("key,n", [("dense_gnn", 5000), ("sparse_gnn", 1500)])
+@pytest.mark.parametrize("frac", [0.0, 0.3, 1.0])
+def test_hybrid_cache_and_store(key, n, frac):
+    """Cached tensors come from the HBM cache, the others from the pinned
+    slots; the rows must be the same as from the slots alone."""
+    from host_transfer_amd import ibp
+    from oracle import oracle as O
+    w = W.WORKLOADS[key].scaled(n)
+    rows = W.rows(w)
+    B, C, S = w.tensor_bytes, w.chunk_bytes, w.slot_bytes
+    G.log(f"[parity] hybrid {key}: n={n} cached fraction {frac}")
+    mask, bitval = G.check_metadata(rows, 0.95)
+    store, part, lengths = G.gpu_compress(rows, mask, bitval, C, S, pinned=True)
+    rng = np.random.default_rng(int(frac * 10) + n)
+    select = (rng.random(n) < frac).astype(np.uint32)
+    offsets = torch.zeros(n + 1, dtype=torch.int64, device="cuda")
+    ibp.cache_offsets(lengths, G.dev(select), n, offsets)
+    g_off = G.host(offsets).view(np.uint64)
+    ln = G.host(lengths).view(np.uint32).astype(np.uint64)
+    pad = np.where(select != 0, (ln + 15) // 16 * 16, 0).astype(np.uint64)
+    run = np.concatenate([[0], np.cumsum(pad)]).astype(np.uint64)
+    want_off = np.where(select != 0, run[:-1], np.uint64(ibp.NOT_CACHED))
+    assert (g_off[:n] == want_off).all() and g_off[n] == run[-1], "cache offsets"
+    total = int(run[-1])
+    cache = torch.full((max(total, 16),), 0x11, dtype=torch.uint8, device="cuda")
+    ibp.cache_fill(store, S, lengths, n, offsets, cache, total)
+    g_cache = G.host(cache)
+    slots = store.array.reshape(n, S)
+    for t in np.nonzero(select)[0][:200]:
+        o, L = int(g_off[t]), int(ln[t])
+        assert (g_cache[o:o + L] == slots[t, :L]).all(), "cached payload differs"
+    ids = rng.integers(0, n, 3000)
+    ids[:4] = [-1, n, 0, n - 1]
+    out = torch.full((len(ids) * B,), -1, dtype=torch.int8, device="cuda")
+    ibp.gather_decompress_hybrid(store, n * S, S, cache, total, offsets, part, n, G.dev(ids),
+                                 len(ids), B, C, G.dev(mask), G.dev(bitval), out)
+    got = G.host(out).view(np.uint8).reshape(len(ids), B)
+    assert (got == G.expected_rows(rows, ids)).all(), "hybrid gather is not the original rows"
+    o_store, o_part, _ = O.compress(rows, mask, bitval, C, slot_bytes=S)
+    ok_ids = ids[(ids >= 0) & (ids < n)]
+    want = O.gather_decompress(o_store, o_part, n, ok_ids, B, C, mask, bitval, slot_bytes=S)
+    assert (got[(ids >= 0) & (ids < n)] == want).all(), "hybrid gather differs from the oracle"
+    # the cache alone: tensors that are not cached give zero rows
+    got2 = G.gpu_gather(cache, total, 0, offsets, part, n, ids, B, C, mask, bitval)
+    cached = np.zeros(len(ids), bool)
+    inr = (ids >= 0) & (ids < n)
+    cached[inr] = select[ids[inr]] != 0
+    assert (got2[cached] == got[cached]).all() and not got2[~cached].any()
+    store.free()
