@@ -11,9 +11,11 @@ Prints ONE JSON line.  `value` is decompressed GB/s (ids x tensor bytes per
 second of wall time over the timed steps, inputs already resident).  Extra
 objects: `roofline` (the gather kernel against the host-link peak),
 `cpu_baseline` (the CPU oracle on a bounded sample of the same batches),
-`hbm_path` (the same kernel reading a compressed cache in HBM), probes of the
-link, and the transfer speedup over an uncompressed GPU gather of the same
-rows ([JH] Table 1 discussion: transfer speedup against plain transfers).
+`hbm_path` (the same kernel reading a compressed cache in HBM), `hybrid_path`
+(cache hits from HBM and misses over PCIe in one launch, at a fixed HBM budget,
+compressed against uncompressed tensors), probes of the link, and the transfer
+speedup over an uncompressed GPU gather of the same rows ([JH] Table 1
+discussion: transfer speedup against plain transfers).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sparse_gnn]
        [--hbm-workloads dense_gnn,dlrm_1k|none] [--hbm-large-batch N]
@@ -80,6 +82,11 @@ def parse():
     p.add_argument("--threshold", type=float, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--mode", default="default", choices=["default", "ablation", "sweep", "kv-step"],
+                   help="default: the headline and the cache paths; ablation: transfer methods "
+                        "for small random tensors; sweep: throughput against space saving and "
+                        "chunk size; kv-step: the online OPT-13B K/V path")
+    p.add_argument("--kv-pairs", type=int, default=80, help="(layer, K|V) pairs in --mode kv-step")
     return p.parse_args()
 
 
@@ -385,6 +392,57 @@ def measure_hbm(torch, ibp, W, key, flags, args, pr):
     return res
 
 
+def measure_hybrid(torch, ibp, table, batches, ids_host, args, budget_fraction):
+    """Cache + store in one launch at a fixed HBM budget: compressed tensors
+    against uncompressed ones (the same kernel with Mask = 0 over the raw
+    rows, whose payloads are the rows themselves)."""
+    import numpy as np
+    w = table.w
+    N, B, C, S = w.n_tensors, w.tensor_bytes, w.chunk_bytes, w.slot_bytes
+    budget = int(budget_fraction * N * B)
+    order = np.random.default_rng(7).permutation(N)
+    zero_words = torch.zeros(B // 4, dtype=torch.int32, device="cuda")
+    n_c = ibp.num_chunks(B, C)
+    zero_bits = torch.zeros((N * n_c + 31) // 32, dtype=torch.int32, device="cuda")
+    raw_len = torch.full((N,), B, dtype=torch.int32, device="cuda")
+    out = torch.empty(w.batch * B, dtype=torch.uint8, device="cuda")
+    res = {"hbm_budget_GB": round(budget / 1e9, 3), "ids": w.batch}
+    for name, store, lengths, len_host, mask, bitval, bits in (
+            ("compressed", table.store, table.lengths, table.len_host, table.mask, table.bitval,
+             table.part),
+            ("uncompressed", table.raw, raw_len, np.full(N, B, np.uint32), zero_words,
+             zero_words, zero_bits)):
+        pad = (len_host[order].astype(np.int64) + 15) // 16 * 16
+        k = int(np.searchsorted(np.cumsum(pad), budget, side="right"))
+        select = np.zeros(N, np.uint32)
+        select[order[:k]] = 1
+        offsets = torch.zeros(N + 1, dtype=torch.int64, device="cuda")
+        ibp.cache_offsets(lengths, torch.from_numpy(select).cuda(), N, offsets)
+        total = int(offsets[-1].item())
+        cache = torch.empty(max(total, 16), dtype=torch.uint8, device="cuda")
+        ibp.cache_fill(store, S, lengths, N, offsets, cache, total)
+
+        def run(i):
+            ibp.gather_decompress_hybrid(store, N * S, S, cache, total, offsets, bits, N,
+                                         batches[i], w.batch, B, C, mask, bitval, out)
+        ms = statistics.mean(timed_launches(torch, run, args.warmup, args.steps))
+        run(len(batches) - 1)
+        torch.cuda.synchronize()
+        got = out.view(w.batch, B)[:64].cpu().numpy()
+        want = table.raw.array.reshape(N, S)[ids_host[-1][:64], :B]
+        if not (got == want).all():
+            raise SystemExit(f"bench: hybrid gather ({name}) differs from the original rows")
+        hits = float(np.mean([select[i].mean() for i in ids_host[args.warmup:]]))
+        res[name] = {"cached_tensors": k, "hit_rate": round(hits, 4),
+                     "kernel_us": round(ms * 1e3, 2),
+                     "decompressed_GBps": round(w.batch * B / (ms * 1e-3) / 1e9, 1)}
+        del cache, offsets
+    res["speedup"] = round(res["uncompressed"]["kernel_us"] / res["compressed"]["kernel_us"], 3)
+    del zero_words, zero_bits, raw_len, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def timed_launches(torch, fn, warmup, steps):
     """HIP-event duration (ms) of each of `steps` launches after `warmup`."""
     for k in range(warmup):
@@ -396,6 +454,250 @@ def timed_launches(torch, fn, warmup, steps):
         fn(k)
         tm.stop(s)
     return tm.ms()
+
+
+# ---------------------------------------------------------------- other modes
+
+def hip_runtime():
+    """torch's HIP runtime (already loaded), for plain hipMemcpyAsync calls."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so.7")
+    hip.hipMemcpyAsync.restype = ctypes.c_int
+    hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                   ctypes.c_void_p]
+    return hip
+
+
+def run_ablation(torch, ibp, args, pr):
+    """Copy throughput of small random tensors from pinned host memory to the
+    GPU by transfer method ([JH] Figure 5 and aligned-copy paragraphs):
+    per-tensor DMA issued by the CPU, a CPU gather into a staging buffer
+    followed by one DMA, GPU zero-copy reads of packed rows (4 B loads, rows
+    at any 4 B offset) and GPU zero-copy reads of 128 B-aligned rows (16 B
+    loads)."""
+    import concurrent.futures as cf
+    import numpy as np
+    hip = hip_runtime()
+    H2D = 1
+    pool_bytes = 4 << 30
+    hb = ibp.HostBuffer(pool_bytes + 4096)
+    rng = np.random.default_rng(5)
+    view64 = hb.array[:(pool_bytes // 8) * 8].view(np.uint64)
+    for i in range(0, view64.size, 1 << 24):
+        view64[i:i + (1 << 24)] = rng.integers(0, 1 << 63, min(1 << 24, view64.size - i),
+                                               dtype=np.uint64)
+    n = 8192
+    stream = torch.cuda.current_stream().cuda_stream
+    threads = min(16, os.cpu_count() or 1)
+    rows = []
+    for size in (64, 256, 1024, 4096, 16384):
+        S = (size + 127) // 128 * 128
+        n_al = pool_bytes // S
+        n_pk = (pool_bytes - 4) // size
+        ids = rng.integers(0, min(n_al, n_pk), n)
+        d_ids = torch.from_numpy(ids).cuda()
+        out = torch.empty(n * size, dtype=torch.uint8, device="cuda")
+        r = {"tensor_bytes": size}
+        # GPU zero-copy, 128 B-aligned rows, 16 B loads
+        ms = timed_launches(torch, lambda k: ibp.raw_gather(hb, S, n_al, d_ids, n, size, out),
+                            3, 20)
+        r["gpu_aligned_GBps"] = round(n * size / (statistics.median(ms) * 1e-3) / 1e9, 2)
+        # GPU zero-copy, packed rows at a 4 B offset, 4 B loads
+        ms = timed_launches(torch, lambda k: ibp.raw_gather(hb.ptr + 4, size, n_pk, d_ids, n,
+                                                            size, out), 3, 20)
+        r["gpu_unaligned_GBps"] = round(n * size / (statistics.median(ms) * 1e-3) / 1e9, 2)
+        # CPU gather into pinned staging (all host threads) + one DMA
+        staging = ibp.HostBuffer(n * size)
+        stage = staging.array.reshape(n, size)
+        src = hb.array[:n_al * S].reshape(n_al, S)
+
+        def cpu_gather(chunk):
+            lo, hi = chunk
+            stage[lo:hi] = src[ids[lo:hi], :size]
+        chunks = [(i, min(n, i + n // threads + 1)) for i in range(0, n, n // threads + 1)]
+        best = float("inf")
+        with cf.ThreadPoolExecutor(threads) as ex:
+            for _ in range(5):
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                list(ex.map(cpu_gather, chunks))
+                hip.hipMemcpyAsync(out.data_ptr(), staging.ptr, n * size, H2D, stream)
+                torch.cuda.synchronize()
+                best = min(best, time.perf_counter() - t0)
+        r["cpu_bulk_GBps"] = round(n * size / best / 1e9, 2)
+        staging.free()
+        # one DMA per tensor, issued by the CPU (a bounded number of rows)
+        m = 1024
+        best = float("inf")
+        for _ in range(3):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(m):
+                hip.hipMemcpyAsync(out.data_ptr() + i * size, hb.ptr + int(ids[i]) * S, size, H2D,
+                                   stream)
+            torch.cuda.synchronize()
+            best = min(best, time.perf_counter() - t0)
+        r["cpu_fine_GBps"] = round(m * size / best / 1e9, 3)
+        r["aligned_over_unaligned"] = round(r["gpu_aligned_GBps"] / r["gpu_unaligned_GBps"], 3)
+        rows.append(r)
+        log(f"ablation {r}")
+        del out, d_ids
+    hb.free()
+    print(json.dumps({"metric": "CPU-to-GPU copy throughput of 8,192 random tensors by transfer "
+                                "method", "unit": "GB/s", "higher_is_better": True,
+                      "limit": {"pcie5_x16_GBps": PCIE5_X16_GBPS, **pr}, "results": rows,
+                      "host_threads": threads, "device": torch.cuda.get_device_name(0)}),
+          flush=True)
+
+
+def run_sweep(torch, ibp, args, pr):
+    """Decompression throughput against space saving and chunk size ([G-EN]
+    Results and [JH] Figure 7 paragraph: above 95 % of the ideal rate below
+    50 % saving, for 256 B, 1 KB and 4 KB chunks), on synthetic 4 KB tensors
+    whose words keep k random low bits under 32-k fixed high bits, so the
+    saving is (32-k)/32; plus a stream of BF16 weight tensors."""
+    import numpy as np
+    rng = np.random.default_rng(11)
+    N, B, n = 65536, 4096, 8192
+    S = B
+    link = max(pr["h2d_dma_GBps"], pr["h2d_zero_copy_read_GBps"])
+    raw = ibp.HostBuffer(N * S)
+    store = ibp.HostBuffer(N * S)
+    out = torch.empty(n * B, dtype=torch.uint8, device="cuda")
+    ids = rng.integers(0, N, n)
+    d_ids = torch.from_numpy(ids).cuda()
+    counts = torch.zeros(8 * B, dtype=torch.int32, device="cuda")
+    mask = torch.zeros(B // 4, dtype=torch.int32, device="cuda")
+    bitval = torch.zeros_like(mask)
+    results = []
+
+    def measure(label, C, extra):
+        n_c = ibp.num_chunks(B, C)
+        part = torch.zeros((N * n_c + 31) // 32, dtype=torch.int32, device="cuda")
+        lengths = torch.zeros(N, dtype=torch.int32, device="cuda")
+        ibp.build_metadata(raw, S, None, N, B, 0.99, mask, bitval, counts)
+        ibp.compress(raw, S, N, 0, N, B, C, mask, bitval, store, S, part, lengths)
+        ms = statistics.median(timed_launches(
+            torch, lambda k: ibp.gather_decompress(store, N * S, S, None, part, N, d_ids, n, B, C,
+                                                   mask, bitval, out), 3, 20))
+        got = out.view(n, B)[:16].cpu().numpy()
+        if not (got == raw.array.reshape(N, S)[ids[:16]]).all():
+            raise SystemExit("bench: sweep gather is not lossless")
+        L = lengths.cpu().numpy().astype(np.float64)
+        ratio = float(L[ids].mean()) / B
+        dec = n * B / (ms * 1e-3) / 1e9
+        ideal = link / ratio
+        r = {"case": label, "chunk_bytes": C, "saving": round(1 - ratio, 4),
+             "kernel_us": round(ms * 1e3, 2), "decompressed_GBps": round(dec, 1),
+             "ideal_GBps": round(ideal, 1), "frac_of_ideal": round(dec / ideal, 4), **extra}
+        results.append(r)
+        log(f"sweep {r}")
+
+    words = raw.array.reshape(N, S).view(np.uint32)
+    for k in (32, 28, 24, 20, 16, 12, 8, 4):
+        hi = rng.integers(0, 1 << 32, B // 4, dtype=np.uint64).astype(np.uint32)
+        low = (1 << k) - 1
+        for i in range(0, N, 8192):
+            r = rng.integers(0, 1 << 32, (min(8192, N - i), B // 4), dtype=np.uint64)
+            words[i:i + 8192] = (r.astype(np.uint32) & np.uint32(low)) | (hi & np.uint32(~low & 0xFFFFFFFF))
+        for C in (256, 1024, 4096):
+            measure(f"kept {k} of 32 bits", C, {"kept_bits": k})
+    # BF16 weights: 2,048 values N(0, 0.02) per 4 KB tensor
+    for i in range(0, N, 8192):
+        x = (rng.standard_normal((min(8192, N - i), B // 2)) * 0.02).astype(np.float32)
+        # bfloat16 = the high half of the float32 encoding (truncated)
+        words[i:i + 8192] = (x.view(np.uint32) >> 16).astype(np.uint16).view(np.uint32)
+    for C in (256, 1024, 4096):
+        measure("bf16 weights N(0, 0.02)", C, {"dtype": "bf16"})
+    raw.free()
+    store.free()
+    print(json.dumps({"metric": "decompressed GB/s against space saving (pinned host store)",
+                      "unit": "GB/s", "higher_is_better": True, "link_peak_GBps": link,
+                      "ids": n, "tensors": N, "tensor_bytes": B, "results": results,
+                      "device": torch.cuda.get_device_name(0)}), flush=True)
+
+
+def run_kv_step(torch, ibp, W, args, pr):
+    """The online K/V path on OPT-13B shapes ([JH] LLM paragraph): Mask and
+    Bitval of each (layer, K|V) pair from its own prefill K/V (38,400 rows),
+    compress-on-write of each decode token's 20 rows into the pinned store, and
+    the decode step's fetch: one gather + decompress launch of 2,560 rows per
+    pair, 80 launches, against an uncompressed GPU gather of the same rows."""
+    import numpy as np
+    w = W.WORKLOADS["kv_opt13b"]
+    P = max(1, min(W.KV_PAIRS, args.kv_pairs))
+    R = W.KV_ROWS_PER_PAIR
+    N, B, C, S = P * R, w.tensor_bytes, w.chunk_bytes, w.slot_bytes
+    n_c = ibp.num_chunks(B, C)
+    raw = ibp.HostBuffer(N * S)
+    W.rows(w, 0, N, out=raw.array.reshape(N, S)[:, :B])
+    store = ibp.HostBuffer(N * S)
+    part = torch.zeros((N * n_c + 31) // 32, dtype=torch.int32, device="cuda")
+    lengths = torch.zeros(N, dtype=torch.int32, device="cuda")
+    counts = torch.zeros(8 * B, dtype=torch.int32, device="cuda")
+    masks, meta_ms = [], []
+    for p in range(P):
+        pre = torch.from_numpy(W.kv_prefill_rows(w, p)).cuda()
+        m = torch.zeros(B // 4, dtype=torch.int32, device="cuda")
+        v = torch.zeros_like(m)
+        ms = timed_launches(torch, lambda k: ibp.build_metadata(pre, B, None, pre.shape[0], B,
+                                                                w.threshold, m, v, counts), 1, 3)
+        meta_ms.append(statistics.median(ms))
+        masks.append((m, v))
+        del pre
+        if p % 10 == 9:
+            log(f"kv-step: Mask/Bitval of {p + 1} pairs")
+    # compress-on-write: token j of every sequence, per pair (rows of a pair
+    # are stored token-major so one token's 20 rows are contiguous)
+    tok = W.KV_SEQS
+    tm = Timer(torch)
+    for j in range(W.KV_DECODE):
+        s0 = tm.start()
+        for p in range(P):
+            first = p * R + j * tok
+            ibp.compress(raw.ptr + first * S, S, tok, first, N, B, C, masks[p][0], masks[p][1],
+                         store, S, part, lengths)
+        tm.stop(s0)
+    write_ms = tm.ms()
+    L = lengths.cpu().numpy()
+    out = torch.empty(R * B, dtype=torch.uint8, device="cuda")
+    d_ids = [torch.arange(p * R, (p + 1) * R, dtype=torch.int64, device="cuda") for p in range(P)]
+
+    def step_ibp(k):
+        for p in range(P):
+            ibp.gather_decompress(store, N * S, S, None, part, N, d_ids[p], R, B, C, masks[p][0],
+                                  masks[p][1], out)
+
+    def step_raw(k):
+        for p in range(P):
+            ibp.raw_gather(raw, S, N, d_ids[p], R, B, out)
+    steps = max(3, min(args.steps, 20))
+    ibp_ms = statistics.median(timed_launches(torch, step_ibp, 2, steps))
+    raw_ms = statistics.median(timed_launches(torch, step_raw, 2, steps))
+    step_ibp(0)
+    torch.cuda.synchronize()
+    if not (out.view(R, B)[:32].cpu().numpy() == raw.array.reshape(N, S)[(P - 1) * R:
+                                                                         (P - 1) * R + 32, :B]).all():
+        raise SystemExit("bench: kv-step gather is not lossless")
+    dense = P * R * B
+    comp = float(L.astype(np.float64).sum())
+    link = max(pr["h2d_dma_GBps"], pr["h2d_zero_copy_read_GBps"])
+    res = {"metric": "OPT-13B K/V decode-step fetch (gather + decompress, 80 launches)",
+           "unit": "GB/s", "higher_is_better": True, "pairs": P,
+           "rows_per_launch": R, "tensor_bytes": B, "chunk_bytes": C,
+           "mean_payload_over_tensor": round(comp / (N * B), 5),
+           "step_ms": round(ibp_ms, 3), "decompressed_GBps": round(dense / (ibp_ms * 1e-3) / 1e9, 2),
+           "compressed_GBps_over_link": round(comp / (ibp_ms * 1e-3) / 1e9, 2),
+           "frac_of_link_peak": round(comp / (ibp_ms * 1e-3) / 1e9 / link, 4),
+           "raw_step_ms": round(raw_ms, 3), "speedup_vs_raw": round(raw_ms / ibp_ms, 3),
+           "prefill_mask_ms_per_pair": round(statistics.mean(meta_ms), 3),
+           "prefill_mask_ms_per_step": round(sum(meta_ms), 2),
+           "prefill_rows_per_pair": W.KV_PREFILL_ROWS,
+           "compress_on_write_us_per_token": round(statistics.median(write_ms) * 1e3, 1),
+           "device": torch.cuda.get_device_name(0)}
+    raw.free()
+    store.free()
+    print(json.dumps(res), flush=True)
 
 
 def main():
@@ -416,6 +718,12 @@ def main():
     log(f"device {torch.cuda.get_device_name(0)}; host {host_info()}")
     pr = probes(torch, ibp, flags)
     log(f"probes {pr}")
+    if args.mode == "ablation":
+        return run_ablation(torch, ibp, args, pr)
+    if args.mode == "sweep":
+        return run_sweep(torch, ibp, args, pr)
+    if args.mode == "kv-step":
+        return run_kv_step(torch, ibp, W, args, pr)
 
     # --- headline: the workload from pinned host memory
     key = args.workload
@@ -482,6 +790,10 @@ def main():
         "host": host_info(),
         "device": torch.cuda.get_device_name(0),
     }
+    log("cache + store at a 10 % HBM budget ...")
+    batches_dev = [torch.from_numpy(i).cuda() for i in m["ids_host"]]
+    result["hybrid_path"] = measure_hybrid(torch, ibp, table, batches_dev, m["ids_host"], args,
+                                           0.10)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline(table, m["ids_host"][args.warmup:], args.cpu_seconds)

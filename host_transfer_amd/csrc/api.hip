@@ -351,9 +351,9 @@ int ibp_host_free(void* ptr) {
 int ibp_raw_gather(const void* src, uint64_t row_stride, uint64_t n_rows, const int64_t* ids,
                    uint64_t n_ids, uint32_t row_bytes, void* out, void* stream) {
   if (!src || !ids || !out) return fail(IBP_ERR_NULL, "ibp_raw_gather: src, ids and out are required");
-  if (row_bytes == 0 || row_bytes % 4 != 0 || row_stride < row_bytes || row_stride % 16 != 0)
-    return fail(IBP_ERR_SIZE, "ibp_raw_gather: row_bytes %% 4, row_stride >= row_bytes and %% 16");
-  if (!aligned(src, 16) || !aligned(out, 16) || !aligned(ids, 8))
+  if (row_bytes == 0 || row_bytes % 4 != 0 || row_stride < row_bytes || row_stride % 4 != 0)
+    return fail(IBP_ERR_SIZE, "ibp_raw_gather: row_bytes %% 4, row_stride >= row_bytes and %% 4");
+  if (!aligned(src, 4) || !aligned(out, 4) || !aligned(ids, 8))
     return fail(IBP_ERR_ALIGN, "ibp_raw_gather: misaligned pointer");
   int r;
   if ((r = require_device("ibp_raw_gather"))) return r;

@@ -8,16 +8,17 @@
 
 namespace ibp {
 
-// One wave per output row.  16 B units when the row size allows it, else 4 B.
+// One wave per output row.  16 B units when rows, stride and buffers are all
+// 16 B aligned ("aligned" transfers), else 4 B units (rows packed at any 4 B
+// stride: the unaligned zero-copy baseline).
 __global__ __launch_bounds__(256) void k_raw_gather(const uint8_t* __restrict__ src,
                                                      uint64_t row_stride, uint64_t n_rows,
                                                      const int64_t* __restrict__ ids,
                                                      uint64_t n_ids, uint32_t row_bytes,
-                                                     uint8_t* __restrict__ out) {
+                                                     uint8_t* __restrict__ out, bool wide) {
   const uint32_t lane = lane_id();
   const uint64_t wave = (uint64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   const uint64_t waves = (uint64_t)gridDim.x * (blockDim.x / kWave);
-  const bool wide = (row_bytes & 15u) == 0;
   for (uint64_t r = wave; r < n_ids; r += waves) {
     const int64_t id = ids[r];
     const bool valid = id >= 0 && (uint64_t)id < n_rows;
@@ -59,8 +60,9 @@ hipError_t launch_raw_gather(const uint8_t* src, uint64_t row_stride, uint64_t n
   if (e != hipSuccess) return e;
   const uint64_t want = (n_ids + 3) / 4;
   const uint64_t cap = (uint64_t)di.cus * 8;
+  const bool wide = ((row_bytes | row_stride | (uintptr_t)src | (uintptr_t)out) & 15u) == 0;
   hipLaunchKernelGGL(k_raw_gather, dim3((uint32_t)(want < cap ? want : cap)), dim3(256), 0, s,
-                     src, row_stride, n_rows, ids, n_ids, row_bytes, out);
+                     src, row_stride, n_rows, ids, n_ids, row_bytes, out, wide);
   return hipGetLastError();
 }
 

@@ -143,7 +143,7 @@ def _draw_block(w: Workload, block: int, stream: int = STREAM_DATA, n_rows: int 
         x = r.random((rows, w.tensor_bytes // 4), dtype=np.float32) * np.float32(0.1)
         x -= np.float32(0.05)
     elif w.key == "kv_opt13b":
-        # block = one (layer, K|V) pair; stream PREFILL draws its prompt rows
+        # block = one (layer, K|V) pair's decode rows
         s = kv_scales(w, block)
         x = (r.standard_normal((rows, KV_CHANNELS), dtype=np.float32) * s[None, :])
         x = x.astype(np.float16)
@@ -181,9 +181,31 @@ def rows(w: Workload, start: int = 0, count: int | None = None, out: np.ndarray 
     return out
 
 
-def kv_prefill_rows(w: Workload, pair: int, n_rows: int = KV_PREFILL_ROWS) -> np.ndarray:
-    """Prompt K/V rows of one (layer, K|V) pair: the sample its Mask comes from."""
-    return _draw_block(w, pair, STREAM_PREFILL, n_rows)
+KV_PREFILL_BLOCK = 4096
+
+
+def kv_prefill_rows(w: Workload, pair: int, n_rows: int = KV_PREFILL_ROWS,
+                    threads: int | None = None) -> np.ndarray:
+    """Prompt K/V rows of one (layer, K|V) pair: the sample its Mask comes
+    from.  Drawn in blocks of 4,096 rows, each from its own seeded stream."""
+    s = kv_scales(w, pair)
+    out = np.empty((n_rows, w.tensor_bytes), np.uint8)
+
+    def fill(b):
+        lo, hi = b * KV_PREFILL_BLOCK, min(n_rows, (b + 1) * KV_PREFILL_BLOCK)
+        r = _rng(w.wid, STREAM_PREFILL, pair, b)
+        x = r.standard_normal((hi - lo, KV_CHANNELS), dtype=np.float32) * s[None, :]
+        out[lo:hi] = x.astype(np.float16).view(np.uint8).reshape(hi - lo, w.tensor_bytes)
+
+    nb = (n_rows + KV_PREFILL_BLOCK - 1) // KV_PREFILL_BLOCK
+    nt = threads or _threads()
+    if nt == 1 or nb == 1:
+        for b in range(nb):
+            fill(b)
+    else:
+        with cf.ThreadPoolExecutor(nt) as ex:
+            list(ex.map(fill, range(nb)))
+    return out
 
 
 # ---------------------------------------------------------------- ids

@@ -261,8 +261,10 @@ int ibp_host_free(void *ptr);
  * streaming read that measures the link or HBM read rate. */
 
 /* out row r = row_bytes bytes at src + ids[r]*row_stride.  Ids outside
- * [0, n_rows) give zero rows.  src device or host-mapped; row_stride and
- * src 16 B aligned; out 16 B aligned; row_bytes % 4 == 0. */
+ * [0, n_rows) give zero rows.  src device or host-mapped; row_bytes,
+ * row_stride, src and out multiples of 4.  When all four are multiples of 16
+ * the rows move in 16 B units (aligned transfers), else in 4 B units (the
+ * unaligned GPU copy the pages compare against). */
 int ibp_raw_gather(const void *src, uint64_t row_stride, uint64_t n_rows,
                    const int64_t *ids, uint64_t n_ids, uint32_t row_bytes,
                    void *out, void *stream);

@@ -116,6 +116,8 @@ def test_other_validation(ibp):
     _expect(ibp, ibp.ERR_NULL, ibp.compact, P, 512, 10, P, 0, 100)
     _expect(ibp, ibp.ERR_SIZE, ibp.compact, P, 500, 10, P, P, 100)
     _expect(ibp, ibp.ERR_SIZE, ibp.raw_gather, P, 512, 10, P, 4, 514, P)
+    _expect(ibp, ibp.ERR_SIZE, ibp.raw_gather, P, 514, 10, P, 4, 512, P)
+    _expect(ibp, ibp.ERR_ALIGN, ibp.raw_gather, P + 2, 512, 10, P, 4, 512, P)
     _expect(ibp, ibp.ERR_SIZE, ibp.stream_read, P, 100, 0, P)
     with pytest.raises(ibp.IbpError) as e:
         ibp.host_alloc(1024, 7)
