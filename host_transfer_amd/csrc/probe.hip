@@ -8,27 +8,33 @@
 
 namespace ibp {
 
-// One wave per output row.  16 B units when rows, stride and buffers are all
+// 2^lanes_log2 lanes per output row (up to a whole wave; several rows per
+// wave when rows are short and the batch is large).  16 B units when rows, stride and buffers are all
 // 16 B aligned ("aligned" transfers), else 4 B units (rows packed at any 4 B
 // stride: the unaligned zero-copy baseline).
 __global__ __launch_bounds__(256) void k_raw_gather(const uint8_t* __restrict__ src,
                                                      uint64_t row_stride, uint64_t n_rows,
                                                      const int64_t* __restrict__ ids,
                                                      uint64_t n_ids, uint32_t row_bytes,
-                                                     uint8_t* __restrict__ out, bool wide) {
+                                                     uint8_t* __restrict__ out, bool wide,
+                                                     uint32_t lanes_log2) {
   const uint32_t lane = lane_id();
+  const uint32_t lanes = 1u << lanes_log2;
+  const uint32_t sub = lane >> lanes_log2, q0 = lane & (lanes - 1);
+  const uint32_t rows_per_wave = kWave >> lanes_log2;
   const uint64_t wave = (uint64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   const uint64_t waves = (uint64_t)gridDim.x * (blockDim.x / kWave);
-  for (uint64_t r = wave; r < n_ids; r += waves) {
+  for (uint64_t r = wave * rows_per_wave + sub; r < n_ids + sub; r += waves * rows_per_wave) {
+    if (r >= n_ids) continue;
     const int64_t id = ids[r];
     const bool valid = id >= 0 && (uint64_t)id < n_rows;
     const uint8_t* s = src + (valid ? (uint64_t)id * row_stride : 0);
     uint8_t* d = out + r * row_bytes;
     if (wide) {
-      for (uint32_t q = lane; q < row_bytes / 16; q += kWave)
+      for (uint32_t q = q0; q < row_bytes / 16; q += lanes)
         ((uint4*)d)[q] = valid ? ((const uint4*)s)[q] : make_uint4(0, 0, 0, 0);
     } else {
-      for (uint32_t q = lane; q < row_bytes / 4; q += kWave)
+      for (uint32_t q = q0; q < row_bytes / 4; q += lanes)
         ((uint32_t*)d)[q] = valid ? ((const uint32_t*)s)[q] : 0u;
     }
   }
@@ -58,11 +64,18 @@ hipError_t launch_raw_gather(const uint8_t* src, uint64_t row_stride, uint64_t n
   DeviceInfo di;
   hipError_t e = device_info(&di);
   if (e != hipSuccess) return e;
-  const uint64_t want = (n_ids + 3) / 4;
-  const uint64_t cap = (uint64_t)di.cus * 8;
   const bool wide = ((row_bytes | row_stride | (uintptr_t)src | (uintptr_t)out) & 15u) == 0;
+  const uint32_t units = row_bytes / (wide ? 16 : 4);
+  uint32_t lanes_log2 = 0;
+  while ((1u << lanes_log2) < units && (1u << lanes_log2) < (uint32_t)kWave) ++lanes_log2;
+  // several rows per wave only while the batch still fills every CU with
+  // waves (a wave per row keeps more requests in flight on small batches)
+  while (lanes_log2 < 6 && n_ids / (kWave >> lanes_log2) < (uint64_t)di.cus * 32) ++lanes_log2;
+  const uint64_t rows_per_block = 4ull * (kWave >> lanes_log2);
+  const uint64_t want = (n_ids + rows_per_block - 1) / rows_per_block;
+  const uint64_t cap = (uint64_t)di.cus * 8;
   hipLaunchKernelGGL(k_raw_gather, dim3((uint32_t)(want < cap ? want : cap)), dim3(256), 0, s,
-                     src, row_stride, n_rows, ids, n_ids, row_bytes, out, wide);
+                     src, row_stride, n_rows, ids, n_ids, row_bytes, out, wide, lanes_log2);
   return hipGetLastError();
 }
 

@@ -192,17 +192,26 @@ def test_compress_in_pieces_matches_whole():
     assert (a[valid] == b[valid]).all()
 
 
-def test_raw_gather_and_stream_read():
+@pytest.mark.parametrize("B,stride,shift,m", [(5732, 5760, 0, 777), (64, 128, 0, 777),
+                                               (64, 128, 0, 140000), (64, 64, 4, 140000),
+                                               (4, 4, 0, 600000), (256, 256, 4, 777),
+                                               (60, 68, 0, 300000), (4096, 4096, 0, 777),
+                                               (16384, 16384, 4, 777)])
+def test_raw_gather_and_stream_read(B, stride, shift, m):
+    """Uncompressed baseline gather: several rows per wave for short rows in
+    large batches, 4 B units for rows at a 4 B offset, zero rows for invalid
+    ids."""
     from host_transfer_amd import ibp
-    rng = np.random.default_rng(11)
-    n, B, stride = 500, 5732, 5760
+    rng = np.random.default_rng(11 + B)
+    n = 500
     raw = rng.integers(0, 256, (n, stride), dtype=np.uint8)
-    hb = ibp.HostBuffer(n * stride)
-    hb.array[:] = raw.ravel()
-    ids = rng.integers(-2, n + 2, 300)
-    out = torch.zeros(300 * B, dtype=torch.int8, device="cuda")
-    ibp.raw_gather(hb, stride, n, G.dev(ids), 300, B, out)
-    got = G.host(out).view(np.uint8).reshape(300, B)
+    hb = ibp.HostBuffer(n * stride + shift)
+    hb.array[shift:] = raw.ravel()
+    ids = rng.integers(-2, n + 2, m)
+    G.log(f"[parity] raw gather B={B} stride={stride} shift={shift} ids={m}")
+    out = torch.zeros(m * B, dtype=torch.int8, device="cuda")
+    ibp.raw_gather(hb.ptr + shift, stride, n, G.dev(ids), m, B, out)
+    got = G.host(out).view(np.uint8).reshape(m, B)
     assert (got == G.expected_rows(raw[:, :B].copy(), ids)).all()
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     ibp.stream_read(hb, n * stride, 0x9E3779B9, sink)
