@@ -198,31 +198,42 @@ class Table:
                               self.bitval, out)
 
 
-def time_gather(torch, ibp, table, batches, warmup, steps, out, raw_baseline=False):
-    """Warm-up, then `steps` launches bracketed by synchronisations.
-    Returns (wall seconds, per-launch kernel ms list)."""
-    w = table.w
-    n = w.batch
+def region_launches(torch, fn, warmup, steps):
+    """`steps` launches back to back after `warmup`, bracketed by one pair of
+    HIP events on the launch stream and by synchronisations.  Returns (mean ms
+    per launch from the events, wall seconds of the region)."""
     for k in range(warmup):
-        d = batches[k]
-        if raw_baseline:
-            ibp.raw_gather(table.raw, w.slot_bytes, w.n_tensors, d, n, w.tensor_bytes, out)
-        else:
-            table.gather(ibp, d, n, out)
+        fn(k)
     torch.cuda.synchronize()
-    tm = Timer(torch)
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    a.record()
     for k in range(warmup, warmup + steps):
-        d = batches[k]
-        s = tm.start()
-        if raw_baseline:
-            ibp.raw_gather(table.raw, w.slot_bytes, w.n_tensors, d, n, w.tensor_bytes, out)
-        else:
-            table.gather(ibp, d, n, out)
-        tm.stop(s)
+        fn(k)
+    b.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, tm.ms()
+    return a.elapsed_time(b) / steps, wall
+
+
+def time_gather(torch, ibp, table, batches, warmup, steps, out, raw_baseline=False):
+    """The timed region (`steps` launches back to back), then the same
+    launches again one at a time between their own events.  Returns (wall
+    seconds of the region, mean ms per launch in the region, per-launch ms of
+    the isolated launches)."""
+    w = table.w
+    n = w.batch
+
+    def run(k):
+        d = batches[k]
+        if raw_baseline:
+            ibp.raw_gather(table.raw, w.slot_bytes, w.n_tensors, d, n, w.tensor_bytes, out)
+        else:
+            table.gather(ibp, d, n, out)
+    region_ms, wall = region_launches(torch, run, warmup, steps)
+    isolated = timed_launches(torch, run, warmup, steps)  # ends on the last batch again
+    return wall, region_ms, isolated
 
 
 def check_rows(table, ids_host, out):
@@ -321,14 +332,16 @@ def measure_workload(torch, ibp, W, key, T, where, host_flags, steps, warmup, wi
     ids_host = [W.batch_ids(w, k) for k in range(nb)]
     batches = [torch.from_numpy(i).cuda() for i in ids_host]
     out = torch.empty(w.batch * w.tensor_bytes, dtype=torch.uint8, device="cuda")
-    wall, ms = time_gather(torch, ibp, table, batches, warmup, steps, out)
+    wall, region_ms, ms = time_gather(torch, ibp, table, batches, warmup, steps, out)
     check_rows(table, ids_host[-1], out)
     comp = [int(table.len_host[i].sum()) for i in ids_host[warmup:]]
-    res = {"table": table, "ids_host": ids_host, "wall": wall, "kernel_ms": ms,
-           "comp_bytes": comp, "T": T}
+    res = {"table": table, "ids_host": ids_host, "wall": wall, "kernel_ms": region_ms,
+           "isolated_ms": ms, "comp_bytes": comp, "T": T}
     if with_raw:
-        rwall, rms = time_gather(torch, ibp, table, batches, warmup, steps, out, raw_baseline=True)
-        res["raw_kernel_ms"] = rms
+        _, rregion, rms = time_gather(torch, ibp, table, batches, warmup, steps, out,
+                                      raw_baseline=True)
+        res["raw_kernel_ms"] = rregion
+        res["raw_isolated_ms"] = rms
     return res
 
 
@@ -360,8 +373,9 @@ def measure_hbm(torch, ibp, W, key, flags, args, pr):
 
         def run_raw(k):
             ibp.raw_gather(raw_dev, S, N, d[k], nb, B, out)
-        kms = timed_launches(torch, run_ibp, args.warmup, steps)
-        rms = timed_launches(torch, run_raw, args.warmup, steps)
+        km, _ = region_launches(torch, run_ibp, args.warmup, steps)
+        rm, _ = region_launches(torch, run_raw, args.warmup, steps)
+        kiso = statistics.mean(timed_launches(torch, run_ibp, 0, steps))
         last = seqs[-1]
         run_ibp(len(seqs) - 1)
         torch.cuda.synchronize()
@@ -370,11 +384,10 @@ def measure_hbm(torch, ibp, W, key, flags, args, pr):
         want = raw_dev.view(N, S)[torch.from_numpy(last[pick]).cuda(), :B].cpu().numpy()
         if not (got == want).all():
             raise SystemExit(f"bench: {key} HBM gather differs from the original rows")
-        km, rm = statistics.mean(kms), statistics.mean(rms)
         comp = statistics.mean(float(table.len_host[i].sum()) for i in seqs[args.warmup:])
         traffic = comp + nb * (B + 16)
         res["batches"].append({
-            "ids": nb, "kernel_us": round(km * 1e3, 2),
+            "ids": nb, "kernel_us": round(km * 1e3, 2), "isolated_launch_us": round(kiso * 1e3, 2),
             "decompressed_GBps": round(nb * B / (km * 1e-3) / 1e9, 1),
             "roofline": {"bound": "hbm", "achieved": round(traffic / (km * 1e-3) / 1e9, 1),
                          "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -425,7 +438,7 @@ def measure_hybrid(torch, ibp, table, batches, ids_host, args, budget_fraction):
         def run(i):
             ibp.gather_decompress_hybrid(store, N * S, S, cache, total, offsets, bits, N,
                                          batches[i], w.batch, B, C, mask, bitval, out)
-        ms = statistics.mean(timed_launches(torch, run, args.warmup, args.steps))
+        ms, _ = region_launches(torch, run, args.warmup, args.steps)
         run(len(batches) - 1)
         torch.cuda.synchronize()
         got = out.view(w.batch, B)[:64].cpu().numpy()
@@ -499,13 +512,13 @@ def run_ablation(torch, ibp, args, pr):
         out = torch.empty(n * size, dtype=torch.uint8, device="cuda")
         r = {"tensor_bytes": size}
         # GPU zero-copy, 128 B-aligned rows, 16 B loads
-        ms = timed_launches(torch, lambda k: ibp.raw_gather(hb, S, n_al, d_ids, n, size, out),
-                            3, 20)
-        r["gpu_aligned_GBps"] = round(n * size / (statistics.median(ms) * 1e-3) / 1e9, 2)
+        ms, _ = region_launches(torch, lambda k: ibp.raw_gather(hb, S, n_al, d_ids, n, size, out),
+                                3, 20)
+        r["gpu_aligned_GBps"] = round(n * size / (ms * 1e-3) / 1e9, 2)
         # GPU zero-copy, packed rows at a 4 B offset, 4 B loads
-        ms = timed_launches(torch, lambda k: ibp.raw_gather(hb.ptr + 4, size, n_pk, d_ids, n,
-                                                            size, out), 3, 20)
-        r["gpu_unaligned_GBps"] = round(n * size / (statistics.median(ms) * 1e-3) / 1e9, 2)
+        ms, _ = region_launches(torch, lambda k: ibp.raw_gather(hb.ptr + 4, size, n_pk, d_ids, n,
+                                                                size, out), 3, 20)
+        r["gpu_unaligned_GBps"] = round(n * size / (ms * 1e-3) / 1e9, 2)
         # CPU gather into pinned staging (all host threads) + one DMA
         staging = ibp.HostBuffer(n * size)
         stage = staging.array.reshape(n, size)
@@ -577,9 +590,9 @@ def run_sweep(torch, ibp, args, pr):
         lengths = torch.zeros(N, dtype=torch.int32, device="cuda")
         ibp.build_metadata(raw, S, None, N, B, 0.99, mask, bitval, counts)
         ibp.compress(raw, S, N, 0, N, B, C, mask, bitval, store, S, part, lengths)
-        ms = statistics.median(timed_launches(
+        ms, _ = region_launches(
             torch, lambda k: ibp.gather_decompress(store, N * S, S, None, part, N, d_ids, n, B, C,
-                                                   mask, bitval, out), 3, 20))
+                                                   mask, bitval, out), 3, 20)
         got = out.view(n, B)[:16].cpu().numpy()
         if not (got == raw.array.reshape(N, S)[ids[:16]]).all():
             raise SystemExit("bench: sweep gather is not lossless")
@@ -672,8 +685,8 @@ def run_kv_step(torch, ibp, W, args, pr):
         for p in range(P):
             ibp.raw_gather(raw, S, N, d_ids[p], R, B, out)
     steps = max(3, min(args.steps, 20))
-    ibp_ms = statistics.median(timed_launches(torch, step_ibp, 2, steps))
-    raw_ms = statistics.median(timed_launches(torch, step_raw, 2, steps))
+    ibp_ms, _ = region_launches(torch, step_ibp, 2, steps)
+    raw_ms, _ = region_launches(torch, step_raw, 2, steps)
     step_ibp(0)
     torch.cuda.synchronize()
     if not (out.view(R, B)[:32].cpu().numpy() == raw.array.reshape(N, S)[(P - 1) * R:
@@ -733,10 +746,10 @@ def main():
     K = args.steps
     dense_bytes = w.batch * w.tensor_bytes
     value = dense_bytes * K / m["wall"] / 1e9
-    kern_ms = statistics.mean(m["kernel_ms"])
+    kern_ms = m["kernel_ms"]
     comp = statistics.mean(m["comp_bytes"])
     achieved = comp / (kern_ms * 1e-3) / 1e9
-    raw_ms = statistics.mean(m["raw_kernel_ms"])
+    raw_ms = m["raw_kernel_ms"]
     link_peak = max(pr["h2d_dma_GBps"], pr["h2d_zero_copy_read_GBps"])
     log(f"{key}: {value:.1f} GB/s decompressed, kernel {kern_ms * 1e3:.1f} us, "
         f"{achieved:.1f} GB/s compressed over the link, raw gather {raw_ms * 1e3:.1f} us")
@@ -776,6 +789,9 @@ def main():
             "frac_of_zero_copy_read": round(achieved / pr["h2d_zero_copy_read_GBps"], 4),
             "kernel": "k_gather_decompress",
             "kernel_us": round(kern_ms * 1e3, 2),
+            "isolated_launch_us": {"mean": round(statistics.mean(m["isolated_ms"]) * 1e3, 2),
+                                   "min": round(min(m["isolated_ms"]) * 1e3, 2),
+                                   "max": round(max(m["isolated_ms"]) * 1e3, 2)},
             "bytes_per_launch": round(comp, 1),
         },
         "compression": {

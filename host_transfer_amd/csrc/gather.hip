@@ -85,8 +85,34 @@ struct Source {
   bool ok;
 };
 
-__device__ __forceinline__ Source row_source(const GatherArgs& a, uint64_t t) {
-  const uint64_t o = *(a.offsets ? a.offsets + t : (const uint64_t*)&g_zero16);
+// Marks the stage flags as redefined at the top of every loop iteration, so
+// the compiler tests their bits in place (one scalar register per word
+// position) rather than hoisting one 64-bit lane mask per stage out of the
+// loop, which overflows the scalar registers into spills.
+template <int J>
+__device__ __forceinline__ void keep_stage_flags(WordRegs<J>& R) {
+#pragma unroll
+  for (int j = 0; j < J; ++j) asm volatile("" : "+s"(R.stages[j]));
+}
+
+// The same for the shape fields: the few scalar instructions that derive
+// per-chunk values from them are cheaper inside the loop than the registers
+// (and spills) that hoisting every derived value costs.
+__device__ __forceinline__ void keep_shape(GatherArgs& a) {
+  asm volatile("" : "+s"(a.sh.n_c), "+s"(a.sh.wpc_log2), "+s"(a.sh.last_bits));
+}
+
+// The offset-table entry of tensor t as loaded (zero without a table; the
+// load is unconditional, see g_zero16).  It is resolved by source_of one
+// pipeline step later, so no wait for it sits in front of the loads issued
+// after it.
+__device__ __forceinline__ uint64_t load_offset(const GatherArgs& a, uint64_t t) {
+  return *(a.offsets ? a.offsets + t : (const uint64_t*)&g_zero16);
+}
+
+// Where tensor t's payload is: its cache entry when the table has one, else
+// its slot; avail bounds every read there.
+__device__ __forceinline__ Source source_of(const GatherArgs& a, uint64_t t, uint64_t o) {
   const bool hit = a.offsets != nullptr && o != kNotCached;
   const uint64_t so = t * a.slot_bytes;
   const uint64_t at = hit ? o : so;
@@ -98,12 +124,14 @@ __device__ __forceinline__ Source row_source(const GatherArgs& a, uint64_t t) {
   return r;
 }
 
-// What the first wave knows about one tensor before its payload is read.
+// One tensor's metadata as loaded, before its payload is read (consumed by
+// scan_row one pipeline step later).
 struct RowMeta {
-  uint64_t addr;   // payload address
-  uint64_t avail;  // whole 16 B units readable there, in bytes
-  uint32_t bits;   // participation word holding this lane's chunk bit (shifted)
-  bool valid;
+  uint64_t t;     // tensor index (0 for an invalid id)
+  uint64_t o;     // offset-table entry
+  uint32_t word;  // participation word holding this lane's chunk bit
+  uint32_t sh;    // position of that bit in it
+  bool valid;     // id in range
 };
 
 // The id of row `row`, or -1 past the batch.  The load itself is
@@ -113,37 +141,37 @@ __device__ __forceinline__ int64_t load_id(const GatherArgs& a, uint64_t row) {
   return row < a.n_ids ? id : -1;
 }
 
-// Participation word and payload offset of tensor `id` (lane c: chunk c).
+// Participation word and offset entry of tensor `id` (lane c: chunk c).
 // Unconditional loads: an invalid id reads tensor 0's entries, ignored later.
 __device__ __forceinline__ RowMeta load_meta(const GatherArgs& a, int64_t id, uint32_t lane) {
   RowMeta m;
   m.valid = id >= 0 && (uint64_t)id < a.n_tensors;
-  const uint64_t t = m.valid ? (uint64_t)id : 0ull;
+  m.t = m.valid ? (uint64_t)id : 0ull;
   const uint32_t c = min(lane % kWave, a.sh.n_c - 1u);
-  const uint64_t bit = t * a.sh.n_c + c;
-  m.bits = a.part_bits[bit >> 5] >> (bit & 31);
-  const Source src = row_source(a, t);
-  m.addr = src.addr;
-  m.avail = src.avail;
-  m.valid = m.valid && src.ok;
+  const uint64_t bit = m.t * a.sh.n_c + c;
+  m.word = a.part_bits[bit >> 5];
+  m.sh = (uint32_t)(bit & 31);
+  m.o = load_offset(a, m.t);
   return m;
 }
 
 // Participation, chunk offsets and payload length of one tensor (first wave).
 __device__ __forceinline__ void scan_row(const GatherArgs& a, const RowMeta& m, uint32_t lane,
                                          const uint32_t* s_kc, GroupHdr* hdr, uint32_t* obuf) {
-  const bool p = m.valid && lane < a.sh.n_c && (m.bits & 1u);
-  const uint32_t size = !m.valid || lane >= a.sh.n_c ? 0u : (p ? s_kc[lane] : chunk_bits(a.sh, lane));
+  const Source src = source_of(a, m.t, m.o);
+  const bool valid = m.valid && src.ok;
+  const bool p = valid && lane < a.sh.n_c && ((m.word >> m.sh) & 1u);
+  const uint32_t size = !valid || lane >= a.sh.n_c ? 0u : (p ? s_kc[lane] : chunk_bits(a.sh, lane));
   const uint32_t incl = wave_inclusive_sum(size);
   if (lane < a.sh.n_c) obuf[lane] = incl - size;
   const uint64_t pm = __ballot(p);
   const uint32_t total = __shfl(incl, kWave - 1, kWave);
   if (lane == 0) {
     hdr->pmask = pm;
-    hdr->valid = m.valid;
+    hdr->valid = valid;
     hdr->len = (total + 7u) >> 3;
-    hdr->addr = m.addr;
-    hdr->avail = m.avail;
+    hdr->addr = src.addr;
+    hdr->avail = src.avail;
   }
 }
 
@@ -213,6 +241,7 @@ __global__ __launch_bounds__(1024) void k_gather_decompress(GatherArgs a) {
   uint32_t cur = 0;
   for (uint64_t row = row0; row < a.n_ids; row += step, cur ^= 1u) {
     const bool has_next = row + step < a.n_ids;
+    keep_stage_flags<J>(R);
     // 1. scan of the next tensor (its metadata was loaded an iteration ago)
     if (first_wave && has_next) scan_row(a, meta_next, gl, s_kc, &hdrs[cur ^ 1u], obufs + 64u * (cur ^ 1u));
     // 2. this payload -> LDS
@@ -299,11 +328,11 @@ struct TileHdr {
 // Every lane loads (lanes >= T duplicate lane % T) and ids are clamped into
 // range, so the loads are unconditional.
 struct TileMeta {
-  uint64_t addr;
-  uint64_t avail;
+  uint64_t t;       // tensor index (0 for an invalid id)
+  uint64_t o;       // offset-table entry as loaded
   uint32_t w0, w1;  // bitmap words holding the tensor's chunk bits
   uint32_t sh;      // bit position of chunk 0 in w0
-  bool valid;
+  bool valid;       // id in range
 };
 
 __device__ __forceinline__ int64_t tile_row_id(const GatherArgs& a, uint64_t row) {
@@ -313,28 +342,27 @@ __device__ __forceinline__ int64_t tile_row_id(const GatherArgs& a, uint64_t row
 __device__ __forceinline__ TileMeta load_tile_meta(const GatherArgs& a, int64_t id) {
   TileMeta m;
   m.valid = id >= 0 && (uint64_t)id < a.n_tensors;
-  const uint64_t t = m.valid ? (uint64_t)id : 0ull;
-  const uint64_t bit = t * a.sh.n_c;
+  m.t = m.valid ? (uint64_t)id : 0ull;
+  const uint64_t bit = m.t * a.sh.n_c;
   const uint64_t q = bit >> 5;
   const uint64_t last_word = (a.n_tensors * a.sh.n_c - 1) >> 5;
   m.sh = bit & 31;
   m.w0 = a.part_bits[q];
   m.w1 = a.part_bits[q < last_word ? q + 1 : q];
-  const Source src = row_source(a, t);
-  m.addr = src.addr;
-  m.avail = src.avail;
-  m.valid = m.valid && src.ok;
+  m.o = load_offset(a, m.t);
   return m;
 }
 
 __device__ __forceinline__ TileHdr make_tile_hdr(const GatherArgs& a, const TileMeta& m,
                                                  const uint32_t* s_kc) {
   TileHdr h;
-  h.valid = m.valid;
-  h.addr = m.addr;
+  const Source src = source_of(a, m.t, m.o);
+  const bool valid = m.valid && src.ok;
+  h.valid = valid;
+  h.addr = src.addr;
   const uint32_t n_c = a.sh.n_c;
   const uint64_t word = (uint64_t)m.w0 | ((uint64_t)m.w1 << 32);
-  const uint32_t pm = m.valid ? (uint32_t)(word >> m.sh) & ((1u << n_c) - 1u) : 0u;
+  const uint32_t pm = valid ? (uint32_t)(word >> m.sh) & ((1u << n_c) - 1u) : 0u;
   uint32_t o = 0, offs[4];
 #pragma unroll
   for (uint32_t c = 0; c < 4; ++c) {  // n_c <= 4; chunks past n_c add nothing
@@ -347,8 +375,8 @@ __device__ __forceinline__ TileHdr make_tile_hdr(const GatherArgs& a, const Tile
   h.pmask = pm;
   // 16 B units: the payload rounded up to 16 B, never past the end of its
   // store or cache
-  const uint32_t len = m.valid ? (o + 7u) >> 3 : 0u;
-  h.n16 = (uint32_t)(min((uint64_t)((len + 15u) & ~15u), m.avail) >> 4);
+  const uint32_t len = valid ? (o + 7u) >> 3 : 0u;
+  h.n16 = (uint32_t)(min((uint64_t)((len + 15u) & ~15u), src.avail) >> 4);
   return h;
 }
 
@@ -368,6 +396,89 @@ __device__ __forceinline__ uint32_t tile_word(const GatherArgs& a, const WordReg
     v = window32(pb32, o + (R.info[j] >> 16));
   }
   return v;
+}
+
+// Unpack stages applied to N words of one word position at once: the stage
+// tests are made once for all of them.
+template <int N>
+__device__ __forceinline__ void unpack_stages_n(uint32_t (&x)[N], const uint32_t mv[5],
+                                                uint32_t stages) {
+  if (stages & 16u) {
+#pragma unroll
+    for (int q = 0; q < N; ++q) x[q] = bfi_op(mv[4], x[q] << 16, x[q]);
+  }
+  if (stages & 8u) {
+#pragma unroll
+    for (int q = 0; q < N; ++q) x[q] = bfi_op(mv[3], x[q] << 8, x[q]);
+  }
+  if (stages & 4u) {
+#pragma unroll
+    for (int q = 0; q < N; ++q) x[q] = bfi_op(mv[2], x[q] << 4, x[q]);
+  }
+  if (stages & 2u) {
+#pragma unroll
+    for (int q = 0; q < N; ++q) x[q] = bfi_op(mv[1], x[q] << 2, x[q]);
+  }
+  if (stages & 1u) {
+#pragma unroll
+    for (int q = 0; q < N; ++q) x[q] = bfi_op(mv[0], x[q] << 1, x[q]);
+  }
+}
+
+#ifndef IBP_TILE_GROUP
+#define IBP_TILE_GROUP 8
+#endif
+
+// Decodes and stores one full tile (W == 64 J) held in LDS.  Word position
+// j = the words lane + 64 j of every tensor: its chunk c_j is the same for
+// all lanes and tensors, so per tensor only the chunk's bit offset (read
+// across lanes from the header lane) and its participation bit (one ballot
+// per tile and j) vary.  Up to 16 tensors are decoded side by side, so their
+// LDS reads overlap and the stage tests are made once for all of them.
+// Invalid tensors have no participating chunk and an all-zero slot, so they
+// decode to zero words without a select.
+template <int J, int T>
+__device__ __forceinline__ void decode_full_tile(const GatherArgs& a, const WordRegs<J>& R,
+                                                 const uint8_t* pbufs, const TileHdr* hcur,
+                                                 uint32_t lane, uint64_t row0) {
+  constexpr uint32_t kW = (uint32_t)kWave * J;  // words per tensor
+  constexpr uint32_t kSlot = 4u * kW + 16u;     // LDS bytes per tensor
+  constexpr int TG = T < IBP_TILE_GROUP ? T : IBP_TILE_GROUP;  // tensors decoded side by side
+  const TileHdr& hl = hcur[lane & (uint32_t)(T - 1)];
+  const uint32_t hpm = hl.pmask, ho1 = hl.off[0], ho2 = hl.off[1], ho3 = hl.off[2];
+  uint32_t* obase = a.out + row0 * kW + lane;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const uint32_t c = uniform(((uint32_t)kWave * j) >> a.sh.wpc_log2);
+    const uint32_t oj = c == 0 ? 0u : c == 1 ? ho1 : c == 2 ? ho2 : ho3;
+    const uint32_t pbits = (uint32_t)__builtin_amdgcn_ballot_w64(((hpm >> c) & 1u) != 0u);
+    const uint32_t lo = R.info[j] & 0xFFFFu, hi = R.info[j] >> 16;
+#pragma unroll
+    for (int i0 = 0; i0 < T; i0 += TG) {
+      uint32_t x[TG];
+#pragma unroll
+      for (int q = 0; q < TG; ++q) {
+        const int i = i0 + q;
+        const uint32_t o = __builtin_amdgcn_readlane(oj, i);
+        const uint32_t* pb32 = (const uint32_t*)(pbufs + i * kSlot);
+        x[q] = window32(pb32, o + (((pbits >> i) & 1u) ? lo : hi));
+      }
+      constexpr uint32_t gmask = TG == 32 ? ~0u : (1u << TG) - 1u;
+      const uint32_t gp = (pbits >> i0) & gmask;
+      if (gp == gmask) {  // every tensor of the group keeps chunk c packed
+        unpack_stages_n<TG>(x, R.mv[j], R.stages[j]);
+#pragma unroll
+        for (int q = 0; q < TG; ++q) x[q] = bfi_op(R.mask[j], R.bitval[j], x[q]);
+      } else if (gp != 0u) {  // some tensors store chunk c whole: one at a time
+#pragma unroll
+        for (int q = 0; q < TG; ++q)
+          if ((gp >> q) & 1u)
+            x[q] = bfi_op(R.mask[j], R.bitval[j], unpack_stages(x[q], R.mv[j], R.stages[j]));
+      }
+#pragma unroll
+      for (int q = 0; q < TG; ++q) obase[(uint64_t)(i0 + q) * kW + (uint32_t)kWave * j] = x[q];
+    }
+  }
 }
 
 // RPI tensors per load instruction (LPR = 64/RPI lanes each, one 16 B unit
@@ -418,6 +529,10 @@ __global__ __launch_bounds__(256) void k_gather_tile(GatherArgs a) {
   uint4 v0, v1, v2, v3, v4, v5, v6, v7;
   uint32_t n0 = 0, n1 = 0, n2 = 0, n3 = 0, n4 = 0, n5 = 0, n6 = 0, n7 = 0;
   const uint32_t lrow = lane / LPR, lunit = lane % LPR;
+  // every unit of a slot that a lane covers is written (zeros past the
+  // payload: lanes past it loaded g_zero16), so a slot never holds a stale
+  // payload and an invalid tensor's slot is all zero
+  const uint32_t slot16 = a.pbuf_bytes >> 4;
 #define IBP_TILE_LOAD(k, hdr)                                                                  \
   if constexpr (k < NL) {                                                                      \
     const TileHdr& h_ = (hdr)[k * RPI + lrow];                                                 \
@@ -429,13 +544,15 @@ __global__ __launch_bounds__(256) void k_gather_tile(GatherArgs a) {
   IBP_TILE_LOAD(4, hdr) IBP_TILE_LOAD(5, hdr) IBP_TILE_LOAD(6, hdr) IBP_TILE_LOAD(7, hdr)
 #define IBP_TILE_STAGE(k)                                                                      \
   if constexpr (k < NL) {                                                                      \
-    if (lunit < n##k) ((uint4*)(pbufs + (k * RPI + lrow) * a.pbuf_bytes))[lunit] = v##k;       \
+    if (lunit < slot16) ((uint4*)(pbufs + (k * RPI + lrow) * a.pbuf_bytes))[lunit] = v##k;     \
   }
   IBP_TILE_ISSUE_LOADS(hdrs)
 
   uint32_t cur = 0;
   for (uint64_t tile = tile0; tile < n_tiles; tile += waves, cur ^= 1u) {
     const bool has_next = tile + waves < n_tiles;
+    keep_stage_flags<J>(R);
+    keep_shape(a);
     TileHdr* hcur = hdrs + cur * T;
     TileHdr* hnext = hdrs + (cur ^ 1u) * T;
     // a. this tile's payloads -> LDS
@@ -457,7 +574,9 @@ __global__ __launch_bounds__(256) void k_gather_tile(GatherArgs a) {
     //    the 64 words lane l handles for one j lie in one chunk: chunk,
     //    participation and offset are wave-uniform.
     const uint64_t row0 = tile * T;
-    if (tile < n_full) {
+    if (FULL && tile < n_full) {
+      decode_full_tile<J, T>(a, R, pbufs, hcur, lane, row0);
+    } else if (tile < n_full) {
 #pragma unroll 1
       for (int i = 0; i < T; ++i) {
         const TileHdr* hp = hcur + i;
