@@ -107,7 +107,7 @@ __device__ __forceinline__ void keep_shape(GatherArgs& a) {
 // pipeline step later, so no wait for it sits in front of the loads issued
 // after it.
 __device__ __forceinline__ uint64_t load_offset(const GatherArgs& a, uint64_t t) {
-  return *(a.offsets ? a.offsets + t : (const uint64_t*)&g_zero16);
+  return load_global(a.offsets ? a.offsets + t : (const uint64_t*)&g_zero16);
 }
 
 // Where tensor t's payload is: its cache entry when the table has one, else
@@ -192,7 +192,7 @@ __global__ __launch_bounds__(1024) void k_gather_decompress(GatherArgs a) {
   uint32_t* s_wsum = (uint32_t*)(smem + L.wsum);
 
   const uint32_t G = a.sh.group;
-  const uint32_t g = threadIdx.x / G;
+  const uint32_t g = uniform(threadIdx.x / G);  // G >= 64: one group per wave or more
   const uint32_t gl = threadIdx.x - g * G;
   uint8_t* gbase = smem + L.group0 + g * L.group_stride;
   GroupHdr* hdrs = (GroupHdr*)gbase;                                   // [2]
@@ -234,8 +234,8 @@ __global__ __launch_bounds__(1024) void k_gather_decompress(GatherArgs a) {
     const GroupHdr h = hdrs[0];
     const uint32_t n16 = payload_units(a, h);
     const uint4* src = (const uint4*)h.addr;
-    v0 = *(gl < n16 ? src + gl : &g_zero16);
-    v1 = *(gl + G < n16 ? src + gl + G : &g_zero16);
+    v0 = load_global(gl < n16 ? src + gl : &g_zero16);
+    v1 = load_global(gl + G < n16 ? src + gl + G : &g_zero16);
   }
 
   uint32_t cur = 0;
@@ -260,8 +260,8 @@ __global__ __launch_bounds__(1024) void k_gather_decompress(GatherArgs a) {
       const GroupHdr hn = hdrs[cur ^ 1u];
       const uint32_t n16 = has_next ? payload_units(a, hn) : 0u;
       const uint4* src = (const uint4*)hn.addr;
-      v0 = *(gl < n16 ? src + gl : &g_zero16);
-      v1 = *(gl + G < n16 ? src + gl + G : &g_zero16);
+      v0 = load_global(gl < n16 ? src + gl : &g_zero16);
+      v1 = load_global(gl + G < n16 ? src + gl + G : &g_zero16);
     }
     // 4. decode this tensor's words and store them.  With chunks of at least
     //    64 words, the 64 words a wave handles for one j lie in one chunk, so
@@ -493,7 +493,7 @@ __global__ __launch_bounds__(256) void k_gather_tile(GatherArgs a) {
   uint32_t* s_pref = (uint32_t*)(smem + L.pref);
   uint32_t* s_kc = (uint32_t*)(smem + L.kc);
   uint32_t* s_wsum = (uint32_t*)(smem + L.wsum);
-  const uint32_t wave = threadIdx.x / kWave;
+  const uint32_t wave = uniform(threadIdx.x / kWave);
   const uint32_t lane = threadIdx.x % kWave;
   uint8_t* wbase = smem + L.group0 + wave * (2 * T * (uint32_t)sizeof(TileHdr) + T * a.pbuf_bytes);
   TileHdr* hdrs = (TileHdr*)wbase;  // [2][T]
@@ -533,11 +533,12 @@ __global__ __launch_bounds__(256) void k_gather_tile(GatherArgs a) {
   // payload: lanes past it loaded g_zero16), so a slot never holds a stale
   // payload and an invalid tensor's slot is all zero
   const uint32_t slot16 = a.pbuf_bytes >> 4;
+  const uint64_t zero_addr = (uint64_t)&g_zero16;
 #define IBP_TILE_LOAD(k, hdr)                                                                  \
   if constexpr (k < NL) {                                                                      \
     const TileHdr& h_ = (hdr)[k * RPI + lrow];                                                 \
     n##k = h_.n16;                                                                             \
-    v##k = *(lunit < n##k ? (const uint4*)h_.addr + lunit : &g_zero16);                        \
+    v##k = load_global((const uint4*)(lunit < n##k ? h_.addr + 16u * lunit : zero_addr));     \
   }
 #define IBP_TILE_ISSUE_LOADS(hdr)                                                              \
   IBP_TILE_LOAD(0, hdr) IBP_TILE_LOAD(1, hdr) IBP_TILE_LOAD(2, hdr) IBP_TILE_LOAD(3, hdr)      \
@@ -551,8 +552,6 @@ __global__ __launch_bounds__(256) void k_gather_tile(GatherArgs a) {
   uint32_t cur = 0;
   for (uint64_t tile = tile0; tile < n_tiles; tile += waves, cur ^= 1u) {
     const bool has_next = tile + waves < n_tiles;
-    keep_stage_flags<J>(R);
-    keep_shape(a);
     TileHdr* hcur = hdrs + cur * T;
     TileHdr* hnext = hdrs + (cur ^ 1u) * T;
     // a. this tile's payloads -> LDS

@@ -103,6 +103,23 @@ __device__ __forceinline__ uint32_t window32(const uint32_t* pb32, uint32_t off)
   return __builtin_amdgcn_alignbit(d1, d0, off & 31u);
 }
 
+// Loads through a global-address-space pointer (device memory or mapped
+// host memory).  A pointer the compiler cannot place is read with a flat
+// instruction, which also counts against the LDS wait counter: every later
+// wait for an LDS read would then wait for these loads as well.
+// (The pointer goes through an integer: a direct cast of a generic pointer
+// still compiles to a flat load.)
+__device__ __forceinline__ uint64_t load_global(const uint64_t* p) {
+  typedef __attribute__((address_space(1))) const uint64_t global_u64;
+  return *(global_u64*)(uintptr_t)p;
+}
+__device__ __forceinline__ uint4 load_global(const uint4* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
+  const u32x4 v = *(global_u32x4*)(uintptr_t)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
 
 // Orders LDS accesses among the lanes of one wave.
