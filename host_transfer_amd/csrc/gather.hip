@@ -426,7 +426,10 @@ __device__ __forceinline__ void unpack_stages_n(uint32_t (&x)[N], const uint32_t
 }
 
 #ifndef IBP_TILE_GROUP
-#define IBP_TILE_GROUP 8
+#define IBP_TILE_GROUP 8  // tensors of a full tile decoded side by side
+#endif
+#ifndef IBP_BIG_NL
+#define IBP_BIG_NL 8      // load instructions per tile on large batches
 #endif
 
 // Decodes and stores one full tile (W == 64 J) held in LDS.  Word position
@@ -653,7 +656,8 @@ static hipError_t launch_small(const Geometry& g, const GatherArgs& a, hipStream
   const bool full = g.W == (uint32_t)kWave * J;
   const bool big = a.n_ids >= (uint64_t)8 * RPI * 8 * (uint64_t)di.cus;
   if (big)
-    return full ? launch_tile<J, 8 * RPI, RPI, true>(g, a, s) : launch_tile<J, 8 * RPI, RPI, false>(g, a, s);
+    return full ? launch_tile<J, IBP_BIG_NL * RPI, RPI, true>(g, a, s)
+                : launch_tile<J, IBP_BIG_NL * RPI, RPI, false>(g, a, s);
   return full ? launch_tile<J, 2 * RPI, RPI, true>(g, a, s) : launch_tile<J, 2 * RPI, RPI, false>(g, a, s);
 }
 
