@@ -11,14 +11,17 @@ Prints ONE JSON line.  `value` is decompressed GB/s (ids x tensor bytes per
 second of wall time over the timed steps, inputs already resident).  Extra
 objects: `roofline` (the gather kernel against the host-link peak),
 `cpu_baseline` (the CPU oracle on a bounded sample of the same batches),
-`hbm_path` (the same kernel reading a compressed cache in HBM), `hybrid_path`
+`pinned_path` (the other workloads from pinned host memory, and the K/V decode
+step), `hbm_path` (the same kernel reading a compressed cache in HBM), `hybrid_path`
 (cache hits from HBM and misses over PCIe in one launch, at a fixed HBM budget,
 compressed against uncompressed tensors), probes of the link, and the transfer
 speedup over an uncompressed GPU gather of the same rows ([JH] Table 1
 discussion: transfer speedup against plain transfers).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sparse_gnn]
+       [--pinned-workloads dense_gnn,dlrm_1k,dlrm_2k|none] [--kv-pairs-default 8]
        [--hbm-workloads dense_gnn,dlrm_1k|none] [--hbm-large-batch N]
+       [--mode default|ablation|sweep|kv-step]
        [--host-flags default|coherent|noncoherent] [--no-cpu-baseline] [--threshold T]
 """
 import argparse
@@ -87,6 +90,10 @@ def parse():
                         "for small random tensors; sweep: throughput against space saving and "
                         "chunk size; kv-step: the online OPT-13B K/V path")
     p.add_argument("--kv-pairs", type=int, default=80, help="(layer, K|V) pairs in --mode kv-step")
+    p.add_argument("--pinned-workloads", default="dense_gnn,dlrm_1k,dlrm_2k",
+                   help="other workloads measured from pinned host memory, or 'none'")
+    p.add_argument("--kv-pairs-default", type=int, default=8,
+                   help="(layer, K|V) pairs of the K/V decode step in the default run (0: skip)")
     return p.parse_args()
 
 
@@ -190,6 +197,27 @@ class Table:
             self.raw = None
         log(f"{w.key}: metadata {self.meta_ms:.2f} ms, compress {self.compress_ms:.2f} ms, "
             f"mean payload {self.len_host.mean() / B:.4f} of {B} B")
+
+    def to_hbm(self, torch, ibp):
+        """Compacts the pinned store into a cache in HBM; gathers then read the cache."""
+        w = self.w
+        N, S = w.n_tensors, w.slot_bytes
+        ev = Timer(torch)
+        self.offsets = torch.zeros(N + 1, dtype=torch.int64, device="cuda")
+        s = ev.start()
+        ibp.compact_offsets(self.lengths, N, self.offsets)
+        ev.stop(s)
+        total = int(self.offsets[-1].item())
+        self.cache = torch.empty(max(total, 16), dtype=torch.uint8, device="cuda")
+        s = ev.start()
+        ibp.compact(self.store, S, N, self.offsets, self.cache, total)
+        ev.stop(s)
+        self.compact_ms = sum(ev.ms())
+        if isinstance(self.store, ibp.HostBuffer):
+            self.store.free()
+        self.store = self.cache
+        self.store_bytes = total
+        self.where = "hbm"
 
     def gather(self, ibp, d_ids, n_ids, out):
         w = self.w
@@ -345,12 +373,14 @@ def measure_workload(torch, ibp, W, key, T, where, host_flags, steps, warmup, wi
     return res
 
 
-def measure_hbm(torch, ibp, W, key, flags, args, pr):
-    """The gather kernel on a compacted HBM cache: Table-D batch and a large
-    batch, with the uncompressed HBM gather of the same ids beside it."""
+def measure_hbm(torch, ibp, W, table, args, pr):
+    """The gather kernel on a compacted HBM cache (the table's pinned store
+    compacted into HBM): Table-D batch and a large batch, with the
+    uncompressed HBM gather of the same ids beside it."""
     import numpy as np
-    w = W.WORKLOADS[key]
-    table = Table(torch, ibp, W, w, w.threshold, "hbm", flags, keep_raw=True)
+    w = table.w
+    key = w.key
+    table.to_hbm(torch, ibp)
     B, S, N = w.tensor_bytes, w.slot_bytes, w.n_tensors
     raw_dev = torch.from_numpy(table.raw.array).cuda()   # uncompressed rows in HBM
     table.raw.free()
@@ -400,9 +430,44 @@ def measure_hbm(torch, ibp, W, key, flags, args, pr):
         })
         del out, d
     res["compact_ms"] = round(table.compact_ms, 3)
-    del raw_dev, table
+    del raw_dev
     torch.cuda.empty_cache()
     return res
+
+
+def measure_pinned(torch, ibp, W, key, flags, args, pr):
+    """A workload's Table-D batches from its pinned-host store, with the raw
+    GPU gather of the same rows from pinned memory beside it.  Returns the
+    result and the table (still pinned)."""
+    w = W.WORKLOADS[key]
+    m = measure_workload(torch, ibp, W, key, None, "pinned", flags, args.steps, args.warmup,
+                         with_raw=True)
+    import numpy as np
+    table = m["table"]
+    comp = statistics.mean(m["comp_bytes"])
+    # bytes of the distinct tensors of a batch: repeated ids are read from
+    # the GPU's caches, not over the link, so this is the link-side count
+    uniq = statistics.mean(float(table.len_host[np.unique(i)].sum())
+                           for i in m["ids_host"][args.warmup:])
+    link = max(pr["h2d_dma_GBps"], pr["h2d_zero_copy_read_GBps"])
+    km, rm = m["kernel_ms"], m["raw_kernel_ms"]
+    achieved = comp / (km * 1e-3) / 1e9
+    achieved_u = uniq / (km * 1e-3) / 1e9
+    res = {"workload": f"{key}: {w.n_tensors} x {w.tensor_bytes} B, {w.chunk_bytes} B chunks, "
+                       f"T={w.threshold}, {w.batch} {w.id_law} ids per launch",
+           "kernel_us": round(km * 1e3, 2),
+           "decompressed_GBps": round(w.batch * w.tensor_bytes / (km * 1e-3) / 1e9, 2),
+           "compressed_GBps_over_link": round(achieved, 2),
+           "frac_of_measured": round(achieved / link, 4),
+           "frac_of_zero_copy_read": round(achieved / pr["h2d_zero_copy_read_GBps"], 4),
+           "unique_ids": round(statistics.mean(len(np.unique(i)) for i in m["ids_host"][args.warmup:]), 1),
+           "unique_payload_GBps_over_link": round(achieved_u, 2),
+           "unique_frac_of_measured": round(achieved_u / link, 4),
+           "batch_payload_over_dense": round(comp / (w.batch * w.tensor_bytes), 5),
+           "raw_gather_us": round(rm * 1e3, 2),
+           "transfer_speedup_vs_raw_gpu_gather": round(rm / km, 3)}
+    log(f"{key} pinned: {res}")
+    return res, table
 
 
 def measure_hybrid(torch, ibp, table, batches, ids_host, args, budget_fraction):
@@ -630,7 +695,7 @@ def run_sweep(torch, ibp, args, pr):
                       "device": torch.cuda.get_device_name(0)}), flush=True)
 
 
-def run_kv_step(torch, ibp, W, args, pr):
+def run_kv_step(torch, ibp, W, args, pr, pairs=None):
     """The online K/V path on OPT-13B shapes ([JH] LLM paragraph): Mask and
     Bitval of each (layer, K|V) pair from its own prefill K/V (38,400 rows),
     compress-on-write of each decode token's 20 rows into the pinned store, and
@@ -638,7 +703,7 @@ def run_kv_step(torch, ibp, W, args, pr):
     pair, 80 launches, against an uncompressed GPU gather of the same rows."""
     import numpy as np
     w = W.WORKLOADS["kv_opt13b"]
-    P = max(1, min(W.KV_PAIRS, args.kv_pairs))
+    P = max(1, min(W.KV_PAIRS, args.kv_pairs if pairs is None else pairs))
     R = W.KV_ROWS_PER_PAIR
     N, B, C, S = P * R, w.tensor_bytes, w.chunk_bytes, w.slot_bytes
     n_c = ibp.num_chunks(B, C)
@@ -695,7 +760,9 @@ def run_kv_step(torch, ibp, W, args, pr):
     dense = P * R * B
     comp = float(L.astype(np.float64).sum())
     link = max(pr["h2d_dma_GBps"], pr["h2d_zero_copy_read_GBps"])
-    res = {"metric": "OPT-13B K/V decode-step fetch (gather + decompress, 80 launches)",
+    res = {"metric": f"OPT-13B K/V decode-step fetch (gather + decompress, {P} launches)",
+           "workload": f"kv_opt13b: {P} (layer, K|V) pairs x {R} rows x {B} B, {C} B chunks, "
+                       f"T={w.threshold}, Mask per pair from its {W.KV_PREFILL_ROWS} prefill rows",
            "unit": "GB/s", "higher_is_better": True, "pairs": P,
            "rows_per_launch": R, "tensor_bytes": B, "chunk_bytes": C,
            "mean_payload_over_tensor": round(comp / (N * B), 5),
@@ -710,7 +777,7 @@ def run_kv_step(torch, ibp, W, args, pr):
            "device": torch.cuda.get_device_name(0)}
     raw.free()
     store.free()
-    print(json.dumps(res), flush=True)
+    return res
 
 
 def main():
@@ -736,7 +803,8 @@ def main():
     if args.mode == "sweep":
         return run_sweep(torch, ibp, args, pr)
     if args.mode == "kv-step":
-        return run_kv_step(torch, ibp, W, args, pr)
+        print(json.dumps(run_kv_step(torch, ibp, W, args, pr)), flush=True)
+        return
 
     # --- headline: the workload from pinned host memory
     key = args.workload
@@ -748,6 +816,8 @@ def main():
     value = dense_bytes * K / m["wall"] / 1e9
     kern_ms = m["kernel_ms"]
     comp = statistics.mean(m["comp_bytes"])
+    uniq = statistics.mean(float(table.len_host[np.unique(i)].sum())
+                           for i in m["ids_host"][args.warmup:])
     achieved = comp / (kern_ms * 1e-3) / 1e9
     raw_ms = m["raw_kernel_ms"]
     link_peak = max(pr["h2d_dma_GBps"], pr["h2d_zero_copy_read_GBps"])
@@ -793,6 +863,8 @@ def main():
                                    "min": round(min(m["isolated_ms"]) * 1e3, 2),
                                    "max": round(max(m["isolated_ms"]) * 1e3, 2)},
             "bytes_per_launch": round(comp, 1),
+            "unique_bytes_per_launch": round(uniq, 1),
+            "unique_frac_of_measured": round(uniq / (kern_ms * 1e-3) / 1e9 / link_peak, 4),
         },
         "compression": {
             "mean_payload_over_tensor": round(float(table.len_host.mean()) / w.tensor_bytes, 5),
@@ -806,6 +878,22 @@ def main():
         "host": host_info(),
         "device": torch.cuda.get_device_name(0),
     }
+    # one launch over 16 batches: the per-launch fixed cost spread over 16x the bytes
+    n16 = max(1, min(2, len(m["ids_host"]) // 16))
+    big_ids = [np.concatenate(m["ids_host"][16 * k:16 * k + 16]) for k in range(n16)]
+    nb16 = min(len(i) for i in big_ids)
+    d16 = [torch.from_numpy(i).cuda() for i in big_ids]
+    out16 = torch.empty(nb16 * w.tensor_bytes, dtype=torch.uint8, device="cuda")
+    ms16, _ = region_launches(torch, lambda k: table.gather(ibp, d16[k % len(d16)], nb16, out16),
+                              2, 6)
+    comp16 = statistics.mean(float(table.len_host[i].sum()) for i in big_ids)
+    result["roofline"]["one_launch_16_batches"] = {
+        "ids": nb16, "kernel_us": round(ms16 * 1e3, 2),
+        "achieved": round(comp16 / (ms16 * 1e-3) / 1e9, 3),
+        "frac_of_measured": round(comp16 / (ms16 * 1e-3) / 1e9 / link_peak, 4),
+        "frac_of_zero_copy_read": round(comp16 / (ms16 * 1e-3) / 1e9 /
+                                        pr["h2d_zero_copy_read_GBps"], 4)}
+    del out16, d16
     log("cache + store at a 10 % HBM budget ...")
     batches_dev = [torch.from_numpy(i).cuda() for i in m["ids_host"]]
     result["hybrid_path"] = measure_hybrid(torch, ibp, table, batches_dev, m["ids_host"], args,
@@ -820,12 +908,28 @@ def main():
     del table, m
     torch.cuda.empty_cache()
 
-    # --- the same kernel on compressed caches in HBM: the Table-D batch and a
+    # --- the other pinned-host configurations (their Table-D batches), then
+    #     the same tables compacted into HBM caches: the Table-D batch and a
     #     large batch (1M ids) that fills the GPU
+    result["pinned_path"] = []
     result["hbm_path"] = []
-    if args.hbm_workloads != "none":
-        for hk in args.hbm_workloads.split(","):
-            result["hbm_path"].append(measure_hbm(torch, ibp, W, hk, flags, args, pr))
+    hbm = [] if args.hbm_workloads == "none" else args.hbm_workloads.split(",")
+    pinned = [] if args.pinned_workloads == "none" else args.pinned_workloads.split(",")
+    for key in pinned + [k for k in hbm if k not in pinned]:
+        res, tb = measure_pinned(torch, ibp, W, key, flags, args, pr)
+        if key in pinned:
+            result["pinned_path"].append(res)
+        if key in hbm:
+            result["hbm_path"].append(measure_hbm(torch, ibp, W, tb, args, pr))
+        if tb.raw is not None:
+            tb.raw.free()
+        if isinstance(tb.store, ibp.HostBuffer):
+            tb.store.free()
+        del tb
+        torch.cuda.empty_cache()
+    if args.kv_pairs_default > 0:
+        result["pinned_path"].append(run_kv_step(torch, ibp, W, args, pr,
+                                                 pairs=args.kv_pairs_default))
     print(json.dumps(result), flush=True)
 
 
