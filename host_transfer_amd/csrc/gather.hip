@@ -213,15 +213,18 @@ __global__ __launch_bounds__(1024) void k_gather_decompress(GatherArgs a) {
   // scan one ahead.
   // (every wave loads the few metadata bytes, so no load sits behind a
   // branch; only the first wave uses them)
-  // the first two tensors' metadata round trips overlap the plan
+  // the first two tensors' metadata round trips overlap the chunk counts;
+  // the first payload is requested before the per-word registers are built,
+  // so its fetch overlaps that arithmetic
   const int64_t id_a = load_id(a, row0);
   const int64_t id_b = load_id(a, row0 + step);
   const RowMeta m0 = load_meta(a, id_a, gl);
   RowMeta meta_next = load_meta(a, id_b, gl);      // tensor row+step
   int64_t id_next2 = load_id(a, row0 + 2 * step);  // tensor row+2*step
-
   WordRegs<J> R;
-  load_plan<J>(a.mask, a.bitval, a.sh, s_pref, s_kc, s_wsum, gl, R);
+  load_plan_fetch<J>(a.mask, a.bitval, a.sh, gl, R);
+
+  load_plan_counts(a.mask, a.sh, s_pref, s_kc, s_wsum);
 
   if (row0 >= a.n_ids) return;  // uniform per group; no workgroup barrier follows for it
   if (first_wave) scan_row(a, m0, gl, s_kc, &hdrs[0], obufs);
@@ -237,6 +240,8 @@ __global__ __launch_bounds__(1024) void k_gather_decompress(GatherArgs a) {
     v0 = load_global(gl < n16 ? src + gl : &g_zero16);
     v1 = load_global(gl + G < n16 ? src + gl + G : &g_zero16);
   }
+
+  load_plan_words<J>(a.sh, s_pref, gl, R);
 
   uint32_t cur = 0;
   for (uint64_t row = row0; row < a.n_ids; row += step, cur ^= 1u) {
@@ -511,18 +516,19 @@ __global__ __launch_bounds__(256) void k_gather_tile(GatherArgs a) {
 
   // Tile metadata runs ahead of the payloads: ids three tiles ahead, bitmap
   // words and offsets two ahead, the headers one ahead.
+  // (the first tile's metadata round trips overlap the chunk counts; its
+  // payloads are requested before the per-word registers are built)
   const int64_t id_a = tile_row_id(a, tile0 * T + mrow);
   const int64_t id_b = tile_row_id(a, (tile0 + waves) * T + mrow);
-
+  const TileMeta m0 = load_tile_meta(a, id_a);
   WordRegs<J> R;
-  load_plan<J>(a.mask, a.bitval, a.sh, s_pref, s_kc, s_wsum, lane, R);
+  load_plan_fetch<J>(a.mask, a.bitval, a.sh, lane, R);
+
+  load_plan_counts(a.mask, a.sh, s_pref, s_kc, s_wsum);
   if (tile0 >= n_tiles) return;  // per wave; no workgroup barrier follows
 
   TileMeta meta_next = load_tile_meta(a, id_b);
-  {
-    const TileMeta m0 = load_tile_meta(a, id_a);
-    if (lane < (uint32_t)T) hdrs[lane] = make_tile_hdr(a, m0, s_kc);
-  }
+  if (lane < (uint32_t)T) hdrs[lane] = make_tile_hdr(a, m0, s_kc);
   int64_t id_next2 = tile_row_id(a, (tile0 + 2 * waves) * T + mrow);
   wave_sync();
 
@@ -551,6 +557,8 @@ __global__ __launch_bounds__(256) void k_gather_tile(GatherArgs a) {
     if (lunit < slot16) ((uint4*)(pbufs + (k * RPI + lrow) * a.pbuf_bytes))[lunit] = v##k;     \
   }
   IBP_TILE_ISSUE_LOADS(hdrs)
+
+  load_plan_words<J>(a.sh, s_pref, lane, R);
 
   uint32_t cur = 0;
   for (uint64_t tile = tile0; tile < n_tiles; tile += waves, cur ^= 1u) {

@@ -58,15 +58,22 @@ __device__ __forceinline__ uint32_t block_inclusive_sum(uint32_t v, uint32_t* s_
   return incl + off;
 }
 
-// Builds the registers of thread gl and the K_c table.  Every thread of the
-// workgroup must call it.  s_pref: W+1 words of LDS (scratch), s_kc: 64 words.
-// The exclusive prefix of kept bits over all words takes one workgroup scan:
-// each thread sums a contiguous run of words, the runs are scanned, then each
-// thread writes the prefixes of its run.
-template <int J>
-__device__ void load_plan(const uint32_t* __restrict__ mask, const uint32_t* __restrict__ bitval,
-                          const Shape& sh, uint32_t* s_pref, uint32_t* s_kc, uint32_t* s_wsum,
-                          uint32_t gl, WordRegs<J>& R) {
+// The plan is built in two parts, so that a kernel can issue its first
+// payload loads between them:
+//   load_plan_counts  the kept-bit prefix of every word (s_pref) and the kept
+//                     bits K_c of every chunk (s_kc), which the chunk scan
+//                     needs; a workgroup scan, so every thread must call it;
+//   load_plan_fetch   the Mask/Bitval words thread gl decodes, into registers;
+//   load_plan_words   the per-word registers of thread gl from them (move
+//                     masks, bit offsets in the chunk stream, wave-uniform
+//                     stage flags): arithmetic and LDS reads only, no
+//                     workgroup barrier.
+// s_pref: W+1 words of LDS, s_kc: 64 words.  The exclusive prefix of kept
+// bits over all words takes one workgroup scan: each thread sums a
+// contiguous run of words, the runs are scanned, then each thread writes the
+// prefixes of its run.
+__device__ void load_plan_counts(const uint32_t* __restrict__ mask, const Shape& sh,
+                                 uint32_t* s_pref, uint32_t* s_kc, uint32_t* s_wsum) {
   const uint32_t nt = blockDim.x, tid = threadIdx.x;
   const uint32_t per = (sh.W + nt - 1) / nt;
   const uint32_t w0 = min(tid * per, sh.W), w1 = min(w0 + per, sh.W);
@@ -85,14 +92,35 @@ __device__ void load_plan(const uint32_t* __restrict__ mask, const uint32_t* __r
     const uint32_t hi = min((c + 1) << sh.wpc_log2, sh.W);
     s_kc[c] = s_pref[hi] - s_pref[lo];
   }
+  __syncthreads();
+}
+
+// Mask and Bitval words of thread gl into R.mask / R.bitval (clamped,
+// unconditional loads; words past W become 0 in load_plan_words).  Issued
+// before the first payload loads, so that waiting for them never waits for a
+// payload.
+template <int J>
+__device__ __forceinline__ void load_plan_fetch(const uint32_t* __restrict__ mask,
+                                                const uint32_t* __restrict__ bitval,
+                                                const Shape& sh, uint32_t gl, WordRegs<J>& R) {
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const uint32_t w = min(gl + sh.group * j, sh.W - 1u);
+    R.mask[j] = mask[w];
+    R.bitval[j] = bitval[w];
+  }
+}
+
+template <int J>
+__device__ void load_plan_words(const Shape& sh, const uint32_t* s_pref, uint32_t gl,
+                                WordRegs<J>& R) {
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const uint32_t w = gl + sh.group * j;
     if (w < sh.W) {
-      const uint32_t m = mask[w];
+      const uint32_t m = R.mask[j];
       move_masks(~m, R.mv[j]);
-      R.mask[j] = m;
-      R.bitval[j] = bitval[w] & m;
+      R.bitval[j] &= m;
       const uint32_t first = (w >> sh.wpc_log2) << sh.wpc_log2;
       R.info[j] = (s_pref[w] - s_pref[first]) | ((32u * (w - first)) << 16);
     } else {
@@ -107,7 +135,6 @@ __device__ void load_plan(const uint32_t* __restrict__ mask, const uint32_t* __r
     for (int s = 0; s < 5; ++s) st |= (__ballot(R.mv[j][s] != 0u) != 0ull ? 1u : 0u) << s;
     R.stages[j] = uniform(st);
   }
-  __syncthreads();
 }
 
 // Synchronises the threads of one group: a wave, or the whole workgroup.
