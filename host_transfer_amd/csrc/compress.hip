@@ -77,8 +77,10 @@ __global__ __launch_bounds__(1024) void k_compress(CompressArgs a) {
   if (gl < kWave) s_fail[gl] = 0;
 
   WordRegs<J> R;
+  PlanRun run;
+  load_plan_run(a.mask, a.sh, run);
   load_plan_fetch<J>(a.mask, a.bitval, a.sh, gl, R);
-  load_plan_counts(a.mask, a.sh, s_pref, s_kc, s_wsum);
+  load_plan_counts(run, a.sh, s_pref, s_kc, s_wsum);
   load_plan_words<J>(a.sh, s_pref, gl, R);
 
   const bool single = G == kWave;

@@ -218,13 +218,15 @@ __global__ __launch_bounds__(1024) void k_gather_decompress(GatherArgs a) {
   // so its fetch overlaps that arithmetic
   const int64_t id_a = load_id(a, row0);
   const int64_t id_b = load_id(a, row0 + step);
-  const RowMeta m0 = load_meta(a, id_a, gl);
-  RowMeta meta_next = load_meta(a, id_b, gl);      // tensor row+step
   int64_t id_next2 = load_id(a, row0 + 2 * step);  // tensor row+2*step
+  PlanRun run;
+  load_plan_run(a.mask, a.sh, run);
   WordRegs<J> R;
   load_plan_fetch<J>(a.mask, a.bitval, a.sh, gl, R);
+  const RowMeta m0 = load_meta(a, id_a, gl);
+  RowMeta meta_next = load_meta(a, id_b, gl);      // tensor row+step
 
-  load_plan_counts(a.mask, a.sh, s_pref, s_kc, s_wsum);
+  load_plan_counts(run, a.sh, s_pref, s_kc, s_wsum);
 
   if (row0 >= a.n_ids) return;  // uniform per group; no workgroup barrier follows for it
   if (first_wave) scan_row(a, m0, gl, s_kc, &hdrs[0], obufs);
@@ -520,11 +522,13 @@ __global__ __launch_bounds__(256) void k_gather_tile(GatherArgs a) {
   // payloads are requested before the per-word registers are built)
   const int64_t id_a = tile_row_id(a, tile0 * T + mrow);
   const int64_t id_b = tile_row_id(a, (tile0 + waves) * T + mrow);
-  const TileMeta m0 = load_tile_meta(a, id_a);
+  PlanRun run;
+  load_plan_run(a.mask, a.sh, run);
   WordRegs<J> R;
   load_plan_fetch<J>(a.mask, a.bitval, a.sh, lane, R);
+  const TileMeta m0 = load_tile_meta(a, id_a);
 
-  load_plan_counts(a.mask, a.sh, s_pref, s_kc, s_wsum);
+  load_plan_counts(run, a.sh, s_pref, s_kc, s_wsum);
   if (tile0 >= n_tiles) return;  // per wave; no workgroup barrier follows
 
   TileMeta meta_next = load_tile_meta(a, id_b);

@@ -60,8 +60,8 @@ __device__ __forceinline__ uint32_t block_inclusive_sum(uint32_t v, uint32_t* s_
 
 // The plan is built in two parts, so that a kernel can issue its first
 // payload loads between them:
-//   load_plan_counts  the kept-bit prefix of every word (s_pref) and the kept
-//                     bits K_c of every chunk (s_kc), which the chunk scan
+//   load_plan_run +   the kept-bit prefix of every word (s_pref) and the kept
+//   load_plan_counts  bits K_c of every chunk (s_kc), which the chunk scan
 //                     needs; a workgroup scan, so every thread must call it;
 //   load_plan_fetch   the Mask/Bitval words thread gl decodes, into registers;
 //   load_plan_words   the per-word registers of thread gl from them (move
@@ -72,18 +72,44 @@ __device__ __forceinline__ uint32_t block_inclusive_sum(uint32_t v, uint32_t* s_
 // bits over all words takes one workgroup scan: each thread sums a
 // contiguous run of words, the runs are scanned, then each thread writes the
 // prefixes of its run.
-__device__ void load_plan_counts(const uint32_t* __restrict__ mask, const Shape& sh,
-                                 uint32_t* s_pref, uint32_t* s_kc, uint32_t* s_wsum) {
+// Words per thread in the kept-bit scan: every launch has W <= 6 * threads
+// (groups of G threads with G * 6 >= W; tile kernels: W <= 256 words, 256
+// threads).
+constexpr int kMaxRun = 6;
+
+// The Mask words of this thread's contiguous run, loaded ahead of the
+// counts (clamped, unconditional loads) so they can be requested before
+// anything else is waited for.
+struct PlanRun {
+  uint32_t m[kMaxRun];
+};
+
+__device__ __forceinline__ void load_plan_run(const uint32_t* __restrict__ mask, const Shape& sh,
+                                              PlanRun& r) {
+  const uint32_t nt = blockDim.x, tid = threadIdx.x;
+  const uint32_t per = (sh.W + nt - 1) / nt;
+  const uint32_t w0 = min(tid * per, sh.W - 1u);
+#pragma unroll
+  for (int k = 0; k < kMaxRun; ++k) r.m[k] = mask[min(w0 + (uint32_t)k, sh.W - 1u)];
+}
+
+__device__ void load_plan_counts(const PlanRun& r, const Shape& sh, uint32_t* s_pref,
+                                 uint32_t* s_kc, uint32_t* s_wsum) {
   const uint32_t nt = blockDim.x, tid = threadIdx.x;
   const uint32_t per = (sh.W + nt - 1) / nt;
   const uint32_t w0 = min(tid * per, sh.W), w1 = min(w0 + per, sh.W);
   uint32_t local = 0;
-  for (uint32_t w = w0; w < w1; ++w) local += (uint32_t)__popc(~mask[w]);
+#pragma unroll
+  for (int k = 0; k < kMaxRun; ++k)
+    if (w0 + (uint32_t)k < w1) local += (uint32_t)__popc(~r.m[k]);
   uint32_t total;
   uint32_t run = block_inclusive_sum(local, s_wsum, &total) - local;
-  for (uint32_t w = w0; w < w1; ++w) {
-    s_pref[w] = run;
-    run += (uint32_t)__popc(~mask[w]);
+#pragma unroll
+  for (int k = 0; k < kMaxRun; ++k) {
+    if (w0 + (uint32_t)k < w1) {
+      s_pref[w0 + k] = run;
+      run += (uint32_t)__popc(~r.m[k]);
+    }
   }
   if (tid == 0) s_pref[sh.W] = total;
   __syncthreads();
