@@ -77,6 +77,14 @@ __device__ __align__(16) uint4 g_zero16 = {0u, 0u, 0u, 0u};
 
 constexpr uint64_t kNotCached = ~0ull;
 
+// Output rows are written once and not read again by the kernel: streaming
+// (non-temporal) stores keep them from displacing the payloads, offsets and
+// bitmap words that repeated ids read again.
+__device__ __forceinline__ void store_out(uint32_t* p, uint32_t v) {
+  __builtin_nontemporal_store(v, p);
+}
+
+
 // Address of tensor t's payload and the bytes readable from there (0 when it
 // has no source).  One unconditional load of the offset table entry.
 struct Source {
@@ -298,7 +306,7 @@ __global__ __launch_bounds__(1024) void k_gather_decompress(GatherArgs a) {
         } else {
           v = window32(pb32, o + (R.info[j] >> 16));
         }
-        if (w < W) orow[w] = v;
+        if (w < W) store_out(orow + w, v);
       }
     }
     group_sync(single);
@@ -486,7 +494,7 @@ __device__ __forceinline__ void decode_full_tile(const GatherArgs& a, const Word
             x[q] = bfi_op(R.mask[j], R.bitval[j], unpack_stages(x[q], R.mv[j], R.stages[j]));
       }
 #pragma unroll
-      for (int q = 0; q < TG; ++q) obase[(uint64_t)(i0 + q) * kW + (uint32_t)kWave * j] = x[q];
+      for (int q = 0; q < TG; ++q) store_out(obase + (uint64_t)(i0 + q) * kW + (uint32_t)kWave * j, x[q]);
     }
   }
 }

@@ -30,12 +30,16 @@ __global__ __launch_bounds__(256) void k_raw_gather(const uint8_t* __restrict__ 
     const bool valid = id >= 0 && (uint64_t)id < n_rows;
     const uint8_t* s = src + (valid ? (uint64_t)id * row_stride : 0);
     uint8_t* d = out + r * row_bytes;
+    // streaming stores, as the gather kernels write their rows
     if (wide) {
-      for (uint32_t q = q0; q < row_bytes / 16; q += lanes)
-        ((uint4*)d)[q] = valid ? ((const uint4*)s)[q] : make_uint4(0, 0, 0, 0);
+      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+      for (uint32_t q = q0; q < row_bytes / 16; q += lanes) {
+        const u32x4 v = valid ? ((const u32x4*)s)[q] : u32x4{0u, 0u, 0u, 0u};
+        __builtin_nontemporal_store(v, (u32x4*)d + q);
+      }
     } else {
       for (uint32_t q = q0; q < row_bytes / 4; q += lanes)
-        ((uint32_t*)d)[q] = valid ? ((const uint32_t*)s)[q] : 0u;
+        __builtin_nontemporal_store(valid ? ((const uint32_t*)s)[q] : 0u, (uint32_t*)d + q);
     }
   }
 }
