@@ -455,10 +455,11 @@ __device__ __forceinline__ void unpack_stages_n(uint32_t (&x)[N], const uint32_t
 // LDS reads overlap and the stage tests are made once for all of them.
 // Invalid tensors have no participating chunk and an all-zero slot, so they
 // decode to zero words without a select.
-template <int J, int T>
+// ROUTED: tensor i's output row is held by lane i (trow); else it is row0 + i.
+template <int J, int T, bool ROUTED = false>
 __device__ __forceinline__ void decode_full_tile(const GatherArgs& a, const WordRegs<J>& R,
                                                  const uint8_t* pbufs, const TileHdr* hcur,
-                                                 uint32_t lane, uint64_t row0) {
+                                                 uint32_t lane, uint64_t row0, uint32_t trow = 0) {
   constexpr uint32_t kW = (uint32_t)kWave * J;  // words per tensor
   constexpr uint32_t kSlot = 4u * kW + 16u;     // LDS bytes per tensor
   constexpr int TG = T < IBP_TILE_GROUP ? T : IBP_TILE_GROUP;  // tensors decoded side by side
@@ -494,7 +495,11 @@ __device__ __forceinline__ void decode_full_tile(const GatherArgs& a, const Word
             x[q] = bfi_op(R.mask[j], R.bitval[j], unpack_stages(x[q], R.mv[j], R.stages[j]));
       }
 #pragma unroll
-      for (int q = 0; q < TG; ++q) store_out(obase + (uint64_t)(i0 + q) * kW + (uint32_t)kWave * j, x[q]);
+      for (int q = 0; q < TG; ++q) {
+        uint32_t* dst = ROUTED ? a.out + (uint64_t)__builtin_amdgcn_readlane(trow, i0 + q) * kW + lane
+                               : obase + (uint64_t)(i0 + q) * kW;
+        store_out(dst + (uint32_t)kWave * j, x[q]);
+      }
     }
   }
 }
@@ -663,6 +668,176 @@ static hipError_t launch_tile(const Geometry& g, GatherArgs a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Tile kernel with XCD-aware routing, for payloads read from their slots.
+//
+// The eight XCDs have an L2 each, and workgroups are dispatched to them round
+// robin (block b on XCD b % 8).  When a batch repeats ids (Zipf), a tensor
+// read by waves on several XCDs crosses the host link (or HBM) once per XCD.
+// Here every id is routed to one XCD, chosen by a hash of the tensor index:
+// the waves of XCD x split the batch into equal segments, and each wave keeps
+// the rows of its segment whose tensor hashes to x, in a small LDS list, and
+// decodes them T at a time.  Every row is processed exactly once: by the wave
+// whose segment holds it, on the XCD its tensor hashes to.  A last, partial
+// tile is padded with copies of its last row (written twice, with the same
+// bytes).  Tiles are processed one after another (no prefetch across tiles):
+// the launches this serves are short and have about one tile per wave.
+
+constexpr uint32_t kXcds = 8;
+
+__device__ __forceinline__ uint32_t xcd_of_tensor(int64_t id) {
+  return (uint32_t)(((uint64_t)id * 0x9E3779B97F4A7C15ull) >> 61);  // Fibonacci hashing, top 3 bits
+}
+
+// LDS bytes of one wave: T headers, T payload slots, the row list.
+__host__ __device__ constexpr uint32_t routed_list_cap(uint32_t T) { return T + (uint32_t)kWave; }
+__host__ __device__ inline uint32_t routed_wave_bytes(uint32_t T, uint32_t pbuf_bytes) {
+  return T * (uint32_t)sizeof(TileHdr) + T * pbuf_bytes + ((routed_list_cap(T) * 12u + 15u) & ~15u);
+}
+
+template <int J, int T, int RPI, bool FULL>
+__global__ __launch_bounds__(256) void k_gather_tile_routed(GatherArgs a) {
+  constexpr uint32_t LPR = kWave / RPI;
+  constexpr int NL = T / RPI;
+  static_assert(NL <= 8, "at most 8 load instructions per tile");
+  constexpr uint32_t kCap = routed_list_cap(T);
+  extern __shared__ __align__(16) uint8_t smem[];
+  const GatherLds L(a.sh.W, a.pbuf_bytes);
+  uint32_t* s_pref = (uint32_t*)(smem + L.pref);
+  uint32_t* s_kc = (uint32_t*)(smem + L.kc);
+  uint32_t* s_wsum = (uint32_t*)(smem + L.wsum);
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  const uint32_t lane = threadIdx.x % kWave;
+  const uint32_t wpb = blockDim.x / kWave;
+  uint8_t* wbase = smem + L.group0 + wave * routed_wave_bytes(T, a.pbuf_bytes);
+  TileHdr* hdrs = (TileHdr*)wbase;                                    // [T]
+  uint8_t* pbufs = wbase + T * sizeof(TileHdr);                       // [T][pbuf_bytes]
+  int64_t* list_id = (int64_t*)(pbufs + T * a.pbuf_bytes);           // [kCap]
+  uint32_t* list_row = (uint32_t*)(list_id + kCap);                   // [kCap]
+
+  // this wave's XCD and segment of the batch (the grid is a multiple of 8)
+  const uint32_t xcd = blockIdx.x % kXcds;
+  const uint64_t wc = (uint64_t)(gridDim.x / kXcds) * wpb;
+  const uint64_t wk = (uint64_t)(blockIdx.x / kXcds) * wpb + wave;
+  const uint64_t seg = (a.n_ids + wc - 1) / wc;
+  const uint64_t s0 = min(wk * seg, a.n_ids), s1 = min(s0 + seg, a.n_ids);
+
+  PlanRun run;
+  load_plan_run(a.mask, a.sh, run);
+  WordRegs<J> R;
+  load_plan_fetch<J>(a.mask, a.bitval, a.sh, lane, R);
+  load_plan_counts(run, a.sh, s_pref, s_kc, s_wsum);  // workgroup barriers: every thread
+  load_plan_words<J>(a.sh, s_pref, lane, R);
+  if (s0 >= s1) return;  // per wave; no workgroup barrier follows
+
+  const uint32_t lrow = lane / LPR, lunit = lane % LPR;
+  const uint32_t slot16 = a.pbuf_bytes >> 4;
+  const uint64_t zero_addr = (uint64_t)&g_zero16;
+  const uint32_t W = a.sh.W;
+  uint32_t count = 0;  // rows in the list (wave-uniform)
+  for (uint64_t base = s0; base < s1; base += kWave) {
+    // 1. this window's rows that belong to this XCD -> the list
+    {
+      const uint64_t r = base + lane;
+      const bool in = r < s1;
+      const int64_t id = a.ids[in ? r : s1 - 1];
+      const bool mine = in && xcd_of_tensor(id) == xcd;
+      const uint64_t bal = __ballot(mine);
+      const uint32_t before = (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+      if (mine) {
+        list_id[count + before] = id;
+        list_row[count + before] = (uint32_t)r;
+      }
+      count += (uint32_t)__popcll(bal);
+      wave_sync();
+    }
+    const bool last = base + kWave >= s1;
+    // 2. full tiles (and, after the last window, the rest)
+    while (count >= (uint32_t)T || (last && count > 0u)) {
+      const uint32_t n = count < (uint32_t)T ? count : (uint32_t)T;
+      const uint32_t e = min(lane % (uint32_t)T, n - 1u);
+      const uint32_t trow = list_row[e];
+      const TileMeta m = load_tile_meta(a, list_id[e]);
+      if (lane < (uint32_t)T) hdrs[lane] = make_tile_hdr(a, m, s_kc);
+      wave_sync();
+      uint4 v0, v1, v2, v3, v4, v5, v6, v7;
+#define IBP_RT_LOAD(k)                                                                          \
+      if constexpr (k < NL) {                                                                   \
+        const TileHdr& h_ = hdrs[k * RPI + lrow];                                               \
+        v##k = load_global((const uint4*)(lunit < h_.n16 ? h_.addr + 16u * lunit : zero_addr)); \
+      }
+#define IBP_RT_STAGE(k)                                                                         \
+      if constexpr (k < NL) {                                                                   \
+        if (lunit < slot16) ((uint4*)(pbufs + (k * RPI + lrow) * a.pbuf_bytes))[lunit] = v##k;  \
+      }
+      IBP_RT_LOAD(0) IBP_RT_LOAD(1) IBP_RT_LOAD(2) IBP_RT_LOAD(3)
+      IBP_RT_LOAD(4) IBP_RT_LOAD(5) IBP_RT_LOAD(6) IBP_RT_LOAD(7)
+      IBP_RT_STAGE(0) IBP_RT_STAGE(1) IBP_RT_STAGE(2) IBP_RT_STAGE(3)
+      IBP_RT_STAGE(4) IBP_RT_STAGE(5) IBP_RT_STAGE(6) IBP_RT_STAGE(7)
+#undef IBP_RT_LOAD
+#undef IBP_RT_STAGE
+      wave_sync();
+      if constexpr (FULL) {
+        decode_full_tile<J, T, true>(a, R, pbufs, hdrs, lane, 0, trow);
+      } else {
+        for (uint32_t i = 0; i < n; ++i) {
+          const TileHdr* hp = hdrs + i;
+          const bool valid = uniform(hp->valid) != 0u;
+          const uint32_t pm = uniform(hp->pmask);
+          const uint32_t o1 = uniform(hp->off[0]), o2 = uniform(hp->off[1]), o3 = uniform(hp->off[2]);
+          const uint32_t* pb32 = (const uint32_t*)(pbufs + i * a.pbuf_bytes);
+          uint32_t* orow = a.out + (uint64_t)__builtin_amdgcn_readlane(trow, i) * W;
+#pragma unroll
+          for (int j = 0; j < J; ++j) {
+            const uint32_t w = lane + kWave * j;
+            const uint32_t val = tile_word<J>(a, R, j, pb32, pm, o1, o2, o3);
+            if (w < W) store_out(orow + w, valid ? val : 0u);
+          }
+        }
+      }
+      // 3. drop the tile's rows from the list
+      const uint32_t rest = count - n;
+      int64_t keep_id = 0;
+      uint32_t keep_row = 0;
+      if (lane < rest) {
+        keep_id = list_id[n + lane];
+        keep_row = list_row[n + lane];
+      }
+      wave_sync();
+      if (lane < rest) {
+        list_id[lane] = keep_id;
+        list_row[lane] = keep_row;
+      }
+      count = rest;
+      wave_sync();
+    }
+  }
+}
+
+template <int J, int T, int RPI, bool FULL>
+static hipError_t launch_tile_routed(const Geometry& g, GatherArgs a, hipStream_t s) {
+  a.sh.group = kWave;
+  const uint32_t waves = 4;
+  const GatherLds L(g.W, a.pbuf_bytes);
+  const uint32_t lds = L.group0 + waves * routed_wave_bytes(T, a.pbuf_bytes);
+  DeviceInfo di;
+  hipError_t e = device_info(&di);
+  if (e != hipSuccess) return e;
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gather_tile_routed<J, T, RPI, FULL>,
+                                                   waves * 64, lds);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) return hipErrorInvalidConfiguration;
+  const uint64_t tiles = (a.n_ids + T - 1) / T;
+  const uint64_t want = (tiles + waves - 1) / waves;
+  const uint64_t cap = (uint64_t)per_cu * (uint64_t)di.cus;
+  uint64_t blocks = want < cap ? want : cap;
+  blocks = blocks < kXcds ? kXcds : blocks / kXcds * kXcds;  // every XCD class has the same blocks
+  hipLaunchKernelGGL((k_gather_tile_routed<J, T, RPI, FULL>), dim3((uint32_t)blocks),
+                     dim3(waves * 64), lds, s, a);
+  return hipGetLastError();
+}
+
 // Small tensors (W <= 256): rows per load instruction RPI from the payload's
 // 16 B units (J fixes them: J = 1 -> <= 16 units, 2 -> <= 32, 3 and 4 ->
 // <= 64), and NL load instructions per tile: 8 when the batch gives every CU
@@ -675,6 +850,10 @@ static hipError_t launch_small(const Geometry& g, const GatherArgs& a, hipStream
   if (e != hipSuccess) return e;
   const bool full = g.W == (uint32_t)kWave * J;
   const bool big = a.n_ids >= (uint64_t)8 * RPI * 8 * (uint64_t)di.cus;
+  // payloads from their slots (no offset table): route repeated ids to one XCD
+  if (a.offsets == nullptr && a.n_ids < (1ull << 32) && !big)
+    return full ? launch_tile_routed<J, 2 * RPI, RPI, true>(g, a, s)
+                : launch_tile_routed<J, 2 * RPI, RPI, false>(g, a, s);
   if (big)
     return full ? launch_tile<J, IBP_BIG_NL * RPI, RPI, true>(g, a, s)
                 : launch_tile<J, IBP_BIG_NL * RPI, RPI, false>(g, a, s);
