@@ -245,7 +245,7 @@ def region_launches(torch, fn, warmup, steps):
     return a.elapsed_time(b) / steps, wall
 
 
-def time_gather(torch, ibp, table, batches, warmup, steps, out, raw_baseline=False):
+def time_gather(torch, ibp, table, batches, warmup, steps, out, raw_baseline=False, raw_flags=0):
     """The timed region (`steps` launches back to back), then the same
     launches again one at a time between their own events.  Returns (wall
     seconds of the region, mean ms per launch in the region, per-launch ms of
@@ -256,7 +256,8 @@ def time_gather(torch, ibp, table, batches, warmup, steps, out, raw_baseline=Fal
     def run(k):
         d = batches[k]
         if raw_baseline:
-            ibp.raw_gather(table.raw, w.slot_bytes, w.n_tensors, d, n, w.tensor_bytes, out)
+            ibp.raw_gather(table.raw, w.slot_bytes, w.n_tensors, d, n, w.tensor_bytes, out,
+                           raw_flags)
         else:
             table.gather(ibp, d, n, out)
     region_ms, wall = region_launches(torch, run, warmup, steps)
@@ -370,6 +371,9 @@ def measure_workload(torch, ibp, W, key, T, where, host_flags, steps, warmup, wi
                                       raw_baseline=True)
         res["raw_kernel_ms"] = rregion
         res["raw_isolated_ms"] = rms
+        _, rregion, _ = time_gather(torch, ibp, table, batches, warmup, steps, out,
+                                    raw_baseline=True, raw_flags=ibp.RAW_ROUTE_XCD)
+        res["raw_routed_kernel_ms"] = rregion
     return res
 
 
@@ -465,7 +469,9 @@ def measure_pinned(torch, ibp, W, key, flags, args, pr):
            "unique_frac_of_measured": round(achieved_u / link, 4),
            "batch_payload_over_dense": round(comp / (w.batch * w.tensor_bytes), 5),
            "raw_gather_us": round(rm * 1e3, 2),
-           "transfer_speedup_vs_raw_gpu_gather": round(rm / km, 3)}
+           "transfer_speedup_vs_raw_gpu_gather": round(rm / km, 3),
+           "raw_gather_xcd_routed_us": round(m["raw_routed_kernel_ms"] * 1e3, 2),
+           "transfer_speedup_vs_raw_xcd_routed": round(m["raw_routed_kernel_ms"] / km, 3)}
     log(f"{key} pinned: {res}")
     return res, table
 

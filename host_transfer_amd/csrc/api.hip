@@ -349,16 +349,20 @@ int ibp_host_free(void* ptr) {
 }
 
 int ibp_raw_gather(const void* src, uint64_t row_stride, uint64_t n_rows, const int64_t* ids,
-                   uint64_t n_ids, uint32_t row_bytes, void* out, void* stream) {
+                   uint64_t n_ids, uint32_t row_bytes, void* out, unsigned flags, void* stream) {
   if (!src || !ids || !out) return fail(IBP_ERR_NULL, "ibp_raw_gather: src, ids and out are required");
   if (row_bytes == 0 || row_bytes % 4 != 0 || row_stride < row_bytes || row_stride % 4 != 0)
     return fail(IBP_ERR_SIZE, "ibp_raw_gather: row_bytes %% 4, row_stride >= row_bytes and %% 4");
   if (!aligned(src, 4) || !aligned(out, 4) || !aligned(ids, 8))
     return fail(IBP_ERR_ALIGN, "ibp_raw_gather: misaligned pointer");
+  if (flags & ~IBP_RAW_ROUTE_XCD) return fail(IBP_ERR_FLAGS, "ibp_raw_gather: unknown flags");
+  const bool route = (flags & IBP_RAW_ROUTE_XCD) != 0;
+  if (route && n_ids >= (1ull << 32))
+    return fail(IBP_ERR_SIZE, "ibp_raw_gather: routing needs n_ids < 2^32");
   int r;
   if ((r = require_device("ibp_raw_gather"))) return r;
   hipError_t e = ibp::launch_raw_gather((const uint8_t*)src, row_stride, n_rows, ids, n_ids,
-                                        row_bytes, (uint8_t*)out, (hipStream_t)stream);
+                                        row_bytes, (uint8_t*)out, route, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "ibp_raw_gather");
   return ok();
 }

@@ -683,12 +683,6 @@ static hipError_t launch_tile(const Geometry& g, GatherArgs a, hipStream_t s) {
 // bytes).  Tiles are processed one after another (no prefetch across tiles):
 // the launches this serves are short and have about one tile per wave.
 
-constexpr uint32_t kXcds = 8;
-
-__device__ __forceinline__ uint32_t xcd_of_tensor(int64_t id) {
-  return (uint32_t)(((uint64_t)id * 0x9E3779B97F4A7C15ull) >> 61);  // Fibonacci hashing, top 3 bits
-}
-
 // LDS bytes of one wave: T headers, T payload slots, the row list.
 __host__ __device__ constexpr uint32_t routed_list_cap(uint32_t T) { return T + (uint32_t)kWave; }
 __host__ __device__ inline uint32_t routed_wave_bytes(uint32_t T, uint32_t pbuf_bytes) {

@@ -120,6 +120,16 @@ __device__ __forceinline__ uint4 load_global(const uint4* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// MI355X has 8 XCDs, each with its own L2; workgroups are dispatched to them
+// round robin (block b runs on XCD b % 8).  The XCD a row is routed to is
+// chosen by a hash of its tensor index (Fibonacci hashing, top 3 bits), so all
+// rows of one tensor meet in one L2.
+constexpr uint32_t kXcds = 8;
+
+__device__ __forceinline__ uint32_t xcd_of_tensor(int64_t id) {
+  return (uint32_t)(((uint64_t)id * 0x9E3779B97F4A7C15ull) >> 61);
+}
+
 __device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
 
 // Orders LDS accesses among the lanes of one wave.

@@ -62,7 +62,7 @@ hipError_t launch_cache_fill(const uint8_t* store, uint64_t slot_bytes, const ui
 
 hipError_t launch_raw_gather(const uint8_t* src, uint64_t row_stride, uint64_t n_rows,
                              const int64_t* ids, uint64_t n_ids, uint32_t row_bytes, uint8_t* out,
-                             hipStream_t s);
+                             bool route, hipStream_t s);
 
 hipError_t launch_stream_read(const uint8_t* src, uint64_t bytes, uint32_t never, uint32_t* sink,
                               hipStream_t s);

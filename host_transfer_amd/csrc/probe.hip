@@ -44,6 +44,64 @@ __global__ __launch_bounds__(256) void k_raw_gather(const uint8_t* __restrict__ 
   }
 }
 
+// The same copy with every row routed to the XCD its id hashes to: the waves
+// of XCD x split the batch into equal segments, and each wave copies the rows
+// of its segment whose id hashes to x (the grid is a multiple of 8).
+__global__ __launch_bounds__(256) void k_raw_gather_routed(const uint8_t* __restrict__ src,
+                                                            uint64_t row_stride, uint64_t n_rows,
+                                                            const int64_t* __restrict__ ids,
+                                                            uint64_t n_ids, uint32_t row_bytes,
+                                                            uint8_t* __restrict__ out, bool wide,
+                                                            uint32_t lanes_log2) {
+  __shared__ uint32_t s_rows[4][kWave];
+  __shared__ int64_t s_ids[4][kWave];
+  const uint32_t lane = lane_id();
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  const uint32_t wpb = blockDim.x / kWave;
+  const uint32_t lanes = 1u << lanes_log2;
+  const uint32_t sub = lane >> lanes_log2, q0 = lane & (lanes - 1);
+  const uint32_t rows_per_wave = kWave >> lanes_log2;
+  const uint32_t xcd = blockIdx.x % kXcds;
+  const uint64_t wc = (uint64_t)(gridDim.x / kXcds) * wpb;
+  const uint64_t wk = (uint64_t)(blockIdx.x / kXcds) * wpb + wave;
+  const uint64_t seg = (n_ids + wc - 1) / wc;
+  const uint64_t s0 = min(wk * seg, n_ids), s1 = min(s0 + seg, n_ids);
+  for (uint64_t base = s0; base < s1; base += kWave) {
+    const uint64_t r = base + lane;
+    const bool in = r < s1;
+    const int64_t rid = ids[in ? r : s1 - 1];
+    const bool mine = in && xcd_of_tensor(rid) == xcd;
+    const uint64_t bal = __ballot(mine);
+    const uint32_t before = (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+    if (mine) {
+      s_rows[wave][before] = (uint32_t)r;
+      s_ids[wave][before] = rid;
+    }
+    const uint32_t n = (uint32_t)__popcll(bal);
+    wave_sync();
+    for (uint32_t k0 = 0; k0 < n; k0 += rows_per_wave) {
+      const uint32_t k = k0 + sub;
+      if (k >= n) continue;
+      const uint64_t row = s_rows[wave][k];
+      const int64_t id = s_ids[wave][k];
+      const bool valid = id >= 0 && (uint64_t)id < n_rows;
+      const uint8_t* sp = src + (valid ? (uint64_t)id * row_stride : 0);
+      uint8_t* d = out + row * row_bytes;
+      if (wide) {
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        for (uint32_t q = q0; q < row_bytes / 16; q += lanes) {
+          const u32x4 v = valid ? ((const u32x4*)sp)[q] : u32x4{0u, 0u, 0u, 0u};
+          __builtin_nontemporal_store(v, (u32x4*)d + q);
+        }
+      } else {
+        for (uint32_t q = q0; q < row_bytes / 4; q += lanes)
+          __builtin_nontemporal_store(valid ? ((const uint32_t*)sp)[q] : 0u, (uint32_t*)d + q);
+      }
+    }
+    wave_sync();
+  }
+}
+
 __global__ __launch_bounds__(256) void k_stream_read(const uint4* __restrict__ src, uint64_t n16,
                                                       uint32_t never, uint32_t* __restrict__ sink) {
   const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
@@ -63,7 +121,7 @@ __global__ __launch_bounds__(256) void k_stream_read(const uint4* __restrict__ s
 
 hipError_t launch_raw_gather(const uint8_t* src, uint64_t row_stride, uint64_t n_rows,
                              const int64_t* ids, uint64_t n_ids, uint32_t row_bytes, uint8_t* out,
-                             hipStream_t s) {
+                             bool route, hipStream_t s) {
   if (n_ids == 0) return hipSuccess;
   DeviceInfo di;
   hipError_t e = device_info(&di);
@@ -72,6 +130,16 @@ hipError_t launch_raw_gather(const uint8_t* src, uint64_t row_stride, uint64_t n
   const uint32_t units = row_bytes / (wide ? 16 : 4);
   uint32_t lanes_log2 = 0;
   while ((1u << lanes_log2) < units && (1u << lanes_log2) < (uint32_t)kWave) ++lanes_log2;
+  if (route) {
+    // about one window of ids per wave, eight XCD classes of blocks
+    const uint64_t want = (n_ids + 4ull * kWave - 1) / (4ull * kWave) * kXcds;
+    const uint64_t cap = (uint64_t)di.cus * 8;
+    uint64_t blocks = want < cap ? want : cap;
+    blocks = blocks < kXcds ? kXcds : blocks / kXcds * kXcds;
+    hipLaunchKernelGGL(k_raw_gather_routed, dim3((uint32_t)blocks), dim3(256), 0, s, src,
+                       row_stride, n_rows, ids, n_ids, row_bytes, out, wide, lanes_log2);
+    return hipGetLastError();
+  }
   // several rows per wave only while the batch still fills every CU with
   // waves (a wave per row keeps more requests in flight on small batches)
   while (lanes_log2 < 6 && n_ids / (kWave >> lanes_log2) < (uint64_t)di.cus * 32) ++lanes_log2;

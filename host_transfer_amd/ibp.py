@@ -54,7 +54,7 @@ _SIGS = {
                                      _u32, _vp, _vp, _vp, _vp],
     "ibp_host_alloc": [_u64, ctypes.c_uint, ctypes.POINTER(_vp)],
     "ibp_host_free": [_vp],
-    "ibp_raw_gather": [_vp, _u64, _u64, _vp, _u64, _u32, _vp, _vp],
+    "ibp_raw_gather": [_vp, _u64, _u64, _vp, _u64, _u32, _vp, ctypes.c_uint, _vp],
     "ibp_stream_read": [_vp, _u64, _u32, _vp, _vp],
 }
 for _name, _args in _SIGS.items():
@@ -160,9 +160,12 @@ def gather_decompress_hybrid(store, store_bytes, slot_bytes, cache, cache_bytes,
                                              _stream(stream)))
 
 
-def raw_gather(src, row_stride, n_rows, ids, n_ids, row_bytes, out, stream=None):
+RAW_ROUTE_XCD = 1
+
+
+def raw_gather(src, row_stride, n_rows, ids, n_ids, row_bytes, out, flags=0, stream=None):
     _check(_lib.ibp_raw_gather(_ptr(src), row_stride, n_rows, _ptr(ids), n_ids, row_bytes,
-                               _ptr(out), _stream(stream)))
+                               _ptr(out), flags, _stream(stream)))
 
 
 def stream_read(src, nbytes, never, sink, stream=None):

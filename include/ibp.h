@@ -264,10 +264,16 @@ int ibp_host_free(void *ptr);
  * [0, n_rows) give zero rows.  src device or host-mapped; row_bytes,
  * row_stride, src and out multiples of 4.  When all four are multiples of 16
  * the rows move in 16 B units (aligned transfers), else in 4 B units (the
- * unaligned GPU copy the pages compare against). */
+ * unaligned GPU copy the pages compare against).
+ * flags: 0, or IBP_RAW_ROUTE_XCD: each row is copied by a wave on the XCD
+ * chosen by a hash of its id, as ibp_gather_decompress does for small batches
+ * read from slots (repeated ids then share one XCD's L2); same output;
+ * requires n_ids < 2^32.  Errors: NULL pointers, sizes, alignment, unknown
+ * flags, n_ids too large for routing. */
+#define IBP_RAW_ROUTE_XCD 1u
 int ibp_raw_gather(const void *src, uint64_t row_stride, uint64_t n_rows,
                    const int64_t *ids, uint64_t n_ids, uint32_t row_bytes,
-                   void *out, void *stream);
+                   void *out, unsigned flags, void *stream);
 
 /* Reads bytes (a multiple of 16) at src with 16 B loads spread over the whole
  * GPU.  sink: device uint32[1]; written only if the XOR of all data equals

@@ -197,10 +197,11 @@ def test_compress_in_pieces_matches_whole():
                                                (4, 4, 0, 600000), (256, 256, 4, 777),
                                                (60, 68, 0, 300000), (4096, 4096, 0, 777),
                                                (16384, 16384, 4, 777)])
-def test_raw_gather_and_stream_read(B, stride, shift, m):
+@pytest.mark.parametrize("flags", [0, 1])
+def test_raw_gather_and_stream_read(B, stride, shift, m, flags):
     """Uncompressed baseline gather: several rows per wave for short rows in
     large batches, 4 B units for rows at a 4 B offset, zero rows for invalid
-    ids."""
+    ids; with flags = 1 every row is copied on the XCD its id hashes to."""
     from host_transfer_amd import ibp
     rng = np.random.default_rng(11 + B)
     n = 500
@@ -208,9 +209,9 @@ def test_raw_gather_and_stream_read(B, stride, shift, m):
     hb = ibp.HostBuffer(n * stride + shift)
     hb.array[shift:] = raw.ravel()
     ids = rng.integers(-2, n + 2, m)
-    G.log(f"[parity] raw gather B={B} stride={stride} shift={shift} ids={m}")
+    G.log(f"[parity] raw gather B={B} stride={stride} shift={shift} ids={m} flags={flags}")
     out = torch.zeros(m * B, dtype=torch.int8, device="cuda")
-    ibp.raw_gather(hb.ptr + shift, stride, n, G.dev(ids), m, B, out)
+    ibp.raw_gather(hb.ptr + shift, stride, n, G.dev(ids), m, B, out, flags)
     got = G.host(out).view(np.uint8).reshape(m, B)
     assert (got == G.expected_rows(raw[:, :B].copy(), ids)).all()
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
