@@ -716,25 +716,29 @@ __global__ __launch_bounds__(256) void k_gather_tile_routed(GatherArgs a) {
   const uint64_t seg = (a.n_ids + wc - 1) / wc;
   const uint64_t s0 = min(wk * seg, a.n_ids), s1 = min(s0 + seg, a.n_ids);
 
+  // The Mask words and the first window of ids are requested first; the
+  // per-word registers are built once the first tile's payloads are in
+  // flight.
   PlanRun run;
   load_plan_run(a.mask, a.sh, run);
   WordRegs<J> R;
   load_plan_fetch<J>(a.mask, a.bitval, a.sh, lane, R);
+  int64_t win_id = a.ids[min(s0 + lane, a.n_ids - 1)];
   load_plan_counts(run, a.sh, s_pref, s_kc, s_wsum);  // workgroup barriers: every thread
-  load_plan_words<J>(a.sh, s_pref, lane, R);
   if (s0 >= s1) return;  // per wave; no workgroup barrier follows
 
   const uint32_t lrow = lane / LPR, lunit = lane % LPR;
   const uint32_t slot16 = a.pbuf_bytes >> 4;
   const uint64_t zero_addr = (uint64_t)&g_zero16;
   const uint32_t W = a.sh.W;
-  uint32_t count = 0;  // rows in the list (wave-uniform)
+  bool planned = false;  // per-word registers built (wave-uniform)
+  uint32_t count = 0;    // rows in the list (wave-uniform)
   for (uint64_t base = s0; base < s1; base += kWave) {
     // 1. this window's rows that belong to this XCD -> the list
     {
       const uint64_t r = base + lane;
       const bool in = r < s1;
-      const int64_t id = a.ids[in ? r : s1 - 1];
+      const int64_t id = base == s0 ? win_id : a.ids[in ? r : s1 - 1];
       const bool mine = in && xcd_of_tensor(id) == xcd;
       const uint64_t bal = __ballot(mine);
       const uint32_t before = (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
@@ -766,6 +770,10 @@ __global__ __launch_bounds__(256) void k_gather_tile_routed(GatherArgs a) {
       }
       IBP_RT_LOAD(0) IBP_RT_LOAD(1) IBP_RT_LOAD(2) IBP_RT_LOAD(3)
       IBP_RT_LOAD(4) IBP_RT_LOAD(5) IBP_RT_LOAD(6) IBP_RT_LOAD(7)
+      if (!planned) {
+        load_plan_words<J>(a.sh, s_pref, lane, R);
+        planned = true;
+      }
       IBP_RT_STAGE(0) IBP_RT_STAGE(1) IBP_RT_STAGE(2) IBP_RT_STAGE(3)
       IBP_RT_STAGE(4) IBP_RT_STAGE(5) IBP_RT_STAGE(6) IBP_RT_STAGE(7)
 #undef IBP_RT_LOAD
