@@ -219,11 +219,11 @@ class Table:
         self.store_bytes = total
         self.where = "hbm"
 
-    def gather(self, ibp, d_ids, n_ids, out):
+    def gather(self, ibp, d_ids, n_ids, out, flags=0):
         w = self.w
-        ibp.gather_decompress(self.store, self.store_bytes, w.slot_bytes, self.offsets, self.part,
-                              w.n_tensors, d_ids, n_ids, w.tensor_bytes, w.chunk_bytes, self.mask,
-                              self.bitval, out)
+        ibp.gather_decompress_ex(self.store, self.store_bytes, w.slot_bytes, self.offsets,
+                                 self.part, w.n_tensors, d_ids, n_ids, w.tensor_bytes,
+                                 w.chunk_bytes, self.mask, self.bitval, out, flags)
 
 
 def region_launches(torch, fn, warmup, steps):
@@ -245,7 +245,8 @@ def region_launches(torch, fn, warmup, steps):
     return a.elapsed_time(b) / steps, wall
 
 
-def time_gather(torch, ibp, table, batches, warmup, steps, out, raw_baseline=False, raw_flags=0):
+def time_gather(torch, ibp, table, batches, warmup, steps, out, raw_baseline=False, raw_flags=0,
+                flags=0):
     """The timed region (`steps` launches back to back), then the same
     launches again one at a time between their own events.  Returns (wall
     seconds of the region, mean ms per launch in the region, per-launch ms of
@@ -259,7 +260,7 @@ def time_gather(torch, ibp, table, batches, warmup, steps, out, raw_baseline=Fal
             ibp.raw_gather(table.raw, w.slot_bytes, w.n_tensors, d, n, w.tensor_bytes, out,
                            raw_flags)
         else:
-            table.gather(ibp, d, n, out)
+            table.gather(ibp, d, n, out, flags)
     region_ms, wall = region_launches(torch, run, warmup, steps)
     isolated = timed_launches(torch, run, warmup, steps)  # ends on the last batch again
     return wall, region_ms, isolated
@@ -361,11 +362,16 @@ def measure_workload(torch, ibp, W, key, T, where, host_flags, steps, warmup, wi
     ids_host = [W.batch_ids(w, k) for k in range(nb)]
     batches = [torch.from_numpy(i).cuda() for i in ids_host]
     out = torch.empty(w.batch * w.tensor_bytes, dtype=torch.uint8, device="cuda")
-    wall, region_ms, ms = time_gather(torch, ibp, table, batches, warmup, steps, out)
+    # batches that repeat ids (Zipf) read from slots: rows routed to XCDs
+    route = ibp.GATHER_ROUTE_XCD if (w.id_law == "zipf" and where == "pinned") else 0
+    wall, region_ms, ms = time_gather(torch, ibp, table, batches, warmup, steps, out, flags=route)
     check_rows(table, ids_host[-1], out)
     comp = [int(table.len_host[i].sum()) for i in ids_host[warmup:]]
     res = {"table": table, "ids_host": ids_host, "wall": wall, "kernel_ms": region_ms,
-           "isolated_ms": ms, "comp_bytes": comp, "T": T}
+           "isolated_ms": ms, "comp_bytes": comp, "T": T, "routed": bool(route)}
+    if route:
+        _, res["unrouted_kernel_ms"], _ = time_gather(torch, ibp, table, batches, warmup, steps,
+                                                      out)
     if with_raw:
         _, rregion, rms = time_gather(torch, ibp, table, batches, warmup, steps, out,
                                       raw_baseline=True)
@@ -471,7 +477,10 @@ def measure_pinned(torch, ibp, W, key, flags, args, pr):
            "raw_gather_us": round(rm * 1e3, 2),
            "transfer_speedup_vs_raw_gpu_gather": round(rm / km, 3),
            "raw_gather_xcd_routed_us": round(m["raw_routed_kernel_ms"] * 1e3, 2),
-           "transfer_speedup_vs_raw_xcd_routed": round(m["raw_routed_kernel_ms"] / km, 3)}
+           "transfer_speedup_vs_raw_xcd_routed": round(m["raw_routed_kernel_ms"] / km, 3),
+           "xcd_routed": m["routed"]}
+    if m["routed"]:
+        res["kernel_us_unrouted"] = round(m["unrouted_kernel_ms"] * 1e3, 2)
     log(f"{key} pinned: {res}")
     return res, table
 

@@ -221,6 +221,23 @@ int ibp_gather_decompress(const void* store, uint64_t store_bytes, uint64_t slot
                           const int64_t* ids, uint64_t n_ids, uint32_t tensor_bytes,
                           uint32_t chunk_bytes, const uint32_t* mask, const uint32_t* bitval,
                           void* out, void* stream) {
+  return ibp_gather_decompress_ex(store, store_bytes, slot_bytes, offsets, part_bits, n_tensors,
+                                  ids, n_ids, tensor_bytes, chunk_bytes, mask, bitval, out, 0u,
+                                  stream);
+}
+
+int ibp_gather_decompress_ex(const void* store, uint64_t store_bytes, uint64_t slot_bytes,
+                             const uint64_t* offsets, const uint32_t* part_bits,
+                             uint64_t n_tensors, const int64_t* ids, uint64_t n_ids,
+                             uint32_t tensor_bytes, uint32_t chunk_bytes, const uint32_t* mask,
+                             const uint32_t* bitval, void* out, unsigned flags, void* stream) {
+  if (flags & ~IBP_GATHER_ROUTE_XCD)
+    return fail(IBP_ERR_FLAGS, "ibp_gather_decompress: unknown flags");
+  const bool route = (flags & IBP_GATHER_ROUTE_XCD) != 0;
+  if (route && offsets)
+    return fail(IBP_ERR_FLAGS, "ibp_gather_decompress: routing applies to slot mode (no offsets)");
+  if (route && n_ids >= (1ull << 32))
+    return fail(IBP_ERR_SIZE, "ibp_gather_decompress: routing needs n_ids < 2^32");
   if (!store || !part_bits || !ids || !mask || !bitval || !out)
     return fail(IBP_ERR_NULL,
                 "ibp_gather_decompress: store, part_bits, ids, mask, bitval and out are required");
@@ -247,10 +264,10 @@ int ibp_gather_decompress(const void* store, uint64_t store_bytes, uint64_t slot
   // slot mode: store holds the slots; cache mode: store is the compacted cache
   hipError_t e = offsets
       ? ibp::launch_gather(g, nullptr, 0, 0, offsets, (const uint8_t*)store, store_bytes,
-                           part_bits, n_tensors, ids, n_ids, mask, bitval, (uint32_t*)out,
+                           part_bits, n_tensors, ids, n_ids, mask, bitval, (uint32_t*)out, false,
                            (hipStream_t)stream)
       : ibp::launch_gather(g, (const uint8_t*)store, store_bytes, slot_bytes, nullptr, nullptr, 0,
-                           part_bits, n_tensors, ids, n_ids, mask, bitval, (uint32_t*)out,
+                           part_bits, n_tensors, ids, n_ids, mask, bitval, (uint32_t*)out, route,
                            (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "ibp_gather_decompress");
   return ok();
@@ -319,7 +336,7 @@ int ibp_gather_decompress_hybrid(const void* store, uint64_t store_bytes, uint64
   const ibp::Geometry g = ibp::make_geometry(tensor_bytes, chunk_bytes);
   hipError_t e = ibp::launch_gather(g, (const uint8_t*)store, store_bytes, slot_bytes,
                                     cache_offsets, (const uint8_t*)cache, cache_bytes, part_bits,
-                                    n_tensors, ids, n_ids, mask, bitval, (uint32_t*)out,
+                                    n_tensors, ids, n_ids, mask, bitval, (uint32_t*)out, false,
                                     (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "ibp_gather_decompress_hybrid");
   return ok();

@@ -50,6 +50,7 @@ struct GatherArgs {
   Shape sh;
   uint32_t groups;      // groups per workgroup
   uint32_t pbuf_bytes;  // LDS payload buffer per group
+  uint32_t route;       // route ids to XCDs (slot mode only)
 };
 
 // LDS layout, in bytes from the start of dynamic shared memory.  Per group:
@@ -191,6 +192,44 @@ __device__ __forceinline__ uint32_t payload_units(const GatherArgs& a, const Gro
   return (uint32_t)(min((uint64_t)want, h.avail) >> 4);
 }
 
+// Decodes one tensor staged in LDS (pb32) and stores its words: thread gl
+// owns words gl + G j.  With chunks of at least 64 words, the 64 words a wave
+// handles for one j lie in one chunk, so the chunk, its participation and its
+// offset (obuf, from the chunk scan) are wave-uniform.
+template <int J>
+__device__ __forceinline__ void decode_group_tensor(const GatherArgs& a, const WordRegs<J>& R,
+                                                    const GroupHdr& h, const uint32_t* obuf,
+                                                    const uint32_t* pb32, uint32_t gl, uint32_t G,
+                                                    uint32_t* orow) {
+  const uint32_t W = a.sh.W;
+  const uint32_t wave_w0 = uniform(gl) & ~(kWave - 1u);
+  if (!uniform(h.valid)) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const uint32_t w = gl + G * j;
+      if (w < W) store_out(orow + w, 0u);
+    }
+    return;
+  }
+  const uint32_t pmask_lo = uniform((uint32_t)h.pmask), pmask_hi = uniform((uint32_t)(h.pmask >> 32));
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const uint32_t w = gl + G * j;
+    const uint32_t c = (wave_w0 + G * j) >> a.sh.wpc_log2;  // uniform
+    if (c >= a.sh.n_c) continue;                            // whole wave past the end
+    const uint32_t o = uniform(obuf[c]);
+    const bool p = ((c < 32 ? pmask_lo >> c : pmask_hi >> (c - 32)) & 1u) != 0u;
+    uint32_t v;
+    if (p) {
+      v = window32(pb32, o + (R.info[j] & 0xFFFFu));
+      v = bfi_op(R.mask[j], R.bitval[j], unpack_stages(v, R.mv[j], R.stages[j]));
+    } else {
+      v = window32(pb32, o + (R.info[j] >> 16));
+    }
+    if (w < W) store_out(orow + w, v);
+  }
+}
+
 template <int J>
 __global__ __launch_bounds__(1024) void k_gather_decompress(GatherArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
@@ -278,38 +317,124 @@ __global__ __launch_bounds__(1024) void k_gather_decompress(GatherArgs a) {
       v0 = load_global(gl < n16 ? src + gl : &g_zero16);
       v1 = load_global(gl + G < n16 ? src + gl + G : &g_zero16);
     }
-    // 4. decode this tensor's words and store them.  With chunks of at least
-    //    64 words, the 64 words a wave handles for one j lie in one chunk, so
-    //    the chunk, its participation and its offset are wave-uniform.
-    const uint32_t* obuf = obufs + 64u * cur;
-    uint32_t* orow = a.out + row * W;
-    const uint32_t wave_w0 = uniform(gl) & ~(kWave - 1u);
-    if (!uniform(h.valid)) {
-#pragma unroll
-      for (int j = 0; j < J; ++j) {
-        const uint32_t w = gl + G * j;
-        if (w < W) orow[w] = 0u;
+    // 4. decode this tensor's words and store them
+    decode_group_tensor<J>(a, R, h, obufs + 64u * cur, pb32, gl, G, a.out + row * W);
+    group_sync(single);
+  }
+}
+
+// Group kernel with XCD-aware routing (see k_gather_tile_routed), for
+// payloads read from their slots, one group per workgroup.  The group's first
+// wave scans its segment of the batch a window of 64 ids at a time and lists
+// the rows whose tensor hashes to this XCD; the group decodes the listed rows
+// in order with a one-deep pipeline: the next tensor's chunk scan and payload
+// loads are issued before the current tensor is decoded, and the metadata of
+// the one after that before those.
+__host__ __device__ constexpr uint32_t routed_group_list_bytes() {
+  return (uint32_t)kWave * 12u + 16u;  // ids, rows, count
+}
+
+template <int J>
+__global__ __launch_bounds__(1024) void k_gather_decompress_routed(GatherArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const GatherLds L(a.sh.W, a.pbuf_bytes);
+  uint32_t* s_pref = (uint32_t*)(smem + L.pref);
+  uint32_t* s_kc = (uint32_t*)(smem + L.kc);
+  uint32_t* s_wsum = (uint32_t*)(smem + L.wsum);
+  const uint32_t G = blockDim.x;  // one group per workgroup
+  const uint32_t gl = threadIdx.x;
+  uint8_t* gbase = smem + L.group0;
+  GroupHdr* hdrs = (GroupHdr*)gbase;                            // [2]
+  uint32_t* obufs = (uint32_t*)(gbase + 2 * sizeof(GroupHdr));  // [2][64]
+  uint8_t* pbuf = gbase + 2 * sizeof(GroupHdr) + 512;
+  const uint32_t* pb32 = (const uint32_t*)pbuf;
+  uint4* pb128 = (uint4*)pbuf;
+  int64_t* list_id = (int64_t*)(smem + L.total(1));  // [64]
+  uint32_t* list_row = (uint32_t*)(list_id + kWave);  // [64]
+  uint32_t* s_n = list_row + kWave;                   // [1]
+  const bool first_wave = gl < kWave;
+  const uint32_t W = a.sh.W;
+
+  const uint32_t xcd = blockIdx.x % kXcds;
+  const uint64_t wc = gridDim.x / kXcds;
+  const uint64_t wk = blockIdx.x / kXcds;
+  const uint64_t seg = (a.n_ids + wc - 1) / wc;
+  const uint64_t s0 = min(wk * seg, a.n_ids), s1 = min(s0 + seg, a.n_ids);
+
+  PlanRun run;
+  load_plan_run(a.mask, a.sh, run);
+  WordRegs<J> R;
+  load_plan_fetch<J>(a.mask, a.bitval, a.sh, gl, R);
+  const int64_t win_id = a.ids[min(s0 + gl % kWave, a.n_ids - 1)];
+  load_plan_counts(run, a.sh, s_pref, s_kc, s_wsum);  // workgroup barriers
+  if (s0 >= s1) return;                               // the whole workgroup
+
+  bool planned = false;
+  for (uint64_t base = s0; base < s1; base += kWave) {
+    if (first_wave) {
+      const uint64_t r = base + gl;
+      const bool in = r < s1;
+      const int64_t id = base == s0 ? win_id : a.ids[in ? r : s1 - 1];
+      const bool mine = in && xcd_of_tensor(id) == xcd;
+      const uint64_t bal = __ballot(mine);
+      const uint32_t before = (uint32_t)__popcll(bal & ((1ull << gl) - 1ull));
+      if (mine) {
+        list_id[before] = id;
+        list_row[before] = (uint32_t)r;
       }
-    } else {
-      const uint32_t pmask_lo = uniform((uint32_t)h.pmask), pmask_hi = uniform((uint32_t)(h.pmask >> 32));
-#pragma unroll
-      for (int j = 0; j < J; ++j) {
-        const uint32_t w = gl + G * j;
-        const uint32_t c = (wave_w0 + G * j) >> a.sh.wpc_log2;  // uniform
-        if (c >= a.sh.n_c) continue;                            // whole wave past the end
-        const uint32_t o = uniform(obuf[c]);
-        const bool p = ((c < 32 ? pmask_lo >> c : pmask_hi >> (c - 32)) & 1u) != 0u;
-        uint32_t v;
-        if (p) {
-          v = window32(pb32, o + (R.info[j] & 0xFFFFu));
-          v = bfi_op(R.mask[j], R.bitval[j], unpack_stages(v, R.mv[j], R.stages[j]));
-        } else {
-          v = window32(pb32, o + (R.info[j] >> 16));
+      if (gl == 0) s_n[0] = (uint32_t)__popcll(bal);
+    }
+    __syncthreads();
+    const uint32_t n = s_n[0];
+    if (n != 0u) {
+      // prologue: the first listed tensor's scan and payload, the second's metadata
+      {
+        const RowMeta m = load_meta(a, list_id[0], gl);
+        if (first_wave) scan_row(a, m, gl, s_kc, &hdrs[0], obufs);
+      }
+      __syncthreads();
+      uint4 v0, v1;
+      {
+        const GroupHdr h = hdrs[0];
+        const uint32_t n16 = payload_units(a, h);
+        const uint4* src = (const uint4*)h.addr;
+        v0 = load_global(gl < n16 ? src + gl : &g_zero16);
+        v1 = load_global(gl + G < n16 ? src + gl + G : &g_zero16);
+      }
+      RowMeta meta_next = load_meta(a, list_id[min(1u, n - 1u)], gl);
+      if (!planned) {
+        load_plan_words<J>(a.sh, s_pref, gl, R);
+        planned = true;
+      }
+      for (uint32_t k = 0; k < n; ++k) {
+        const uint32_t cur = k & 1u;
+        const bool has_next = k + 1u < n;
+        // 1. this payload -> LDS; the next tensor's scan
+        const GroupHdr h = hdrs[cur];
+        {
+          const uint32_t n16 = payload_units(a, h);
+          if (gl < n16) pb128[gl] = v0;
+          if (gl + G < n16) pb128[gl + G] = v1;
         }
-        if (w < W) store_out(orow + w, v);
+        if (first_wave && has_next)
+          scan_row(a, meta_next, gl, s_kc, &hdrs[cur ^ 1u], obufs + 64u * (cur ^ 1u));
+        __syncthreads();
+        // 2. the next payload and the metadata after it, before this decode
+        {
+          const GroupHdr hn = hdrs[cur ^ 1u];
+          const uint32_t n16 = has_next ? payload_units(a, hn) : 0u;
+          const uint4* src = (const uint4*)hn.addr;
+          v0 = load_global(gl < n16 ? src + gl : &g_zero16);
+          v1 = load_global(gl + G < n16 ? src + gl + G : &g_zero16);
+        }
+        meta_next = load_meta(a, list_id[min(k + 2u, n - 1u)], gl);
+        // 3. decode and store this tensor
+        decode_group_tensor<J>(a, R, h, obufs + 64u * cur, pb32, gl, G,
+                               a.out + (uint64_t)list_row[k] * W);
+        __syncthreads();
       }
     }
-    group_sync(single);
+    __syncthreads();  // the list and its count are rewritten by the next window
   }
 }
 
@@ -852,8 +977,7 @@ static hipError_t launch_small(const Geometry& g, const GatherArgs& a, hipStream
   if (e != hipSuccess) return e;
   const bool full = g.W == (uint32_t)kWave * J;
   const bool big = a.n_ids >= (uint64_t)8 * RPI * 8 * (uint64_t)di.cus;
-  // payloads from their slots (no offset table): route repeated ids to one XCD
-  if (a.offsets == nullptr && a.n_ids < (1ull << 32) && !big)
+  if (a.route)
     return full ? launch_tile_routed<J, 2 * RPI, RPI, true>(g, a, s)
                 : launch_tile_routed<J, 2 * RPI, RPI, false>(g, a, s);
   if (big)
@@ -863,7 +987,29 @@ static hipError_t launch_small(const Geometry& g, const GatherArgs& a, hipStream
 }
 
 template <int J>
+static hipError_t launch_j_routed(const Geometry& g, const GatherArgs& a, hipStream_t s) {
+  const GatherLds L(g.W, a.pbuf_bytes);
+  const uint32_t lds = L.total(1) + routed_group_list_bytes();
+  const uint32_t threads = g.group;
+  DeviceInfo di;
+  hipError_t e = device_info(&di);
+  if (e != hipSuccess) return e;
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gather_decompress_routed<J>, threads,
+                                                   lds);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) return hipErrorInvalidConfiguration;
+  const uint64_t cap = (uint64_t)per_cu * (uint64_t)di.cus;
+  uint64_t blocks = a.n_ids < cap ? a.n_ids : cap;
+  blocks = blocks < kXcds ? kXcds : blocks / kXcds * kXcds;
+  hipLaunchKernelGGL(k_gather_decompress_routed<J>, dim3((uint32_t)blocks), dim3(threads), lds, s,
+                     a);
+  return hipGetLastError();
+}
+
+template <int J>
 static hipError_t launch_j(const Geometry& g, const GatherArgs& a, hipStream_t s) {
+  if (a.route && g.groups == 1) return launch_j_routed<J>(g, a, s);
   const GatherLds L(g.W, a.pbuf_bytes);
   const uint32_t lds = L.total(g.groups);
   const uint32_t threads = g.group * g.groups;
@@ -885,7 +1031,7 @@ hipError_t launch_gather(const Geometry& g, const uint8_t* store, uint64_t store
                          uint64_t slot_bytes, const uint64_t* offsets, const uint8_t* cache,
                          uint64_t cache_bytes, const uint32_t* part_bits, uint64_t n_tensors,
                          const int64_t* ids, uint64_t n_ids, const uint32_t* mask,
-                         const uint32_t* bitval, uint32_t* out, hipStream_t s) {
+                         const uint32_t* bitval, uint32_t* out, bool route, hipStream_t s) {
   if (n_ids == 0) return hipSuccess;
   // no tensors: every id is out of range and every row is zero
   if (n_tensors == 0) return launch_fill_u32(out, n_ids * (uint64_t)g.W, 0u, s);
@@ -905,6 +1051,7 @@ hipError_t launch_gather(const Geometry& g, const uint8_t* store, uint64_t store
   a.out = out;
   a.sh = Shape{g.W, g.n_c, g.wpc_log2, g.last_bits, g.group};
   a.groups = g.groups;
+  a.route = route && offsets == nullptr && n_ids < (1ull << 32);
   // payload rounded to 16 B, plus one word read past the end by the window
   a.pbuf_bytes = ((g.tensor_bytes + 15u) & ~15u) + 16u;
   if (g.W <= 4 * (uint32_t)kWave) {

@@ -51,7 +51,7 @@ hipError_t launch_gather(const Geometry& g, const uint8_t* store, uint64_t store
                          uint64_t slot_bytes, const uint64_t* offsets, const uint8_t* cache,
                          uint64_t cache_bytes, const uint32_t* part_bits, uint64_t n_tensors,
                          const int64_t* ids, uint64_t n_ids, const uint32_t* mask,
-                         const uint32_t* bitval, uint32_t* out, hipStream_t s);
+                         const uint32_t* bitval, uint32_t* out, bool route, hipStream_t s);
 
 hipError_t launch_cache_offsets(const uint32_t* lengths, const uint32_t* select, uint64_t n,
                                 uint64_t* offsets, hipStream_t s);

@@ -48,6 +48,8 @@ _SIGS = {
     "ibp_compact": [_vp, _u64, _u64, _vp, _vp, _u64, _vp],
     "ibp_gather_decompress": [_vp, _u64, _u64, _vp, _vp, _u64, _vp, _u64, _u32, _u32, _vp, _vp,
                               _vp, _vp],
+    "ibp_gather_decompress_ex": [_vp, _u64, _u64, _vp, _vp, _u64, _vp, _u64, _u32, _u32, _vp,
+                                 _vp, _vp, ctypes.c_uint, _vp],
     "ibp_cache_offsets": [_vp, _vp, _u64, _vp, _vp],
     "ibp_cache_fill": [_vp, _u64, _vp, _u64, _vp, _vp, _u64, _vp],
     "ibp_gather_decompress_hybrid": [_vp, _u64, _u64, _vp, _u64, _vp, _vp, _u64, _vp, _u64, _u32,
@@ -138,6 +140,17 @@ def gather_decompress(store, store_bytes, slot_bytes, offsets, part_bits, n_tens
                                       _ptr(part_bits), n_tensors, _ptr(ids), n_ids, tensor_bytes,
                                       chunk_bytes, _ptr(mask), _ptr(bitval), _ptr(out),
                                       _stream(stream)))
+
+
+GATHER_ROUTE_XCD = 1
+
+
+def gather_decompress_ex(store, store_bytes, slot_bytes, offsets, part_bits, n_tensors, ids, n_ids,
+                         tensor_bytes, chunk_bytes, mask, bitval, out, flags=0, stream=None):
+    _check(_lib.ibp_gather_decompress_ex(_ptr(store), store_bytes, slot_bytes, _ptr(offsets),
+                                         _ptr(part_bits), n_tensors, _ptr(ids), n_ids,
+                                         tensor_bytes, chunk_bytes, _ptr(mask), _ptr(bitval),
+                                         _ptr(out), flags, _stream(stream)))
 
 
 def cache_offsets(lengths, select, n_tensors, offsets, stream=None):

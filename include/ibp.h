@@ -197,6 +197,25 @@ int ibp_gather_decompress(const void *store, uint64_t store_bytes,
                           const uint32_t *mask, const uint32_t *bitval,
                           void *out, void *stream);
 
+/* ibp_gather_decompress with flags (0 = ibp_gather_decompress).
+ *   IBP_GATHER_ROUTE_XCD  slot mode only (offsets == NULL), n_ids < 2^32.
+ *     Each row is decoded on the XCD (the GPU's eight dies, each with its own
+ *     L2 cache) chosen by a hash of its tensor index, so a tensor that the
+ *     batch repeats is read over the host link (or from HBM) once per launch
+ *     instead of once per XCD.  Same output.  For batches with repeated ids
+ *     (Zipf embedding or feature lookups); batches without repeats are as
+ *     fast or faster without it, because rows then spread less evenly.
+ * Errors: as ibp_gather_decompress; unknown flags, routing with an offset
+ * table (IBP_ERR_FLAGS); routing with n_ids >= 2^32 (IBP_ERR_SIZE). */
+#define IBP_GATHER_ROUTE_XCD 1u
+int ibp_gather_decompress_ex(const void *store, uint64_t store_bytes,
+                             uint64_t slot_bytes, const uint64_t *offsets,
+                             const uint32_t *part_bits, uint64_t n_tensors,
+                             const int64_t *ids, uint64_t n_ids,
+                             uint32_t tensor_bytes, uint32_t chunk_bytes,
+                             const uint32_t *mask, const uint32_t *bitval,
+                             void *out, unsigned flags, void *stream);
+
 /* ------------------------------------------------------ cache + store together
  * [G-EN] System Integration uses both placements at once: a compressed
  * software cache in GPU memory for hot tensors, and compressed in-place
@@ -266,8 +285,8 @@ int ibp_host_free(void *ptr);
  * the rows move in 16 B units (aligned transfers), else in 4 B units (the
  * unaligned GPU copy the pages compare against).
  * flags: 0, or IBP_RAW_ROUTE_XCD: each row is copied by a wave on the XCD
- * chosen by a hash of its id, as ibp_gather_decompress does for small batches
- * read from slots (repeated ids then share one XCD's L2); same output;
+ * chosen by a hash of its id, as ibp_gather_decompress_ex does with
+ * IBP_GATHER_ROUTE_XCD (repeated ids then share one XCD's L2); same output;
  * requires n_ids < 2^32.  Errors: NULL pointers, sizes, alignment, unknown
  * flags, n_ids too large for routing. */
 #define IBP_RAW_ROUTE_XCD 1u

@@ -106,12 +106,21 @@ def check_store(rows, mask, bitval, C, slot, store, part, lengths, first=0, n_te
     return o_store, o_part, o_len
 
 
-def gpu_gather(store, store_nbytes, slot, offsets, part, n_tensors, ids, B, C, mask, bitval):
+ROUTE = 1  # IBP_GATHER_ROUTE_XCD
+
+
+def gpu_gather(store, store_nbytes, slot, offsets, part, n_tensors, ids, B, C, mask, bitval,
+               flags=0):
+    """ibp_gather_decompress (flags == 0) or ibp_gather_decompress_ex(flags)."""
     ids = np.ascontiguousarray(ids, np.int64)
     out = torch.full((max(1, len(ids)) * B,), -1, dtype=torch.int8, device="cuda")
     d_ids = dev(ids) if len(ids) else torch.zeros(1, dtype=torch.int64, device="cuda")
-    ibp.gather_decompress(store, store_nbytes, slot, offsets, part, n_tensors, d_ids, len(ids), B,
-                          C, dev(mask), dev(bitval), out)
+    if flags:
+        ibp.gather_decompress_ex(store, store_nbytes, slot, offsets, part, n_tensors, d_ids,
+                                 len(ids), B, C, dev(mask), dev(bitval), out, flags)
+    else:
+        ibp.gather_decompress(store, store_nbytes, slot, offsets, part, n_tensors, d_ids, len(ids),
+                              B, C, dev(mask), dev(bitval), out)
     return host(out).view(np.uint8)[:len(ids) * B].reshape(len(ids), B)
 
 

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(ibp):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     out = subprocess.run(["nm", "-D", "--defined-only", ibp.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (ibp_\w+)$", out, flags=re.M))
@@ -109,6 +109,12 @@ def test_gather_validation(ibp):
     _expect(ibp, ibp.ERR_ALIGN, f, *args(out=P + 4))
     _expect(ibp, ibp.ERR_ALIGN, f, *args(ids=P + 4))
     _expect(ibp, ibp.ERR_ALIGN, f, *args(offs=P + 4))
+    # the flags of ibp_gather_decompress_ex
+    fx = ibp.gather_decompress_ex
+    _expect(ibp, ibp.ERR_FLAGS, fx, *args(), 2)
+    _expect(ibp, ibp.ERR_FLAGS, fx, *args(offs=P), ibp.GATHER_ROUTE_XCD)
+    _expect(ibp, ibp.ERR_SIZE, fx, *args(nids=1 << 32), ibp.GATHER_ROUTE_XCD)
+    _expect(ibp, ibp.ERR_SIZE, fx, *args(sbytes=10 * 512 - 1), ibp.GATHER_ROUTE_XCD)
 
 
 def test_other_validation(ibp):

@@ -77,15 +77,15 @@ def check_sampled_store(t, rng):
     return g_len
 
 
-def check_gather(t, ids, store, store_bytes, offsets, rng, label):
+def check_gather(t, ids, store, store_bytes, offsets, rng, label, flags=0):
     """Every row lossless; SAMPLE rows equal to the oracle's gather."""
     w = t["w"]
     N, B, C, S = w.n_tensors, w.tensor_bytes, w.chunk_bytes, w.slot_bytes
     nb = len(ids)
     out = torch.empty(nb * B, dtype=torch.uint8, device="cuda")
-    G.log(f"[fullsize] {w.key}: gather {nb} ids ({label})")
-    ibp.gather_decompress(store, store_bytes, S, offsets, t["part"], N, G.dev(ids), nb, B, C,
-                          t["d_mask"], t["d_bitval"], out)
+    G.log(f"[fullsize] {w.key}: gather {nb} ids ({label}, flags {flags})")
+    ibp.gather_decompress_ex(store, store_bytes, S, offsets, t["part"], N, G.dev(ids), nb, B, C,
+                             t["d_mask"], t["d_bitval"], out, flags)
     got = G.host(out).reshape(nb, B)
     assert (got == t["view"][ids]).all(), f"{label}: gathered rows are not the original rows"
     pick = rng.choice(nb, min(SAMPLE, nb), replace=False)
@@ -141,14 +141,15 @@ def test_fullsize_hbm_cache(key):
     t["raw"].free()
 
 
-@pytest.mark.parametrize("key", ["dense_gnn", "dlrm_2k"])
+@pytest.mark.parametrize("key", ["dense_gnn", "dlrm_1k", "dlrm_2k"])
 def test_fullsize_pinned(key):
     rng = np.random.default_rng(303)
     w = W.WORKLOADS[key]
     t = build_table(w, "pinned")
     check_sampled_store(t, rng)
-    check_gather(t, W.batch_ids(w, 0), t["store"], w.n_tensors * w.slot_bytes, None, rng,
-                 "Table-D batch")
+    for flags in (0, G.ROUTE):  # plain, and routed to XCDs (the bench's launch for Zipf ids)
+        check_gather(t, W.batch_ids(w, 0), t["store"], w.n_tensors * w.slot_bytes, None, rng,
+                     "Table-D batch", flags)
     t["raw"].free()
     t["store"].free()
 

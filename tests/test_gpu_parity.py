@@ -2,8 +2,10 @@
 
 Inputs are the seeded workloads at sizes the oracle finishes in seconds
 (several tiles and a ragged tail each), random tensors covering every thread
-grouping (1..8 words per thread, 64..512 threads per tensor, 1..64 chunks),
-and the degenerate cases of the method.  All GPU work goes through the C ABI.
+grouping (tiles of 1..4 words per lane, groups of 64..1024 threads with 1..6
+words per thread, 1..64 chunks), and the degenerate cases of the method.
+Gathers from slots run both plain and with rows routed to XCDs.  All GPU work
+goes through the C ABI.
 """
 import numpy as np
 import pytest
@@ -27,11 +29,12 @@ def full_roundtrip(name, rows, C, T, sample_ids=None, slot=None, pinned=False, b
     o_store, o_part, o_len = G.check_store(rows, mask, bitval, C, slot, store, part, lengths)
     batches = batches or [rng.integers(0, n, 777), np.arange(n)[::-1].copy(), np.array([0, n - 1, 0])]
     for ids in batches:
-        got = G.gpu_gather(store, n * slot, slot, None, part, n, ids, B, C, mask, bitval)
-        want = G.expected_rows(rows, ids)
-        assert (got == want).all(), f"{name}: gather from slots is not the original rows"
         ora = O_gather(o_store, o_part, n, ids, B, C, mask, bitval, slot)
-        assert (got == ora).all(), f"{name}: gather differs from the oracle"
+        want = G.expected_rows(rows, ids)
+        for flags in (0, G.ROUTE):  # plain, and rows routed to XCDs by tensor
+            got = G.gpu_gather(store, n * slot, slot, None, part, n, ids, B, C, mask, bitval, flags)
+            assert (got == want).all(), f"{name}: gather from slots is not the original rows ({flags})"
+            assert (got == ora).all(), f"{name}: gather differs from the oracle ({flags})"
     # compacted HBM cache
     offsets = torch.zeros(n + 1, dtype=torch.int64, device="cuda")
     from host_transfer_amd import ibp
@@ -151,14 +154,37 @@ def test_batch_edges_and_invalid_ids():
     B, C, slot = w.tensor_bytes, w.chunk_bytes, w.slot_bytes
     mask, bitval = G.check_metadata(rows, w.threshold)
     store, part, lens = G.gpu_compress(rows, mask, bitval, C, slot)
-    for nb in (0, 1, 63, 64, 65, 255, 256, 257):
-        ids = (np.arange(nb) * 37) % 1000
-        got = G.gpu_gather(store, 1000 * slot, slot, None, part, 1000, ids, B, C, mask, bitval)
-        assert (got == rows[ids]).all(), nb
-    ids = np.array([5, -1, 1000, 999, 1 << 40, 5, 5])
-    got = G.gpu_gather(store, 1000 * slot, slot, None, part, 1000, ids, B, C, mask, bitval)
-    assert (got == G.expected_rows(rows, ids)).all()
-    assert not got[[1, 2, 4]].any()
+    for flags in (0, G.ROUTE):
+        for nb in (0, 1, 63, 64, 65, 255, 256, 257):
+            ids = (np.arange(nb) * 37) % 1000
+            got = G.gpu_gather(store, 1000 * slot, slot, None, part, 1000, ids, B, C, mask, bitval,
+                               flags)
+            assert (got == rows[ids]).all(), (nb, flags)
+        ids = np.array([5, -1, 1000, 999, 1 << 40, 5, 5])
+        got = G.gpu_gather(store, 1000 * slot, slot, None, part, 1000, ids, B, C, mask, bitval,
+                           flags)
+        assert (got == G.expected_rows(rows, ids)).all()
+        assert not got[[1, 2, 4]].any()
+
+
+def test_routed_zipf_repeats():
+    """Routed gathers of a batch that repeats a few tensors many times (the
+    case routing is for), tile and group kernels, device and pinned slots."""
+    rng = np.random.default_rng(5)
+    for key, n in (("dense_gnn", 3000), ("dlrm_2k", 1200), ("kv_opt13b", 300)):
+        w = W.WORKLOADS[key].scaled(n)
+        rows = W.rows(w, 0, n)
+        B, C, slot = w.tensor_bytes, w.chunk_bytes, w.slot_bytes
+        mask, bitval = G.check_metadata(rows, w.threshold)
+        for pinned in (False, True):
+            store, part, lens = G.gpu_compress(rows, mask, bitval, C, slot, pinned=pinned)
+            hot = rng.integers(0, n, 7)
+            ids = np.where(rng.random(5000) < 0.6, hot[rng.integers(0, 7, 5000)],
+                           rng.integers(-3, n + 3, 5000))
+            G.log(f"[parity] routed repeats {key}: n={n} pinned={pinned}")
+            got = G.gpu_gather(store, n * slot, slot, None, part, n, ids, B, C, mask, bitval,
+                               G.ROUTE)
+            assert (got == G.expected_rows(rows, ids)).all(), key
 
 
 def test_deterministic_and_store_bound():
