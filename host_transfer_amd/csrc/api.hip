@@ -92,6 +92,10 @@ hipError_t device_info(DeviceInfo* out) {
   return c.err;
 }
 
+#ifndef IBP_MAX_WORDS_PER_THREAD
+#define IBP_MAX_WORDS_PER_THREAD 6  // 1..6: registers per word bound J (see k_gather_decompress)
+#endif
+
 Geometry make_geometry(uint32_t tensor_bytes, uint32_t chunk_bytes) {
   Geometry g;
   g.tensor_bytes = tensor_bytes;
@@ -105,7 +109,7 @@ Geometry make_geometry(uint32_t tensor_bytes, uint32_t chunk_bytes) {
   // the per-word registers fit without spilling (and a payload of at most
   // B <= 24*G bytes fits in two 16 B registers per thread)
   g.group = 64;
-  while (g.group * 6 < g.W) g.group *= 2;
+  while (g.group * IBP_MAX_WORDS_PER_THREAD < g.W) g.group *= 2;
   g.J = (g.W + g.group - 1) / g.group;
   g.groups = g.group == 64 ? 4 : 1;
   return g;
