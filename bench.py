@@ -47,8 +47,8 @@ HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E
 # to GATHER_SOURCES_SHA256, else traffic is null.
 GATHER_SOURCES = ("host_transfer_amd/csrc/gather.hip", "host_transfer_amd/csrc/ibp_plan.h",
                   "host_transfer_amd/csrc/ibp_device.h")
-GATHER_SOURCES_SHA256 = "253ee320b6446b554bcfdde2c97c10fe00d2914e3cc2bba051ae7df4399a5dfd"
-TRAFFIC_FETCH_KIB, TRAFFIC_WRITE_KIB = 6161.0, 48339.0  # sparse_gnn, 8,192 ids
+GATHER_SOURCES_SHA256 = "9051c35832e42b7693a109c1c278daeabe4a865759152f01f6ad18aca125d13f"
+TRAFFIC_FETCH_KIB, TRAFFIC_WRITE_KIB = 6168.5, 48517.1  # sparse_gnn, 8,192 ids
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 
 
