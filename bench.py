@@ -385,7 +385,7 @@ def measure_workload(torch, ibp, W, key, T, where, host_flags, steps, warmup, wi
 
 def measure_hbm(torch, ibp, W, table, args, pr):
     """The gather kernel on a compacted HBM cache (the table's pinned store
-    compacted into HBM): Table-D batch and a large batch, with the
+    compacted into HBM): the workload's batch and a large batch, with the
     uncompressed HBM gather of the same ids beside it."""
     import numpy as np
     w = table.w
@@ -446,7 +446,7 @@ def measure_hbm(torch, ibp, W, table, args, pr):
 
 
 def measure_pinned(torch, ibp, W, key, flags, args, pr):
-    """A workload's Table-D batches from its pinned-host store, with the raw
+    """A workload's batches from its pinned-host store, with the raw
     GPU gather of the same rows from pinned memory beside it.  Returns the
     result and the table (still pinned)."""
     w = W.WORKLOADS[key]
@@ -798,8 +798,9 @@ def run_kv_step(torch, ibp, W, args, pr, pairs=None):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the gathered tensors are independent, see the design notes on sharding)",
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(gathered tensors are independent, so a batch would split across GPUs "
+              "with no exchange)",
               file=sys.stderr)
         sys.exit(2)
     import numpy as np
@@ -923,8 +924,8 @@ def main():
     del table, m
     torch.cuda.empty_cache()
 
-    # --- the other pinned-host configurations (their Table-D batches), then
-    #     the same tables compacted into HBM caches: the Table-D batch and a
+    # --- the other pinned-host workloads (their own batch sizes), then
+    #     the same tables compacted into HBM caches: the workload's batch and a
     #     large batch (1M ids) that fills the GPU
     result["pinned_path"] = []
     result["hbm_path"] = []

@@ -135,7 +135,7 @@ def test_fullsize_hbm_cache(key):
     offsets, cache, total = _hbm_cache(t)
     del t["store"]
     torch.cuda.empty_cache()
-    check_gather(t, W.batch_ids(w, 0), cache, total, offsets, rng, "Table-D batch")
+    check_gather(t, W.batch_ids(w, 0), cache, total, offsets, rng, "workload batch")
     big = np.concatenate([W.batch_ids(w, k) for k in range((1 << 20) // w.batch)])
     check_gather(t, big, cache, total, offsets, rng, "1M ids")
     t["raw"].free()
@@ -149,7 +149,7 @@ def test_fullsize_pinned(key):
     check_sampled_store(t, rng)
     for flags in (0, G.ROUTE):  # plain, and routed to XCDs (the bench's launch for Zipf ids)
         check_gather(t, W.batch_ids(w, 0), t["store"], w.n_tensors * w.slot_bytes, None, rng,
-                     "Table-D batch", flags)
+                     "workload batch", flags)
     t["raw"].free()
     t["store"].free()
 
