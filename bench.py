@@ -333,24 +333,35 @@ def cpu_baseline(table, batches_host, seconds):
         store = table.cache.cpu().numpy()
         offs = table.offsets.cpu().numpy().view(np.uint64)
     out = np.empty((w.batch, w.tensor_bytes), np.uint8)
-    rows = 0
-    t0 = time.perf_counter()
-    k = 0
-    while True:
-        ids = batches_host[k % len(batches_host)]
-        O.gather_decompress(store, part, w.n_tensors, ids, w.tensor_bytes, w.chunk_bytes,
-                            table.mask_host, table.bitval_host, slot_bytes=w.slot_bytes,
-                            offsets=offs, out=out)
-        rows += len(ids)
-        k += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or k >= 4 * len(batches_host):
-            break
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+    def run(limit):
+        rows, k = 0, 0
+        t0 = time.perf_counter()
+        while True:
+            ids = batches_host[k % len(batches_host)]
+            O.gather_decompress(store, part, w.n_tensors, ids, w.tensor_bytes, w.chunk_bytes,
+                                table.mask_host, table.bitval_host, slot_bytes=w.slot_bytes,
+                                offsets=offs, out=out)
+            rows += len(ids)
+            k += 1
+            el = time.perf_counter() - t0
+            if el >= limit or k >= 4 * len(batches_host):
+                return rows, k, el
+
+    # the oracle's OpenMP runtime: all host threads, then one
+    import ctypes
+    gomp = ctypes.CDLL("libgomp.so.1")
+    threads = gomp.omp_get_max_threads()
+    rows, k, el = run(seconds)
+    gomp.omp_set_num_threads(1)
+    rows1, k1, el1 = run(seconds / 3)
+    gomp.omp_set_num_threads(threads)
     return {"value": round(rows * w.tensor_bytes / el / 1e9, 4), "unit": "GB/s",
             "cores": threads, "kind": "oracle",
             "sample": f"{k} batches of {w.batch} ids ({rows} rows) of the timed id sequence, "
-                      f"{el:.1f} s"}
+                      f"{el:.1f} s",
+            "value_1_thread": round(rows1 * w.tensor_bytes / el1 / 1e9, 4),
+            "sample_1_thread": f"{k1} batches ({rows1} rows), {el1:.1f} s"}
 
 
 def measure_workload(torch, ibp, W, key, T, where, host_flags, steps, warmup, with_raw):
