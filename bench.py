@@ -42,22 +42,35 @@ HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E
 
 # HBM/host traffic of the headline launch from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE (KiB per dispatch), scaled by what the same counters read for
-# transfers of known size (factors below).  Valid only for the gather sources
-# they were measured on: bench.py reports them while the sources still hash
-# to GATHER_SOURCES_SHA256, else traffic is null.
+# transfers of known size (factors below).  Valid only for the gather code
+# they were measured on: bench.py reports them while the sources (comments
+# and spacing aside) still hash to GATHER_SOURCES_SHA256, else traffic is null.
 GATHER_SOURCES = ("host_transfer_amd/csrc/gather.hip", "host_transfer_amd/csrc/ibp_plan.h",
                   "host_transfer_amd/csrc/ibp_device.h")
-GATHER_SOURCES_SHA256 = "9051c35832e42b7693a109c1c278daeabe4a865759152f01f6ad18aca125d13f"
+GATHER_SOURCES_SHA256 = "bc1481ec5af0cee02c996d661f874ab153a8ab011cb4fda7bf27739d9818bcaa"
 TRAFFIC_FETCH_KIB, TRAFFIC_WRITE_KIB = 6168.5, 48517.1  # sparse_gnn, 8,192 ids
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 
 
-def gather_sources_sha256():
+def code_text(src):
+    """C++ source without comments and with runs of whitespace collapsed, so
+    that only changes to the code itself change its hash."""
+    import re
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
+def gather_sources_sha256(read=None):
     import hashlib
     h = hashlib.sha256()
     for rel in GATHER_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        if read is None:
+            with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+                text = f.read()
+        else:
+            text = read(rel)
+        h.update(code_text(text).encode())
     return h.hexdigest()
 
 

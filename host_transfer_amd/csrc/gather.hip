@@ -5,25 +5,34 @@
 // then every thread re-inserts the invariant bits on its own, with fetches
 // overlapped with decoding.  [JH] decompression paragraph: one thread per
 // chunk, no cross-warp synchronisation; transfer paragraph: GPU-initiated
-// 128 B-aligned reads of host memory.  On gfx950 a group of G = 64..512
-// threads (one or more wave64s) handles one tensor at a time:
-//   1. the first wave reads the tensor's id and participation bits (lane c
-//      owns chunk c, n_c <= 64); a wave scan gives each chunk's bit offset in
-//      the payload and the payload length;
+// 128 B-aligned reads of host memory.
+//
+// On gfx950 there are two kernels, chosen by the tensor size W (words):
+//
+// k_gather_decompress (W > 256): a group of G = 64..1024 threads (one or more
+// wave64s, G the smallest with W <= 6 G) handles one tensor at a time:
+//   1. the first wave reads the tensor's participation bits (lane c owns
+//      chunk c, n_c <= 64); a wave scan gives each chunk's bit offset in the
+//      payload and the payload length;
 //   2. the group loads the payload (whole 16 B units from a 16 B-aligned
 //      start, so every 128 B line is read once) from the host-mapped slot or
 //      the HBM cache into registers, then LDS;
 //   3. each thread decodes its own words: a 64-bit window of the payload at
 //      the word's bit offset (two LDS words and v_alignbit), unpack with the
 //      word's move masks, insert Bitval; raw chunks take the window as is;
-//   4. coalesced 4 B stores of the dense row (consecutive lanes, consecutive
-//      words).
+//   4. coalesced streaming stores of the dense row.
 // Software pipeline per group: while tensor i is decoded, the payload loads of
-// tensor i+1 are in flight, and while tensor i's payload arrives the first
-// wave fetches and scans the id and participation bits of tensor i+1.  A
-// payload is at most B <= 24*G bytes (at most 6 words per thread), so it
+// tensor i+1 are in flight, and the ids and participation words of tensors
+// i+2 and i+3 are loaded ahead.  A payload is at most B <= 24*G bytes, so it
 // fits in two 16 B registers per thread.  Workgroup barriers only wait for
 // LDS traffic, so global loads stay in flight across them.
+//
+// k_gather_tile (W <= 256): one wave decodes a tile of T small tensors at a
+// time (see its comment), with the same pipeline across tiles.
+//
+// Both have a routed variant (k_gather_decompress_routed, k_gather_tile_routed)
+// that sends every row to the XCD its tensor hashes to, for batches that
+// repeat ids (see k_gather_tile_routed).
 #include "ibp_internal.h"
 #include "ibp_plan.h"
 
