@@ -575,7 +575,7 @@ __device__ __forceinline__ void unpack_stages_n(uint32_t (&x)[N], const uint32_t
 }
 
 #ifndef IBP_TILE_GROUP
-#define IBP_TILE_GROUP 8  // tensors of a full tile decoded side by side
+#define IBP_TILE_GROUP 8  // tensors of a full tile decoded side by side (4 when J >= 4)
 #endif
 #ifndef IBP_BIG_NL
 #define IBP_BIG_NL 8      // load instructions per tile on large batches
@@ -596,7 +596,8 @@ __device__ __forceinline__ void decode_full_tile(const GatherArgs& a, const Word
                                                  uint32_t lane, uint64_t row0, uint32_t trow = 0) {
   constexpr uint32_t kW = (uint32_t)kWave * J;  // words per tensor
   constexpr uint32_t kSlot = 4u * kW + 16u;     // LDS bytes per tensor
-  constexpr int TG = T < IBP_TILE_GROUP ? T : IBP_TILE_GROUP;  // tensors decoded side by side
+  constexpr int TGmax = J >= 4 && IBP_TILE_GROUP > 4 ? 4 : IBP_TILE_GROUP;  // registers of J words
+  constexpr int TG = T < TGmax ? T : TGmax;  // tensors decoded side by side
   const TileHdr& hl = hcur[lane & (uint32_t)(T - 1)];
   const uint32_t hpm = hl.pmask, ho1 = hl.off[0], ho2 = hl.off[1], ho3 = hl.off[2];
   uint32_t* obase = a.out + row0 * kW + lane;
