@@ -47,8 +47,8 @@ HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E
 # and spacing aside) still hash to GATHER_SOURCES_SHA256, else traffic is null.
 GATHER_SOURCES = ("host_transfer_amd/csrc/gather.hip", "host_transfer_amd/csrc/ibp_plan.h",
                   "host_transfer_amd/csrc/ibp_device.h")
-GATHER_SOURCES_SHA256 = "bc1481ec5af0cee02c996d661f874ab153a8ab011cb4fda7bf27739d9818bcaa"
-TRAFFIC_FETCH_KIB, TRAFFIC_WRITE_KIB = 6168.5, 48517.1  # sparse_gnn, 8,192 ids
+GATHER_SOURCES_SHA256 = "2e913997e33047ec26a6360dfd45a995f95d1e2d0eec74070b47bc019e003939"
+TRAFFIC_FETCH_KIB, TRAFFIC_WRITE_KIB = 6168.5, 48514.0  # sparse_gnn, 8,192 ids
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 
 
