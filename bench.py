@@ -239,6 +239,17 @@ class Table:
                                  w.chunk_bytes, self.mask, self.bitval, out, flags)
 
 
+def percentiles_us(ms):
+    """mean, min, p10, median, p90, max of launch times given in ms, in us."""
+    q = sorted(ms)
+
+    def at(f):
+        return q[min(len(q) - 1, int(round(f * (len(q) - 1))))]
+    return {"mean": round(statistics.mean(q) * 1e3, 2), "min": round(q[0] * 1e3, 2),
+            "p10": round(at(0.1) * 1e3, 2), "median": round(statistics.median(q) * 1e3, 2),
+            "p90": round(at(0.9) * 1e3, 2), "max": round(q[-1] * 1e3, 2), "launches": len(q)}
+
+
 def region_launches(torch, fn, warmup, steps):
     """`steps` launches back to back after `warmup`, bracketed by one pair of
     HIP events on the launch stream and by synchronisations.  Returns (mean ms
@@ -810,7 +821,8 @@ def run_kv_step(torch, ibp, W, args, pr, pairs=None):
            "frac_of_link_peak": round(comp / (ibp_ms * 1e-3) / 1e9 / link, 4),
            "raw_step_ms": round(raw_ms, 3), "speedup_vs_raw": round(raw_ms / ibp_ms, 3),
            "prefill_mask_ms_per_pair": round(statistics.mean(meta_ms), 3),
-           "prefill_mask_ms_per_step": round(sum(meta_ms), 2),
+           "prefill_mask_ms_all_pairs": round(sum(meta_ms), 2),
+           "prefill_mask_over_decode_fetch": round(sum(meta_ms) / (W.KV_DECODE * ibp_ms), 4),
            "prefill_rows_per_pair": W.KV_PREFILL_ROWS,
            "compress_on_write_us_per_token": round(statistics.median(write_ms) * 1e3, 1),
            "device": torch.cuda.get_device_name(0)}
@@ -899,9 +911,7 @@ def main():
             "frac_of_zero_copy_read": round(achieved / pr["h2d_zero_copy_read_GBps"], 4),
             "kernel": "k_gather_decompress",
             "kernel_us": round(kern_ms * 1e3, 2),
-            "isolated_launch_us": {"mean": round(statistics.mean(m["isolated_ms"]) * 1e3, 2),
-                                   "min": round(min(m["isolated_ms"]) * 1e3, 2),
-                                   "max": round(max(m["isolated_ms"]) * 1e3, 2)},
+            "isolated_launch_us": percentiles_us(m["isolated_ms"]),
             "bytes_per_launch": round(comp, 1),
             "unique_bytes_per_launch": round(uniq, 1),
             "unique_frac_of_measured": round(uniq / (kern_ms * 1e-3) / 1e9 / link_peak, 4),
