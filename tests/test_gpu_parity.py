@@ -167,6 +167,27 @@ def test_batch_edges_and_invalid_ids():
         assert not got[[1, 2, 4]].any()
 
 
+@pytest.mark.parametrize("flags", [0, 1, 2])  # IBP_HOST_DEFAULT, _COHERENT, _NONCOHERENT
+def test_host_store_flags(flags):
+    """Compression into, and gathers from, pinned stores of every host
+    allocation kind (the GPU writes and reads them over PCIe)."""
+    from host_transfer_amd import ibp
+    w = W.WORKLOADS["sparse_gnn"].scaled(800)
+    rows = W.rows(w)
+    B, C, slot = w.tensor_bytes, w.chunk_bytes, w.slot_bytes
+    mask, bitval = G.check_metadata(rows, 0.95)
+    store = ibp.HostBuffer(800 * slot, flags)
+    store.array[:] = 0xA5
+    G.log(f"[parity] host store flags {flags}")
+    store, part, lens = G.gpu_compress(rows, mask, bitval, C, slot, store=store)
+    G.check_store(rows, mask, bitval, C, slot, store, part, lens)
+    ids = np.random.default_rng(flags).integers(0, 800, 1000)
+    for route in (0, G.ROUTE):
+        got = G.gpu_gather(store, 800 * slot, slot, None, part, 800, ids, B, C, mask, bitval, route)
+        assert (got == rows[ids]).all(), (flags, route)
+    store.free()
+
+
 def test_routed_zipf_repeats():
     """Routed gathers of a batch that repeats a few tensors many times (the
     case routing is for), tile and group kernels, device and pinned slots."""
