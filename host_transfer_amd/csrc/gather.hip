@@ -677,7 +677,11 @@ __global__ __launch_bounds__(256) void k_gather_tile(GatherArgs a) {
   const TileMeta m0 = load_tile_meta(a, id_a);
 
   load_plan_counts(run, a.sh, s_pref, s_kc, s_wsum);
-  if (tile0 >= n_tiles) return;  // per wave; no workgroup barrier follows
+  // short batches (NL == 2: a tile or two per wave) build the per-word plan
+  // once per workgroup (load_plan_words_shared, a barrier below), so idle
+  // waves stay until then
+  constexpr bool kSharedPlan = NL == 2;
+  if (!kSharedPlan && tile0 >= n_tiles) return;  // per wave; no workgroup barrier follows
 
   TileMeta meta_next = load_tile_meta(a, id_b);
   if (lane < (uint32_t)T) hdrs[lane] = make_tile_hdr(a, m0, s_kc);
@@ -710,7 +714,15 @@ __global__ __launch_bounds__(256) void k_gather_tile(GatherArgs a) {
   }
   IBP_TILE_ISSUE_LOADS(hdrs)
 
-  load_plan_words<J>(a.sh, s_pref, lane, R);
+  if constexpr (kSharedPlan) {
+    uint32_t* s_mv = (uint32_t*)(smem + L.group0 +
+                                 (blockDim.x / kWave) *
+                                     (2 * T * (uint32_t)sizeof(TileHdr) + T * a.pbuf_bytes));
+    load_plan_words_shared<J>(a.sh, s_pref, lane, wave, R, s_mv);
+    if (tile0 >= n_tiles) return;  // per wave; no workgroup barrier follows
+  } else {
+    load_plan_words<J>(a.sh, s_pref, lane, R);
+  }
 
   uint32_t cur = 0;
   for (uint64_t tile = tile0; tile < n_tiles; tile += waves, cur ^= 1u) {
@@ -786,7 +798,9 @@ static hipError_t launch_tile(const Geometry& g, GatherArgs a, hipStream_t s) {
   a.sh.group = kWave;  // lane l owns words l + 64j
   const uint32_t waves = 4;
   const GatherLds L(g.W, a.pbuf_bytes);
-  const uint32_t lds = L.group0 + waves * (2 * T * (uint32_t)sizeof(TileHdr) + T * a.pbuf_bytes);
+  const uint32_t shared_plan = T / RPI == 2 ? 20u * g.W : 0u;  // move masks, see k_gather_tile
+  const uint32_t lds = L.group0 + waves * (2 * T * (uint32_t)sizeof(TileHdr) + T * a.pbuf_bytes) +
+                       shared_plan;
   DeviceInfo di;
   hipError_t e = device_info(&di);
   if (e != hipSuccess) return e;

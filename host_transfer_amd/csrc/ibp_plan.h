@@ -163,6 +163,52 @@ __device__ void load_plan_words(const Shape& sh, const uint32_t* s_pref, uint32_
   }
 }
 
+// load_plan_words for a workgroup of four waves that all own the same words
+// (lane l: words l + 64 j, j < J <= 4, as in the tile kernel): wave k
+// computes the move masks of word position j = k from the Mask words it holds
+// and shares them through LDS (s_mv: 5 * W words), so each wave does a
+// quarter of that arithmetic.  Contains a workgroup barrier: every thread of
+// the workgroup must call it.
+template <int J>
+__device__ void load_plan_words_shared(const Shape& sh, const uint32_t* s_pref, uint32_t lane,
+                                       uint32_t wave, WordRegs<J>& R, uint32_t* s_mv) {
+  static_assert(J <= 4, "one word position per wave of four");
+  const uint32_t W = sh.W;
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const uint32_t w = lane + (uint32_t)kWave * j;
+    if (wave == (uint32_t)j && w < W) {
+      uint32_t mv[5];
+      move_masks(~R.mask[j], mv);
+#pragma unroll
+      for (int q = 0; q < 5; ++q) s_mv[q * W + w] = mv[q];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const uint32_t w = lane + (uint32_t)kWave * j;
+    if (w < W) {
+      const uint32_t m = R.mask[j];
+#pragma unroll
+      for (int q = 0; q < 5; ++q) R.mv[j][q] = s_mv[q * W + w];
+      R.bitval[j] &= m;
+      const uint32_t first = (w >> sh.wpc_log2) << sh.wpc_log2;
+      R.info[j] = (s_pref[w] - s_pref[first]) | ((32u * (w - first)) << 16);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 5; ++q) R.mv[j][q] = 0;
+      R.mask[j] = 0;
+      R.bitval[j] = 0;
+      R.info[j] = 0;
+    }
+    uint32_t st = 0;
+#pragma unroll
+    for (int q = 0; q < 5; ++q) st |= (__ballot(R.mv[j][q] != 0u) != 0ull ? 1u : 0u) << q;
+    R.stages[j] = uniform(st);
+  }
+}
+
 // Synchronises the threads of one group: a wave, or the whole workgroup.
 __device__ __forceinline__ void group_sync(bool single_wave) {
   if (single_wave)
