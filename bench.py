@@ -21,7 +21,7 @@ discussion: transfer speedup against plain transfers).
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sparse_gnn]
        [--pinned-workloads dense_gnn,dlrm_1k,dlrm_2k|none] [--kv-pairs-default 8]
        [--hbm-workloads dense_gnn,dlrm_1k|none] [--hbm-large-batch N]
-       [--mode default|ablation|sweep|kv-step]
+       [--mode default|ablation|sweep|kv-step|configs]
        [--host-flags default|coherent|noncoherent] [--no-cpu-baseline] [--threshold T]
 """
 import argparse
@@ -47,8 +47,8 @@ HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E
 # and spacing aside) still hash to GATHER_SOURCES_SHA256, else traffic is null.
 GATHER_SOURCES = ("host_transfer_amd/csrc/gather.hip", "host_transfer_amd/csrc/ibp_plan.h",
                   "host_transfer_amd/csrc/ibp_device.h")
-GATHER_SOURCES_SHA256 = "2e913997e33047ec26a6360dfd45a995f95d1e2d0eec74070b47bc019e003939"
-TRAFFIC_FETCH_KIB, TRAFFIC_WRITE_KIB = 6168.5, 48514.0  # sparse_gnn, 8,192 ids
+GATHER_SOURCES_SHA256 = "1a1f38c082b819d471622f6739c1df5fc740c1ec0eb95ad0634e6e05b93820c8"
+TRAFFIC_FETCH_KIB, TRAFFIC_WRITE_KIB = 6163.0, 48475.7  # sparse_gnn, 8,192 ids
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 
 
@@ -98,10 +98,12 @@ def parse():
     p.add_argument("--threshold", type=float, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
-    p.add_argument("--mode", default="default", choices=["default", "ablation", "sweep", "kv-step"],
+    p.add_argument("--mode", default="default",
+                   choices=["default", "ablation", "sweep", "kv-step", "configs"],
                    help="default: the headline and the cache paths; ablation: transfer methods "
                         "for small random tensors; sweep: throughput against space saving and "
-                        "chunk size; kv-step: the online OPT-13B K/V path")
+                        "chunk size; kv-step: the online OPT-13B K/V path; configs: one row per "
+                        "workload (oracle on 1 and all threads, GPU from pinned memory and HBM)")
     p.add_argument("--kv-pairs", type=int, default=80, help="(layer, K|V) pairs in --mode kv-step")
     p.add_argument("--pinned-workloads", default="dense_gnn,dlrm_1k,dlrm_2k",
                    help="other workloads measured from pinned host memory, or 'none'")
@@ -831,6 +833,117 @@ def run_kv_step(torch, ibp, W, args, pr, pairs=None):
     return res
 
 
+def run_configs(torch, ibp, W, args, pr):
+    """One row per workload: space saving, the oracle on one thread and on all
+    host threads, the GPU gather from pinned memory (against the link) and,
+    for the cache workloads, from a compacted HBM cache (against 8 TB/s)."""
+    import numpy as np
+    from oracle import oracle as O
+    link = max(pr["h2d_dma_GBps"], pr["h2d_zero_copy_read_GBps"])
+    steps, warmup = max(5, min(args.steps, 30)), max(2, min(args.warmup, 5))
+    rows_out = []
+    for key in ("tiny", "sparse_gnn", "dense_gnn", "dlrm_1k", "dlrm_2k"):
+        w = W.WORKLOADS[key]
+        m = measure_workload(torch, ibp, W, key, None, "pinned", args.host_flags_value, steps,
+                             warmup, with_raw=False)
+        t = m["table"]
+        B = w.tensor_bytes
+        km = m["kernel_ms"]
+        comp = statistics.mean(m["comp_bytes"])
+        uniq = statistics.mean(float(t.len_host[np.unique(i)].sum()) for i in m["ids_host"][warmup:])
+        cpu = cpu_baseline(t, m["ids_host"][warmup:], 3.0)
+        r = {"config": key, "tensor_bytes": B, "batch": w.batch,
+             "space_saving": round(1.0 - float(t.len_host.mean()) / B, 4),
+             "oracle_1_thread_GBps": cpu["value_1_thread"], "oracle_all_GBps": cpu["value"],
+             "oracle_threads": cpu["cores"],
+             "gpu_pinned_GBps": round(w.batch * B / (km * 1e-3) / 1e9, 2),
+             "pcie_frac_all_ids": round(comp / (km * 1e-3) / 1e9 / link, 4),
+             "pcie_frac_unique": round(uniq / (km * 1e-3) / 1e9 / link, 4),
+             "xcd_routed": m["routed"]}
+        if key in ("tiny", "dense_gnn", "dlrm_1k"):
+            t.to_hbm(torch, ibp)
+            for nb, tag in ((w.batch, ""), (args.hbm_large_batch, "_1M_ids")):
+                if tag and key == "tiny":
+                    continue
+                nbatches = (nb + w.batch - 1) // w.batch
+                n_seq = warmup + steps
+                seqs = [np.concatenate([W.batch_ids(w, k * nbatches + i)
+                                        for i in range(nbatches)])[:nb] for k in range(n_seq)]
+                d = [torch.from_numpy(i).cuda() for i in seqs]
+                out = torch.empty(nb * B, dtype=torch.uint8, device="cuda")
+                hm, _ = region_launches(torch, lambda k: t.gather(ibp, d[k], nb, out), warmup,
+                                        steps)
+                hc = statistics.mean(float(t.len_host[i].sum()) for i in seqs[warmup:])
+                traffic = hc + nb * (B + 16)
+                r["gpu_hbm" + tag + "_GBps"] = round(nb * B / (hm * 1e-3) / 1e9, 1)
+                r["hbm" + tag + "_frac"] = round(traffic / (hm * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
+                del out, d
+            if key == "tiny":
+                r["note"] = "the 1.8 MB cache fits the 256 MB last-level cache: a latency point"
+        if t.raw is not None:
+            t.raw.free()
+        if isinstance(t.store, ibp.HostBuffer):
+            t.store.free()
+        del t, m
+        torch.cuda.empty_cache()
+        rows_out.append(r)
+        log(f"configs: {r}")
+    # K/V: one (layer, K|V) pair, Mask from its prefill rows, its 2,560 decode rows
+    w = W.WORKLOADS["kv_opt13b"]
+    B, C, S, R = w.tensor_bytes, w.chunk_bytes, w.slot_bytes, W.KV_ROWS_PER_PAIR
+    pre = torch.from_numpy(W.kv_prefill_rows(w, 0)).cuda()
+    mask = torch.zeros(B // 4, dtype=torch.int32, device="cuda")
+    bitval = torch.zeros_like(mask)
+    counts = torch.zeros(8 * B, dtype=torch.int32, device="cuda")
+    ibp.build_metadata(pre, B, None, pre.shape[0], B, w.threshold, mask, bitval, counts)
+    del pre
+    raw = ibp.HostBuffer(R * S)
+    W.rows(w, 0, R, out=raw.array.reshape(R, S)[:, :B])
+    store = ibp.HostBuffer(R * S)
+    part = torch.zeros((R * ibp.num_chunks(B, C) + 31) // 32, dtype=torch.int32, device="cuda")
+    lengths = torch.zeros(R, dtype=torch.int32, device="cuda")
+    ibp.compress(raw, S, R, 0, R, B, C, mask, bitval, store, S, part, lengths)
+    ids = np.arange(R, dtype=np.int64)
+    d = torch.from_numpy(ids).cuda()
+    out = torch.empty(R * B, dtype=torch.uint8, device="cuda")
+    km, _ = region_launches(torch, lambda k: ibp.gather_decompress(
+        store, R * S, S, None, part, R, d, R, B, C, mask, bitval, out), warmup, steps)
+    if not (out.view(R, B)[::97].cpu().numpy() == raw.array.reshape(R, S)[::97, :B]).all():
+        raise SystemExit("bench: kv_opt13b gather is not lossless")
+    len_h = lengths.cpu().numpy().view(np.uint32)
+    comp = float(len_h.astype(np.float64).sum())
+    part_h, mask_h, bitval_h = (x.cpu().numpy().view(np.uint32) for x in (part, mask, bitval))
+    import ctypes
+    gomp = ctypes.CDLL("libgomp.so.1")
+    threads = gomp.omp_get_max_threads()
+    rates = {}
+    for nt in (threads, 1):
+        gomp.omp_set_num_threads(nt)
+        t0 = time.perf_counter()
+        k = 0
+        while True:
+            O.gather_decompress(store.array, part_h, R, ids, B, C, mask_h, bitval_h, slot_bytes=S)
+            k += 1
+            el = time.perf_counter() - t0
+            if el >= 2.0 or k >= 20:
+                break
+        rates[nt] = round(k * R * B / el / 1e9, 4)
+    gomp.omp_set_num_threads(threads)
+    rows_out.append({"config": "kv_opt13b", "tensor_bytes": B, "batch": R,
+                     "space_saving": round(1.0 - float(len_h.mean()) / B, 4),
+                     "oracle_1_thread_GBps": rates[1], "oracle_all_GBps": rates[threads],
+                     "oracle_threads": threads,
+                     "gpu_pinned_GBps": round(R * B / (km * 1e-3) / 1e9, 2),
+                     "pcie_frac_all_ids": round(comp / (km * 1e-3) / 1e9 / link, 4),
+                     "pcie_frac_unique": round(comp / (km * 1e-3) / 1e9 / link, 4),
+                     "xcd_routed": False})
+    raw.free()
+    store.free()
+    return {"metric": "per-workload gather + decompress: oracle and GPU", "unit": "GB/s",
+            "higher_is_better": True, "link_peak_GBps": link, "hbm_peak_GBps": HBM_PEAK_GBPS,
+            "configs": rows_out, "device": torch.cuda.get_device_name(0), "host": host_info()}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -856,6 +969,10 @@ def main():
         return run_sweep(torch, ibp, args, pr)
     if args.mode == "kv-step":
         print(json.dumps(run_kv_step(torch, ibp, W, args, pr)), flush=True)
+        return
+    if args.mode == "configs":
+        args.host_flags_value = flags
+        print(json.dumps(run_configs(torch, ibp, W, args, pr)), flush=True)
         return
 
     # --- headline: the workload from pinned host memory
