@@ -206,6 +206,15 @@ def test_routed_zipf_repeats():
             got = G.gpu_gather(store, n * slot, slot, None, part, n, ids, B, C, mask, bitval,
                                G.ROUTE)
             assert (got == G.expected_rows(rows, ids)).all(), key
+        # one tensor in every row (spread over all XCDs), and invalid ids whose
+        # low 32 bits equal a valid id's
+        one = np.full(3001, n // 2)
+        coll = np.where(np.arange(3001) % 3 == 0, n // 2 + (1 << 32), one)
+        for ids in (one, coll):
+            G.log(f"[parity] routed single tensor {key}: {len(ids)} ids")
+            got = G.gpu_gather(store, n * slot, slot, None, part, n, ids, B, C, mask, bitval,
+                               G.ROUTE)
+            assert (got == G.expected_rows(rows, ids)).all(), key
 
 
 def test_deterministic_and_store_bound():
