@@ -374,6 +374,8 @@ int ibp_raw_gather(const void* src, uint64_t row_stride, uint64_t n_rows, const 
   if (!src || !ids || !out) return fail(IBP_ERR_NULL, "ibp_raw_gather: src, ids and out are required");
   if (row_bytes == 0 || row_bytes % 4 != 0 || row_stride < row_bytes || row_stride % 4 != 0)
     return fail(IBP_ERR_SIZE, "ibp_raw_gather: row_bytes %% 4, row_stride >= row_bytes and %% 4");
+  if (n_rows > UINT64_MAX / row_stride || n_ids > UINT64_MAX / row_bytes)
+    return fail(IBP_ERR_SIZE, "ibp_raw_gather: n_rows * row_stride or n_ids * row_bytes overflows");
   if (!aligned(src, 4) || !aligned(out, 4) || !aligned(ids, 8))
     return fail(IBP_ERR_ALIGN, "ibp_raw_gather: misaligned pointer");
   if (flags & ~IBP_RAW_ROUTE_XCD) return fail(IBP_ERR_FLAGS, "ibp_raw_gather: unknown flags");

@@ -287,8 +287,9 @@ int ibp_host_free(void *ptr);
  * flags: 0, or IBP_RAW_ROUTE_XCD: each row is copied by a wave on the XCD
  * chosen by a hash of its id, as ibp_gather_decompress_ex does with
  * IBP_GATHER_ROUTE_XCD (repeated ids then share one XCD's L2); same output;
- * requires n_ids < 2^32.  Errors: NULL pointers, sizes, alignment, unknown
- * flags, n_ids too large for routing. */
+ * requires n_ids < 2^32.  Errors: NULL pointers, sizes (including
+ * n_rows*row_stride or n_ids*row_bytes past 2^64), alignment, unknown flags,
+ * n_ids too large for routing. */
 #define IBP_RAW_ROUTE_XCD 1u
 int ibp_raw_gather(const void *src, uint64_t row_stride, uint64_t n_rows,
                    const int64_t *ids, uint64_t n_ids, uint32_t row_bytes,

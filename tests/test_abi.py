@@ -125,6 +125,8 @@ def test_other_validation(ibp):
     _expect(ibp, ibp.ERR_SIZE, ibp.raw_gather, P, 514, 10, P, 4, 512, P)
     _expect(ibp, ibp.ERR_ALIGN, ibp.raw_gather, P + 2, 512, 10, P, 4, 512, P)
     _expect(ibp, ibp.ERR_FLAGS, ibp.raw_gather, P, 512, 10, P, 4, 512, P, 2)
+    _expect(ibp, ibp.ERR_SIZE, ibp.raw_gather, P, 512, 1 << 56, P, 4, 512, P)
+    _expect(ibp, ibp.ERR_SIZE, ibp.raw_gather, P, 512, 10, P, 1 << 56, 512, P)
     _expect(ibp, ibp.ERR_SIZE, ibp.raw_gather, P, 512, 10, P, 1 << 32, 512, P,
             ibp.RAW_ROUTE_XCD)
     _expect(ibp, ibp.ERR_SIZE, ibp.stream_read, P, 100, 0, P)
