@@ -271,6 +271,40 @@ def region_launches(torch, fn, warmup, steps):
     return a.elapsed_time(b) / steps, wall
 
 
+def graph_launches(torch, fn, k, reps):
+    """Launches fn(0..k-1) captured in one HIP graph and replayed `reps` times,
+    against the same k launches issued eagerly `reps` times (the same id
+    buffers both ways, so caches see the same reuse): mean us per launch."""
+    for i in range(k):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(k):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+
+    def region(body):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            body()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / (reps * k)
+
+    def eager():
+        for i in range(k):
+            fn(i)
+    graph_us = region(g.replay)
+    eager_us = region(eager)
+    del g
+    return {"launches": k, "replays": reps, "graph_us_per_launch": round(graph_us, 2),
+            "eager_us_per_launch": round(eager_us, 2)}
+
+
 def time_gather(torch, ibp, table, batches, warmup, steps, out, raw_baseline=False, raw_flags=0,
                 flags=0):
     """The timed region (`steps` launches back to back), then the same
@@ -453,6 +487,9 @@ def measure_hbm(torch, ibp, W, table, args, pr):
         km, _ = region_launches(torch, run_ibp, args.warmup, steps)
         rm, _ = region_launches(torch, run_raw, args.warmup, steps)
         kiso = statistics.mean(timed_launches(torch, run_ibp, 0, steps))
+        graph = None
+        if nb == w.batch:
+            graph = graph_launches(torch, run_ibp, min(16, len(d)), max(3, steps // 4))
         last = seqs[-1]
         run_ibp(len(seqs) - 1)
         torch.cuda.synchronize()
@@ -475,6 +512,8 @@ def measure_hbm(torch, ibp, W, table, args, pr):
             "speedup_vs_raw_hbm_gather": round(rm / km, 3),
             "unique_ids": int(len(np.unique(last))),
         })
+        if graph is not None:
+            res["batches"][-1]["hip_graph"] = graph
         del out, d
     res["compact_ms"] = round(table.compact_ms, 3)
     del raw_dev

@@ -217,6 +217,62 @@ def test_routed_zipf_repeats():
             assert (got == G.expected_rows(rows, ids)).all(), key
 
 
+def test_side_stream_and_graph_replay():
+    """Gathers launched on a side stream, and gathers captured in a HIP graph
+    and replayed with the captured ids buffer refilled in between (eager work
+    and synchronisations between replays): tile kernel (dense_gnn) and group
+    kernel (sparse_gnn), from slots and from a compacted cache.  Every replay
+    is checked against an eager launch of the same ids and the original rows."""
+    from host_transfer_amd import ibp
+    rng = np.random.default_rng(11)
+    for key, n in (("dense_gnn", 3000), ("sparse_gnn", 1500)):
+        w = W.WORKLOADS[key].scaled(n)
+        rows = W.rows(w)
+        B, C, slot = w.tensor_bytes, w.chunk_bytes, w.slot_bytes
+        mask, bitval = G.check_metadata(rows, w.threshold)
+        store, part, lens = G.gpu_compress(rows, mask, bitval, C, slot)
+        offsets = torch.zeros(n + 1, dtype=torch.int64, device="cuda")
+        ibp.compact_offsets(lens, n, offsets)
+        total = int(offsets[-1].item())
+        cache = torch.zeros(max(total, 16), dtype=torch.uint8, device="cuda")
+        ibp.compact(store, slot, n, offsets, cache, total)
+        d_mask, d_bitval = G.dev(mask), G.dev(bitval)
+        nb = 700
+        ids = torch.zeros(nb, dtype=torch.int64, device="cuda")
+        out = torch.zeros(nb * B, dtype=torch.uint8, device="cuda")
+        ref = torch.zeros_like(out)
+        sources = (("slots", store, n * slot, slot, None), ("cache", cache, total, 0, offsets))
+        for name, src, src_bytes, sb, offs in sources:
+            def launch(dst):
+                ibp.gather_decompress(src, src_bytes, sb, offs, part, n, ids, nb, B, C, d_mask,
+                                      d_bitval, dst)
+            G.log(f"[parity] side stream + graph {key} from {name}")
+            batch = rng.integers(0, n, nb)
+            ids.copy_(torch.from_numpy(batch))
+            torch.cuda.synchronize()
+            side = torch.cuda.Stream()
+            with torch.cuda.stream(side):
+                launch(out)
+            side.synchronize()
+            assert (G.host(out).reshape(nb, B) == rows[batch]).all(), (key, name, "side stream")
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                launch(out)
+            torch.cuda.synchronize()
+            for rep in range(3):
+                batch = rng.integers(-2, n + 2, nb)
+                ids.copy_(torch.from_numpy(batch))
+                out.fill_(0x5A)
+                launch(ref)  # eager launch of the same ids
+                torch.cuda.synchronize()
+                graph.replay()
+                torch.cuda.synchronize()
+                got = G.host(out).reshape(nb, B)
+                assert (got == G.host(ref).reshape(nb, B)).all(), (key, name, rep, "eager")
+                assert (got == G.expected_rows(rows, batch)).all(), (key, name, rep)
+            del graph
+
+
 def test_deterministic_and_store_bound():
     w = W.WORKLOADS["dense_gnn"].scaled(2000)
     rows = W.rows(w)
