@@ -375,8 +375,22 @@ def probes(torch, ibp, host_flags):
     hbm = 4 * GiB / (statistics.median(tm.ms()) * 1e-3) / 1e9
     del big, dst
     torch.cuda.empty_cache()
+    # HBM copy, 2 GiB to 2 GiB (reads and writes together, like a gather):
+    # bytes read + bytes written per second
+    a = torch.ones(2 * GiB, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    tm = Timer(torch)
+    for _ in range(10):
+        s = tm.start()
+        b.copy_(a)
+        tm.stop(s)
+    copy = 4 * GiB / (statistics.median(tm.ms()) * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
     return {"h2d_dma_GBps": round(dma, 2), "h2d_zero_copy_read_GBps": round(zc, 2),
-            "hbm_stream_read_GBps": round(hbm, 1)}
+            "hbm_stream_read_GBps": round(hbm, 1), "hbm_copy_read_plus_write_GBps": round(copy, 1)}
 
 
 def cpu_baseline(table, batches_host, seconds):
@@ -507,7 +521,9 @@ def measure_hbm(torch, ibp, W, table, args, pr):
                          "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": round(traffic / (km * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                          "frac_of_measured_read": round(traffic / (km * 1e-3) / 1e9 /
-                                                        pr["hbm_stream_read_GBps"], 4)},
+                                                        pr["hbm_stream_read_GBps"], 4),
+                         "frac_of_measured_copy": round(traffic / (km * 1e-3) / 1e9 /
+                                                        pr["hbm_copy_read_plus_write_GBps"], 4)},
             "raw_hbm_gather_us": round(rm * 1e3, 2),
             "speedup_vs_raw_hbm_gather": round(rm / km, 3),
             "unique_ids": int(len(np.unique(last))),
