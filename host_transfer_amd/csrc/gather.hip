@@ -29,6 +29,8 @@
 //
 // k_gather_tile (W <= 256): one wave decodes a tile of T small tensors at a
 // time (see its comment), with the same pipeline across tiles.
+// k_gather_direct: short batches of such tensors held in an HBM cache, read
+// in place without staging (see its comment).
 //
 // Both have a routed variant (k_gather_decompress_routed, k_gather_tile_routed)
 // that sends every row to the XCD its tensor hashes to, for batches that
@@ -577,6 +579,9 @@ __device__ __forceinline__ void unpack_stages_n(uint32_t (&x)[N], const uint32_t
 #ifndef IBP_TILE_GROUP
 #define IBP_TILE_GROUP 8  // tensors of a full tile decoded side by side (4 when J >= 4)
 #endif
+#ifndef IBP_DIRECT_TG
+#define IBP_DIRECT_TG 8   // tensors per tile of k_gather_direct (half when J >= 3)
+#endif
 #ifndef IBP_BIG_NL
 #define IBP_BIG_NL 8      // load instructions per tile on large batches
 #endif
@@ -631,7 +636,7 @@ __device__ __forceinline__ void decode_full_tile(const GatherArgs& a, const Word
       }
 #pragma unroll
       for (int q = 0; q < TG; ++q) {
-        uint32_t* dst = ROUTED ? a.out + (uint64_t)__builtin_amdgcn_readlane(trow, i0 + q) * kW + lane
+        uint32_t* dst = ROUTED ? a.out + (uint64_t)lane_u32(trow, i0 + q) * kW + lane
                                : obase + (uint64_t)(i0 + q) * kW;
         store_out(dst + (uint32_t)kWave * j, x[q]);
       }
@@ -818,6 +823,207 @@ static hipError_t launch_tile(const Geometry& g, GatherArgs a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
+// Cache-mode kernel for short batches of small tensors (W == 64 J) whose
+// payloads are all in HBM.
+//
+// The tile kernel stages every payload in LDS by way of registers.  A payload
+// in HBM can be read where it lies instead: each lane reads the 8 bytes that
+// hold its word's bits straight from the cache (neighbouring lanes' windows
+// share cache lines, so L1 serves most of them).  Nothing is staged and no
+// workgroup barrier follows the plan, so a launch's chain of dependent steps
+// (ids, metadata, payload, store) is shorter: on batches of a few thousand
+// ids, which latency bounds, that wins.  On long batches the tile kernel's
+// 16 B loads move more bytes per instruction and it is faster, so it keeps
+// those.  A wave decodes TG tensors at a time, J word positions each.
+// Pipeline per wave: the windows of tile k+1 are requested after tile k is
+// decoded and before its rows are stored, so waiting for them never waits for
+// those stores; the metadata of tile k+2 (and the ids of tile k+3) are
+// requested just before.  Not for payloads in host memory, which this would
+// read more than once.
+
+// Per-lane header of tensor (lane % TG) of a tile.
+struct DirectHdr {
+  uint64_t addr;    // payload address (g_zero16 when nothing is readable)
+  uint32_t pmask;   // participation bits
+  uint32_t off[3];  // bit offsets of chunks 1..3
+  uint32_t lim;     // readable bytes at addr, when an 8 B window may pass them
+  uint32_t tail;    // 1: windows are bounded by lim (the cache's last entries)
+};
+
+__device__ __forceinline__ DirectHdr make_direct_hdr(const GatherArgs& a, const TileMeta& m,
+                                                     const uint32_t* s_kc) {
+  DirectHdr h;
+  const Source src = source_of(a, m.t, m.o);
+  const bool valid = m.valid && src.ok;
+  const uint32_t n_c = a.sh.n_c;
+  const uint64_t word = (uint64_t)m.w0 | ((uint64_t)m.w1 << 32);
+  const uint32_t pm = valid ? (uint32_t)(word >> m.sh) & ((1u << n_c) - 1u) : 0u;
+  uint32_t o = 0, offs[4];
+#pragma unroll
+  for (uint32_t c = 0; c < 4; ++c) {  // n_c <= 4
+    offs[c] = o;
+    if (c < n_c) o += ((pm >> c) & 1u) ? s_kc[c] : chunk_bits(a.sh, c);
+  }
+  h.off[0] = offs[1];
+  h.off[1] = offs[2];
+  h.off[2] = offs[3];
+  h.pmask = pm;
+  // a window starts at most 4 bytes before the payload's 16 B-rounded end
+  const uint64_t len16 = valid ? (uint64_t)((((o + 7u) >> 3) + 15u) & ~15u) : 0ull;
+  const bool readable = valid && len16 > 0 && src.avail >= len16;
+  h.addr = readable ? src.addr : (uint64_t)&g_zero16;
+  const uint64_t lim = src.avail < len16 + 16u ? src.avail : len16 + 16u;
+  h.lim = readable ? (uint32_t)lim : 16u;
+  h.tail = (!readable || src.avail < len16 + 4) ? 1u : 0u;
+  return h;
+}
+
+// The 8 bytes at byte `byte` of a payload; past `lim` (tail headers only)
+// they read as zero.  Invalid or empty payloads read g_zero16, whose words
+// are all zero, so their windows are zero whatever the offset.
+__device__ __forceinline__ uint2 direct_window(uint64_t base, uint32_t byte, bool tail,
+                                               uint32_t lim) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2), aligned(4)));
+  typedef __attribute__((address_space(1))) const u32x2 global_u32x2;
+  typedef __attribute__((address_space(1))) const uint32_t global_u32;
+  if (!tail) {
+    const u32x2 v = *(global_u32x2*)(uintptr_t)(base + byte);
+    return make_uint2(v.x, v.y);
+  }
+  const uint32_t b0 = byte + 4u <= lim ? byte : 0u;
+  const uint32_t b1 = byte + 8u <= lim ? byte + 4u : 0u;
+  const uint32_t d0 = *(global_u32*)(uintptr_t)(base + b0);
+  const uint32_t d1 = *(global_u32*)(uintptr_t)(base + b1);
+  return make_uint2(byte + 4u <= lim ? d0 : 0u, byte + 8u <= lim ? d1 : 0u);
+}
+
+template <int J, int TG>
+__global__ __launch_bounds__(256) void k_gather_direct(GatherArgs a) {
+  constexpr uint32_t kW = (uint32_t)kWave * J;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const GatherLds L(a.sh.W, a.pbuf_bytes);
+  uint32_t* s_pref = (uint32_t*)(smem + L.pref);
+  uint32_t* s_kc = (uint32_t*)(smem + L.kc);
+  uint32_t* s_wsum = (uint32_t*)(smem + L.wsum);
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  const uint32_t lane = threadIdx.x % kWave;
+  const uint64_t n_tiles = (a.n_ids + TG - 1) / TG;
+  const uint64_t waves = (uint64_t)gridDim.x * (blockDim.x / kWave);
+  const uint64_t tile0 = (uint64_t)blockIdx.x * (blockDim.x / kWave) + wave;
+  const uint32_t mrow = lane % TG;
+
+  const int64_t id_a = tile_row_id(a, tile0 * TG + mrow);
+  const int64_t id_b = tile_row_id(a, (tile0 + waves) * TG + mrow);
+  PlanRun run;
+  load_plan_run(a.mask, a.sh, run);
+  WordRegs<J> R;
+  load_plan_fetch<J>(a.mask, a.bitval, a.sh, lane, R);
+  const TileMeta m0 = load_tile_meta(a, id_a);
+  TileMeta meta_next = load_tile_meta(a, id_b);
+  int64_t id_next2 = tile_row_id(a, (tile0 + 2 * waves) * TG + mrow);
+  load_plan_counts(run, a.sh, s_pref, s_kc, s_wsum);  // workgroup barriers: every thread
+  if (tile0 >= n_tiles) return;                       // per wave; no workgroup barrier follows
+  load_plan_words<J>(a.sh, s_pref, lane, R);
+
+  // windows of the tile in flight: [j][q]
+  uint2 win[J][TG];
+  DirectHdr h = make_direct_hdr(a, m0, s_kc);
+#define IBP_DIRECT_ISSUE(hdr)                                                                 \
+  {                                                                                           \
+    const uint32_t hpm_ = (hdr).pmask;                                                        \
+    _Pragma("unroll") for (int j = 0; j < J; ++j) {                                           \
+      const uint32_t c_ = uniform(((uint32_t)kWave * j) >> a.sh.wpc_log2);                    \
+      const uint32_t oj_ = c_ == 0 ? 0u : c_ == 1 ? (hdr).off[0] : c_ == 2 ? (hdr).off[1]     \
+                                                                          : (hdr).off[2];     \
+      const uint32_t pb_ = (uint32_t)__builtin_amdgcn_ballot_w64(((hpm_ >> c_) & 1u) != 0u);  \
+      const uint32_t lo_ = R.info[j] & 0xFFFFu, hi_ = R.info[j] >> 16;                        \
+      _Pragma("unroll") for (int q = 0; q < TG; ++q) {                                        \
+        const uint64_t base_ = lane_u64((hdr).addr, q);                                       \
+        const uint32_t bit_ = lane_u32(oj_, q) + (((pb_ >> q) & 1u) ? lo_ : hi_);             \
+        const bool tail_ = lane_u32((hdr).tail, q) != 0u;                                     \
+        win[j][q] = direct_window(base_, (bit_ >> 5) << 2, tail_, lane_u32((hdr).lim, q));    \
+        const int k_ = j * TG + q;                                                            \
+        shp[k_ / 6] = (k_ % 6 == 0 ? 0u : shp[k_ / 6]) | ((bit_ & 31u) << (5 * (k_ % 6)));     \
+      }                                                                                       \
+    }                                                                                         \
+  }
+  // the windows' bit shifts, 5 bits each (applied once the windows arrive;
+  // alignbit reads only the low 5 bits of its shift operand)
+  uint32_t shp[(J * TG + 5) / 6];
+  IBP_DIRECT_ISSUE(h)
+  uint32_t pm_cur = h.pmask;
+
+  for (uint64_t tile = tile0; tile < n_tiles; tile += waves) {
+    const bool has_next = tile + waves < n_tiles;
+    // 1. decode this tile's windows
+    uint32_t x[J][TG];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const uint32_t c = uniform(((uint32_t)kWave * j) >> a.sh.wpc_log2);
+      const uint32_t pbits = (uint32_t)__builtin_amdgcn_ballot_w64(((pm_cur >> c) & 1u) != 0u);
+#pragma unroll
+      for (int q = 0; q < TG; ++q) {
+        const int k = j * TG + q;
+        x[j][q] = __builtin_amdgcn_alignbit(win[j][q].y, win[j][q].x, shp[k / 6] >> (5 * (k % 6)));
+      }
+      constexpr uint32_t gmask = TG == 32 ? ~0u : (1u << TG) - 1u;
+      const uint32_t gp = pbits & gmask;
+      if (gp == gmask) {
+        unpack_stages_n<TG>(x[j], R.mv[j], R.stages[j]);
+#pragma unroll
+        for (int q = 0; q < TG; ++q) x[j][q] = bfi_op(R.mask[j], R.bitval[j], x[j][q]);
+      } else if (gp != 0u) {
+#pragma unroll
+        for (int q = 0; q < TG; ++q)
+          if ((gp >> q) & 1u)
+            x[j][q] = bfi_op(R.mask[j], R.bitval[j], unpack_stages(x[j][q], R.mv[j], R.stages[j]));
+      }
+    }
+    // 2. next tile: header, metadata two ahead, windows
+    if (has_next) {
+      h = make_direct_hdr(a, meta_next, s_kc);
+      meta_next = load_tile_meta(a, id_next2);
+      id_next2 = tile_row_id(a, (tile + 3 * waves) * TG + mrow);
+      IBP_DIRECT_ISSUE(h)
+      pm_cur = h.pmask;
+    }
+    // 3. store this tile (rows past the batch are not written)
+    const uint64_t row0 = tile * TG;
+#pragma unroll
+    for (int q = 0; q < TG; ++q) {
+      if (row0 + q < a.n_ids) {
+        uint32_t* dst = a.out + (row0 + q) * kW + lane;
+#pragma unroll
+        for (int j = 0; j < J; ++j) store_out(dst + (uint32_t)kWave * j, x[j][q]);
+      }
+    }
+  }
+#undef IBP_DIRECT_ISSUE
+}
+
+template <int J, int TG>
+static hipError_t launch_direct(const Geometry& g, GatherArgs a, hipStream_t s) {
+  a.sh.group = kWave;  // lane l owns words l + 64j
+  const uint32_t waves = 4;
+  const GatherLds L(g.W, a.pbuf_bytes);
+  const uint32_t lds = L.group0;
+  DeviceInfo di;
+  hipError_t e = device_info(&di);
+  if (e != hipSuccess) return e;
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gather_direct<J, TG>, waves * 64,
+                                                   lds);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) return hipErrorInvalidConfiguration;
+  const uint64_t tiles = (a.n_ids + TG - 1) / TG;
+  const uint64_t want = (tiles + waves - 1) / waves;
+  const uint64_t cap = (uint64_t)per_cu * (uint64_t)di.cus;
+  const uint32_t blocks = (uint32_t)(want < cap ? want : cap);
+  hipLaunchKernelGGL((k_gather_direct<J, TG>), dim3(blocks), dim3(waves * 64), lds, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Tile kernel with XCD-aware routing, for payloads read from their slots.
 //
 // The eight XCDs have an L2 each, and workgroups are dispatched to them round
@@ -937,7 +1143,7 @@ __global__ __launch_bounds__(256) void k_gather_tile_routed(GatherArgs a) {
           const uint32_t pm = uniform(hp->pmask);
           const uint32_t o1 = uniform(hp->off[0]), o2 = uniform(hp->off[1]), o3 = uniform(hp->off[2]);
           const uint32_t* pb32 = (const uint32_t*)(pbufs + i * a.pbuf_bytes);
-          uint32_t* orow = a.out + (uint64_t)__builtin_amdgcn_readlane(trow, i) * W;
+          uint32_t* orow = a.out + (uint64_t)lane_u32(trow, i) * W;
 #pragma unroll
           for (int j = 0; j < J; ++j) {
             const uint32_t w = lane + kWave * j;
@@ -1001,6 +1207,9 @@ static hipError_t launch_small(const Geometry& g, const GatherArgs& a, hipStream
   if (e != hipSuccess) return e;
   const bool full = g.W == (uint32_t)kWave * J;
   const bool big = a.n_ids >= (uint64_t)8 * RPI * 8 * (uint64_t)di.cus;
+  // short launches with every payload in HBM (no host slots): read in place
+  if (full && !big && a.offsets != nullptr && a.store == nullptr && !a.route)
+    return launch_direct<J, (J >= 3 ? IBP_DIRECT_TG / 2 : IBP_DIRECT_TG)>(g, a, s);
   if (a.route)
     return full ? launch_tile_routed<J, 2 * RPI, RPI, true>(g, a, s)
                 : launch_tile_routed<J, 2 * RPI, RPI, false>(g, a, s);

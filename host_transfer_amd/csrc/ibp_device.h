@@ -132,6 +132,16 @@ __device__ __forceinline__ uint32_t xcd_of_tensor(int64_t id) {
 
 __device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
 
+// Lane l's value of v (l wave-uniform).  The builtin returns a signed int:
+// going through uint32_t keeps a later widening to 64 bits (an address, a
+// row index) from sign-extending it.
+__device__ __forceinline__ uint32_t lane_u32(uint32_t v, uint32_t l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, (int)l);
+}
+__device__ __forceinline__ uint64_t lane_u64(uint64_t v, uint32_t l) {
+  return ((uint64_t)lane_u32((uint32_t)(v >> 32), l) << 32) | (uint64_t)lane_u32((uint32_t)v, l);
+}
+
 // Orders LDS accesses among the lanes of one wave.
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

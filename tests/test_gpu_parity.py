@@ -109,7 +109,8 @@ def test_kv_pair():
 
 # ------------------------------------------------------------ geometry sweep
 
-SHAPES = [(4, 256), (12, 256), (260, 256), (508, 1024), (1028, 256), (2052, 1024),
+SHAPES = [(4, 256), (12, 256), (256, 256), (260, 256), (508, 1024), (768, 256), (1024, 256),
+          (1024, 1024), (1028, 256), (2052, 1024),
           (4100, 4096), (5732, 1024), (8196, 256), (10240, 256), (16384, 256), (16384, 4096)]
 
 
