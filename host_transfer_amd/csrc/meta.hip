@@ -54,6 +54,10 @@ constexpr uint32_t kMetaWaves = 4;  // waves per workgroup, all on the same 64 w
 // that word is added into the 32 counters.  About 9 operations per row and
 // word instead of 64.  The workgroup's four waves add their counts in LDS,
 // and the workgroup adds the totals to the global counters with atomics.
+// kIds: rows are picked by sample ids (else rows 0..n-1).  A template
+// parameter rather than a test per row, so the sixteen loads of a group are
+// issued together instead of each one waiting behind a branch.
+template <bool kIds>
 __global__ __launch_bounds__(256) void k_meta_count(const uint8_t* __restrict__ rows,
                                                      uint64_t row_stride,
                                                      const int64_t* __restrict__ ids, uint64_t n,
@@ -80,12 +84,12 @@ __global__ __launch_bounds__(256) void k_meta_count(const uint8_t* __restrict__ 
   uint32_t ones = 0, twos = 0, fours = 0, eights = 0;
   uint64_t s = r0;
   for (; s + 16 <= r1; s += 16) {
+    uint64_t r[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r[i] = kIds ? (uint64_t)ids[s + i] : s + i;
     uint32_t x[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint64_t r = ids ? (uint64_t)ids[s + i] : s + i;
-      x[i] = *(const uint32_t*)(base + r * row_stride);
-    }
+    for (int i = 0; i < 16; ++i) x[i] = *(const uint32_t*)(base + r[i] * row_stride);
     uint32_t twosA, twosB, foursA, foursB, eightsA, eightsB, sixteens;
     csa(twosA, ones, ones, x[0], x[1]);
     csa(twosB, ones, ones, x[2], x[3]);
@@ -107,7 +111,7 @@ __global__ __launch_bounds__(256) void k_meta_count(const uint8_t* __restrict__ 
   }
   // fewer than 16 rows left: add them one at a time through the planes
   for (; s < r1; ++s) {
-    const uint64_t r = ids ? (uint64_t)ids[s] : s;
+    const uint64_t r = kIds ? (uint64_t)ids[s] : s;
     uint32_t c = *(const uint32_t*)(base + r * row_stride);
     uint32_t t = ones & c;
     ones ^= c;
@@ -179,9 +183,14 @@ hipError_t launch_build_metadata(const uint8_t* rows, uint64_t row_stride, const
   if (slabs > (n + min_rows - 1) / min_rows) slabs = (n + min_rows - 1) / min_rows;
   const uint64_t per_slab = (n + slabs - 1) / slabs;
   slabs = (n + per_slab - 1) / per_slab;
-  hipLaunchKernelGGL(k_meta_count, dim3((uint32_t)(slabs * word_groups)),
-                     dim3(kWave * kMetaWaves), 0, s, rows, row_stride, ids, n, W, word_groups,
-                     per_slab, counts);
+  if (ids)
+    hipLaunchKernelGGL(k_meta_count<true>, dim3((uint32_t)(slabs * word_groups)),
+                       dim3(kWave * kMetaWaves), 0, s, rows, row_stride, ids, n, W, word_groups,
+                       per_slab, counts);
+  else
+    hipLaunchKernelGGL(k_meta_count<false>, dim3((uint32_t)(slabs * word_groups)),
+                       dim3(kWave * kMetaWaves), 0, s, rows, row_stride, ids, n, W, word_groups,
+                       per_slab, counts);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_meta_threshold, dim3((W + 255) / 256), dim3(256), 0, s, counts, W, n,
