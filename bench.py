@@ -859,6 +859,23 @@ def run_kv_step(torch, ibp, W, args, pr, pairs=None):
     steps = max(3, min(args.steps, 20))
     ibp_ms, _ = region_launches(torch, step_ibp, 2, steps)
     raw_ms, _ = region_launches(torch, step_raw, 2, steps)
+    # the whole step in one launch: one segment per pair, each with its Mask
+    masks_all = torch.cat([mv[0] for mv in masks])
+    bitvals_all = torch.cat([mv[1] for mv in masks])
+    d_all = torch.arange(N, dtype=torch.int64, device="cuda")
+    seg = [p * R for p in range(P + 1)]
+    out_all = torch.empty(N * B, dtype=torch.uint8, device="cuda")
+
+    def step_seg(k):
+        ibp.gather_decompress_segments(store, N * S, S, None, part, N, d_all, seg, B, C, masks_all,
+                                       bitvals_all, out_all)
+    seg_ms, _ = region_launches(torch, step_seg, 2, steps)
+    torch.cuda.synchronize()
+    pick = np.linspace(0, N - 1, 257).astype(np.int64)
+    if not (out_all.view(N, B)[torch.from_numpy(pick).cuda()].cpu().numpy() ==
+            raw.array.reshape(N, S)[pick, :B]).all():
+        raise SystemExit("bench: the segmented K/V step is not lossless")
+    del out_all, d_all
     step_ibp(0)
     torch.cuda.synchronize()
     if not (out.view(R, B)[:32].cpu().numpy() == raw.array.reshape(N, S)[(P - 1) * R:
@@ -877,6 +894,9 @@ def run_kv_step(torch, ibp, W, args, pr, pairs=None):
            "compressed_GBps_over_link": round(comp / (ibp_ms * 1e-3) / 1e9, 2),
            "frac_of_link_peak": round(comp / (ibp_ms * 1e-3) / 1e9 / link, 4),
            "raw_step_ms": round(raw_ms, 3), "speedup_vs_raw": round(raw_ms / ibp_ms, 3),
+           "one_launch_step_ms": round(seg_ms, 3),
+           "one_launch_frac_of_link_peak": round(comp / (seg_ms * 1e-3) / 1e9 / link, 4),
+           "one_launch_speedup_vs_raw": round(raw_ms / seg_ms, 3),
            "prefill_mask_ms_per_pair": round(statistics.mean(meta_ms), 3),
            "prefill_mask_ms_all_pairs": round(sum(meta_ms), 2),
            "prefill_mask_over_decode_fetch": round(sum(meta_ms) / (W.KV_DECODE * ibp_ms), 4),

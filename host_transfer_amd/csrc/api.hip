@@ -277,6 +277,54 @@ int ibp_gather_decompress_ex(const void* store, uint64_t store_bytes, uint64_t s
   return ok();
 }
 
+int ibp_gather_decompress_segments(const void* store, uint64_t store_bytes, uint64_t slot_bytes,
+                                   const uint64_t* offsets, const uint32_t* part_bits,
+                                   uint64_t n_tensors, const int64_t* ids,
+                                   const uint64_t* seg_ids, uint32_t n_segments,
+                                   uint32_t tensor_bytes, uint32_t chunk_bytes,
+                                   const uint32_t* masks, const uint32_t* bitvals, void* out,
+                                   void* stream) {
+  static_assert(ibp::kMaxSegments == IBP_MAX_SEGMENTS, "segment limit");
+  const char* name = "ibp_gather_decompress_segments";
+  if (!store || !part_bits || !ids || !seg_ids || !masks || !bitvals || !out)
+    return fail(IBP_ERR_NULL, "%s: a required pointer is null", name);
+  if (n_segments == 0 || n_segments > IBP_MAX_SEGMENTS)
+    return fail(IBP_ERR_SIZE, "%s: n_segments %u must be in [1, %u]", name, n_segments,
+                IBP_MAX_SEGMENTS);
+  if (seg_ids[0] != 0) return fail(IBP_ERR_SIZE, "%s: seg_ids[0] must be 0", name);
+  for (uint32_t k = 0; k < n_segments; ++k)
+    if (seg_ids[k + 1] < seg_ids[k])
+      return fail(IBP_ERR_SIZE, "%s: seg_ids must not decrease (segment %u)", name, k);
+  const uint64_t n_ids = seg_ids[n_segments];
+  int r = check_tensor(tensor_bytes);
+  if (r) return r;
+  if ((r = check_chunk(chunk_bytes))) return r;
+  const uint32_t n_c = (tensor_bytes + chunk_bytes - 1) / chunk_bytes;
+  if (n_tensors && !bitmap_bits(n_tensors, n_c))
+    return fail(IBP_ERR_SIZE, "%s: n_tensors too large", name);
+  if (!offsets) {
+    if (slot_bytes < tensor_bytes || slot_bytes % 16 != 0)
+      return fail(IBP_ERR_SIZE, "%s: slot_bytes must be >= tensor_bytes and %% 16", name);
+    if (n_tensors > UINT64_MAX / slot_bytes || store_bytes < n_tensors * slot_bytes)
+      return fail(IBP_ERR_SIZE, "%s: store_bytes < n_tensors * slot_bytes", name);
+  }
+  if (n_ids > UINT64_MAX / tensor_bytes) return fail(IBP_ERR_SIZE, "%s: n_ids too large", name);
+  if (!aligned(store, 16) || !aligned(out, 16) || !aligned(ids, 8) || !aligned(masks, 4) ||
+      !aligned(bitvals, 4) || !aligned(part_bits, 4) || (offsets && !aligned(offsets, 8)))
+    return fail(IBP_ERR_ALIGN, "%s: misaligned pointer", name);
+  if ((r = require_device(name))) return r;
+  const ibp::Geometry g = ibp::make_geometry(tensor_bytes, chunk_bytes);
+  hipError_t e = offsets
+      ? ibp::launch_gather_segments(g, nullptr, 0, 0, offsets, (const uint8_t*)store, store_bytes,
+                                    part_bits, n_tensors, ids, seg_ids, n_segments, masks,
+                                    bitvals, (uint32_t*)out, (hipStream_t)stream)
+      : ibp::launch_gather_segments(g, (const uint8_t*)store, store_bytes, slot_bytes, nullptr,
+                                    nullptr, 0, part_bits, n_tensors, ids, seg_ids, n_segments,
+                                    masks, bitvals, (uint32_t*)out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, name);
+  return ok();
+}
+
 int ibp_cache_offsets(const uint32_t* lengths, const uint32_t* select, uint64_t n_tensors,
                       uint64_t* cache_offsets, void* stream) {
   if (!lengths || !select || !cache_offsets)

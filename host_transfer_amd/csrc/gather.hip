@@ -241,8 +241,10 @@ __device__ __forceinline__ void decode_group_tensor(const GatherArgs& a, const W
   }
 }
 
+// The body of the group kernel for workgroup `block` of `blocks` (the whole
+// grid, or the workgroups of one segment of k_gather_decompress_seg).
 template <int J>
-__global__ __launch_bounds__(1024) void k_gather_decompress(GatherArgs a) {
+__device__ __forceinline__ void gather_group_body(GatherArgs& a, uint32_t block, uint32_t blocks) {
   extern __shared__ __align__(16) uint8_t smem[];
   const GatherLds L(a.sh.W, a.pbuf_bytes);
   uint32_t* s_pref = (uint32_t*)(smem + L.pref);
@@ -262,8 +264,8 @@ __global__ __launch_bounds__(1024) void k_gather_decompress(GatherArgs a) {
   const bool single = G == kWave;
   const bool first_wave = gl < kWave;
   const uint32_t W = a.sh.W;
-  const uint64_t step = (uint64_t)gridDim.x * a.groups;
-  const uint64_t row0 = (uint64_t)blockIdx.x * a.groups + g;
+  const uint64_t step = (uint64_t)blocks * a.groups;
+  const uint64_t row0 = (uint64_t)block * a.groups + g;
 
   // Metadata runs ahead of the payloads so that no wait for it also waits
   // for a payload still in flight (vector loads retire in issue order):
@@ -332,6 +334,38 @@ __global__ __launch_bounds__(1024) void k_gather_decompress(GatherArgs a) {
     decode_group_tensor<J>(a, R, h, obufs + 64u * cur, pb32, gl, G, a.out + row * W);
     group_sync(single);
   }
+}
+
+template <int J>
+__global__ __launch_bounds__(1024) void k_gather_decompress(GatherArgs a) {
+  gather_group_body<J>(a, blockIdx.x, gridDim.x);
+}
+
+// Several gathers of one tensor shape in one launch, each segment with its
+// own Mask/Bitval (the K/V decode step: one segment per (layer, K|V) pair).
+// Segment s is ids [off[s], off[s+1]) -> out rows [off[s], off[s+1]), with
+// the Mask and Bitval words at s * W.  The grid is n_seg * per_seg
+// workgroups; workgroup b serves segment b / per_seg as workgroup
+// b % per_seg of per_seg, so it builds that segment's plan once, and the
+// launch pays its fixed cost once for all segments.
+struct SegTable {
+  uint64_t off[kMaxSegments + 1];
+  uint32_t n_seg;
+  uint32_t per_seg;
+};
+
+template <int J>
+__global__ __launch_bounds__(1024) void k_gather_decompress_seg(GatherArgs a, SegTable t) {
+  const uint32_t seg = blockIdx.x / t.per_seg;  // < n_seg: the grid is n_seg * per_seg
+  const uint64_t o = t.off[seg], n = t.off[seg + 1] - o;
+  GatherArgs b = a;
+  b.ids = a.ids + o;
+  b.n_ids = n;
+  b.out = a.out + o * a.sh.W;
+  b.mask = a.mask + (uint64_t)seg * a.sh.W;
+  b.bitval = a.bitval + (uint64_t)seg * a.sh.W;
+  if (n == 0) return;  // the whole workgroup, before any barrier
+  gather_group_body<J>(b, blockIdx.x % t.per_seg, t.per_seg);
 }
 
 // Group kernel with XCD-aware routing (see k_gather_tile_routed), for
@@ -1304,6 +1338,93 @@ hipError_t launch_gather(const Geometry& g, const uint8_t* store, uint64_t store
     case 4: return launch_j<4>(g, a, s);
     case 5: return launch_j<5>(g, a, s);
     case 6: return launch_j<6>(g, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int J>
+static hipError_t launch_j_seg(const Geometry& g, const GatherArgs& a, const SegTable& t0,
+                               uint64_t max_rows, hipStream_t s) {
+  const GatherLds L(g.W, a.pbuf_bytes);
+  const uint32_t lds = L.total(g.groups);
+  const uint32_t threads = g.group * g.groups;
+  DeviceInfo di;
+  hipError_t e = device_info(&di);
+  if (e != hipSuccess) return e;
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gather_decompress_seg<J>, threads,
+                                                   lds);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) return hipErrorInvalidConfiguration;
+  // the resident capacity shared evenly by the segments, but no more
+  // workgroups per segment than its largest one has rows for
+  SegTable t = t0;
+  const uint64_t cap = (uint64_t)per_cu * (uint64_t)di.cus;
+  uint64_t per = cap / t.n_seg;
+  const uint64_t need = (max_rows + g.groups - 1) / g.groups;
+  if (per > need) per = need;
+  if (per < 1) per = 1;
+  t.per_seg = (uint32_t)per;
+  hipLaunchKernelGGL(k_gather_decompress_seg<J>, dim3((uint32_t)(per * t.n_seg)), dim3(threads),
+                     lds, s, a, t);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_segments(const Geometry& g, const uint8_t* store, uint64_t store_bytes,
+                                  uint64_t slot_bytes, const uint64_t* offsets,
+                                  const uint8_t* cache, uint64_t cache_bytes,
+                                  const uint32_t* part_bits, uint64_t n_tensors,
+                                  const int64_t* ids, const uint64_t* seg_off, uint32_t n_seg,
+                                  const uint32_t* masks, const uint32_t* bitvals, uint32_t* out,
+                                  hipStream_t s) {
+  const uint64_t n_ids = seg_off[n_seg];
+  if (n_ids == 0) return hipSuccess;
+  if (n_tensors == 0 || g.W <= 4 * (uint32_t)kWave) {
+    // no tensors (zero rows), or small tensors (tile kernels): one launch
+    // per non-empty segment
+    for (uint32_t k = 0; k < n_seg; ++k) {
+      const uint64_t o = seg_off[k], n = seg_off[k + 1] - o;
+      if (n == 0) continue;
+      const hipError_t e = launch_gather(g, store, store_bytes, slot_bytes, offsets, cache,
+                                         cache_bytes, part_bits, n_tensors, ids + o, n,
+                                         masks + (uint64_t)k * g.W, bitvals + (uint64_t)k * g.W,
+                                         out + o * g.W, false, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  GatherArgs a;
+  a.store = store;
+  a.store_bytes = store ? store_bytes : 0;
+  a.slot_bytes = slot_bytes;
+  a.offsets = offsets;
+  a.cache = cache;
+  a.cache_bytes = cache ? cache_bytes : 0;
+  a.part_bits = part_bits;
+  a.n_tensors = n_tensors;
+  a.ids = ids;
+  a.n_ids = n_ids;
+  a.mask = masks;
+  a.bitval = bitvals;
+  a.out = out;
+  a.sh = Shape{g.W, g.n_c, g.wpc_log2, g.last_bits, g.group};
+  a.groups = g.groups;
+  a.route = 0;
+  a.pbuf_bytes = ((g.tensor_bytes + 15u) & ~15u) + 16u;
+  SegTable t;
+  uint64_t max_rows = 0;
+  for (uint32_t k = 0; k <= n_seg; ++k) t.off[k] = seg_off[k];
+  for (uint32_t k = 0; k < n_seg; ++k)
+    max_rows = seg_off[k + 1] - seg_off[k] > max_rows ? seg_off[k + 1] - seg_off[k] : max_rows;
+  t.n_seg = n_seg;
+  t.per_seg = 1;
+  switch (g.J) {
+    case 1: return launch_j_seg<1>(g, a, t, max_rows, s);
+    case 2: return launch_j_seg<2>(g, a, t, max_rows, s);
+    case 3: return launch_j_seg<3>(g, a, t, max_rows, s);
+    case 4: return launch_j_seg<4>(g, a, t, max_rows, s);
+    case 5: return launch_j_seg<5>(g, a, t, max_rows, s);
+    case 6: return launch_j_seg<6>(g, a, t, max_rows, s);
     default: return hipErrorInvalidValue;
   }
 }

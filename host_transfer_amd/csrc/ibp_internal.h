@@ -47,6 +47,17 @@ hipError_t launch_compact(const uint8_t* store, uint64_t slot_bytes, uint64_t n,
 
 // store: in-place slots (or null); offsets + cache: compacted cache entries
 // (kNotCached marks a tensor that is read from its slot instead).
+// Most segments one ibp_gather_decompress_segments call takes (IBP_MAX_SEGMENTS).
+constexpr uint32_t kMaxSegments = 256;
+
+hipError_t launch_gather_segments(const Geometry& g, const uint8_t* store, uint64_t store_bytes,
+                                  uint64_t slot_bytes, const uint64_t* offsets,
+                                  const uint8_t* cache, uint64_t cache_bytes,
+                                  const uint32_t* part_bits, uint64_t n_tensors,
+                                  const int64_t* ids, const uint64_t* seg_off, uint32_t n_seg,
+                                  const uint32_t* masks, const uint32_t* bitvals, uint32_t* out,
+                                  hipStream_t s);
+
 hipError_t launch_gather(const Geometry& g, const uint8_t* store, uint64_t store_bytes,
                          uint64_t slot_bytes, const uint64_t* offsets, const uint8_t* cache,
                          uint64_t cache_bytes, const uint32_t* part_bits, uint64_t n_tensors,

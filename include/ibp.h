@@ -216,6 +216,36 @@ int ibp_gather_decompress_ex(const void *store, uint64_t store_bytes,
                              const uint32_t *mask, const uint32_t *bitval,
                              void *out, unsigned flags, void *stream);
 
+/*
+ * ibp_gather_decompress_segments -- several gathers of one tensor shape in
+ * one launch, each segment with its own Mask and Bitval ([JH] LLM paragraph:
+ * one Mask per (layer, K|V) pair, from that pair's prompt K/V; a decode step
+ * fetches every pair).  Segment k gathers ids[seg_ids[k] .. seg_ids[k+1])
+ * into out rows seg_ids[k] .. seg_ids[k+1]-1, decoded with the Mask words at
+ * masks + k*W and the Bitval words at bitvals + k*W (W = tensor_bytes / 4).
+ * The segments share the store or cache, the bitmap and n_tensors, as in
+ * ibp_gather_decompress (store, store_bytes, slot_bytes, offsets, part_bits,
+ * n_tensors: same meaning).  Same rows as one ibp_gather_decompress call
+ * per segment; for tensors of more than 256 words the launch's fixed cost is
+ * paid once for all segments (tensors of up to 256 words: one launch per
+ * non-empty segment).
+ *   seg_ids     HOST uint64[n_segments + 1], seg_ids[0] = 0, non-decreasing;
+ *               n_ids = seg_ids[n_segments].  Empty segments are allowed.
+ *   n_segments  1 .. IBP_MAX_SEGMENTS.
+ *   ids         device int64[n_ids];  out  device, n_ids*tensor_bytes bytes.
+ *   masks, bitvals  device uint32[n_segments * W] each.
+ * Errors: as ibp_gather_decompress; n_segments out of range, seg_ids[0] != 0
+ * or decreasing (IBP_ERR_SIZE).
+ */
+#define IBP_MAX_SEGMENTS 256u
+int ibp_gather_decompress_segments(const void *store, uint64_t store_bytes,
+                                   uint64_t slot_bytes, const uint64_t *offsets,
+                                   const uint32_t *part_bits, uint64_t n_tensors,
+                                   const int64_t *ids, const uint64_t *seg_ids,
+                                   uint32_t n_segments, uint32_t tensor_bytes,
+                                   uint32_t chunk_bytes, const uint32_t *masks,
+                                   const uint32_t *bitvals, void *out, void *stream);
+
 /* ------------------------------------------------------ cache + store together
  * [G-EN] System Integration uses both placements at once: a compressed
  * software cache in GPU memory for hot tensors, and compressed in-place

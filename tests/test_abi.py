@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(ibp):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     out = subprocess.run(["nm", "-D", "--defined-only", ibp.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (ibp_\w+)$", out, flags=re.M))
@@ -115,6 +115,20 @@ def test_gather_validation(ibp):
     _expect(ibp, ibp.ERR_FLAGS, fx, *args(offs=P), ibp.GATHER_ROUTE_XCD)
     _expect(ibp, ibp.ERR_SIZE, fx, *args(nids=1 << 32), ibp.GATHER_ROUTE_XCD)
     _expect(ibp, ibp.ERR_SIZE, fx, *args(sbytes=10 * 512 - 1), ibp.GATHER_ROUTE_XCD)
+    # ibp_gather_decompress_segments: the host segment table
+    fs = ibp.gather_decompress_segments
+
+    def seg(seg_ids, **kw):
+        a = args(**kw)
+        return a[:7] + [seg_ids] + a[8:]
+    _expect(ibp, ibp.ERR_SIZE, fs, *seg([0]))                     # no segment
+    _expect(ibp, ibp.ERR_SIZE, fs, *seg(list(range(258))))        # 257 segments
+    _expect(ibp, ibp.ERR_SIZE, fs, *seg([1, 4]))                  # must start at 0
+    _expect(ibp, ibp.ERR_SIZE, fs, *seg([0, 5, 3]))               # decreasing
+    _expect(ibp, ibp.ERR_NULL, fs, *seg([0, 4], ids=0))
+    _expect(ibp, ibp.ERR_SIZE, fs, *seg([0, 4], sbytes=10 * 512 - 1))
+    _expect(ibp, ibp.ERR_ALIGN, fs, *seg([0, 4], out=P + 4))
+    _expect(ibp, ibp.ERR_CHUNK, fs, *seg([0, 4], cb=2048))
 
 
 def test_other_validation(ibp):

@@ -274,6 +274,80 @@ def test_side_stream_and_graph_replay():
             del graph
 
 
+def _segment_case(rows, masks, bitvals, parts, B, C, S, n, rng, mode, cache=None):
+    """One segmented gather over `parts` = [(first, count) of the tensors
+    compressed with mask k]; segment order shuffled, plus an empty segment and
+    invalid ids.  Returns (got, want)."""
+    from host_transfer_amd import ibp
+    store, part, offsets, store_bytes, slot = mode
+    order = list(rng.permutation(len(parts)))
+    seg_ids, ids, m_all, v_all = [0], [], [], []
+    for k in order + ["empty"]:
+        if k == "empty":
+            m_all.append(masks[0]), v_all.append(bitvals[0])
+            seg_ids.append(seg_ids[-1])
+            continue
+        first, count = parts[k]
+        x = rng.integers(first, first + count, 300)
+        x[:3] = [first, first + count - 1, -1]
+        ids.append(x)
+        m_all.append(masks[k]), v_all.append(bitvals[k])
+        seg_ids.append(seg_ids[-1] + len(x))
+    ids = np.concatenate(ids).astype(np.int64)
+    out = torch.full((len(ids) * B,), -1, dtype=torch.int8, device="cuda")
+    ibp.gather_decompress_segments(store, store_bytes, slot, offsets, part, n, G.dev(ids), seg_ids,
+                                   B, C, G.dev(np.concatenate(m_all)), G.dev(np.concatenate(v_all)),
+                                   out)
+    got = G.host(out).view(np.uint8).reshape(len(ids), B)
+    return got, G.expected_rows(rows, ids)
+
+
+def test_segments():
+    """ibp_gather_decompress_segments: every segment decoded with its own
+    Mask/Bitval; one launch for the group kernel (K/V rows), one per segment
+    for the tile kernel (dense_gnn rows); from slots and from a compacted
+    cache; an empty segment and invalid ids."""
+    from host_transfer_amd import ibp
+    rng = np.random.default_rng(31)
+    cases = []
+    w = W.WORKLOADS["kv_opt13b"]
+    R = 400
+    rows = np.concatenate([W.rows(w, p * W.KV_ROWS_PER_PAIR, R) for p in range(3)])
+    samples = [W.kv_prefill_rows(w, p, 1500) for p in range(3)]
+    cases.append(("kv_opt13b", rows, samples, [w.threshold] * 3, w.chunk_bytes, w.slot_bytes))
+    w = W.WORKLOADS["dense_gnn"]
+    rows = W.rows(w, 0, 900)
+    cases.append(("dense_gnn", rows, [rows[:300], rows[300:600], rows[600:]], [0.99, 0.9, 0.75],
+                  w.chunk_bytes, w.slot_bytes))
+    for key, rows, samples, Ts, C, S in cases:
+        n, B = rows.shape
+        k = len(samples)
+        per = n // k
+        masks, bitvals = [], []
+        store = part = lens = None
+        for p in range(k):
+            m, v = G.check_metadata(samples[p], Ts[p])
+            masks.append(m), bitvals.append(v)
+            store, part, lens = G.gpu_compress(rows[p * per:(p + 1) * per], m, v, C, S,
+                                               n_tensors=n, first=p * per, store=store, part=part,
+                                               lengths=lens)
+        assert len({m.tobytes() for m in masks}) > 1, "the segments' masks should differ"
+        parts = [(p * per, per) for p in range(k)]
+        G.log(f"[parity] segments {key}: {k} masks, slots")
+        got, want = _segment_case(rows, masks, bitvals, parts, B, C, S, n, rng,
+                                  (store, part, None, n * S, S))
+        assert (got == want).all(), (key, "slots")
+        offsets = torch.zeros(n + 1, dtype=torch.int64, device="cuda")
+        ibp.compact_offsets(lens, n, offsets)
+        total = int(offsets[-1].item())
+        cache = torch.zeros(max(total, 16), dtype=torch.uint8, device="cuda")
+        ibp.compact(store, S, n, offsets, cache, total)
+        G.log(f"[parity] segments {key}: {k} masks, cache")
+        got, want = _segment_case(rows, masks, bitvals, parts, B, C, S, n, rng,
+                                  (cache, part, offsets, total, 0))
+        assert (got == want).all(), (key, "cache")
+
+
 def test_deterministic_and_store_bound():
     w = W.WORKLOADS["dense_gnn"].scaled(2000)
     rows = W.rows(w)
