@@ -844,6 +844,17 @@ def run_kv_step(torch, ibp, W, args, pr, pairs=None):
                          store, S, part, lengths)
         tm.stop(s0)
     write_ms = tm.ms()
+    # the same compress-on-write with one launch per token: one segment per pair
+    masks_all = torch.cat([mv[0] for mv in masks])
+    bitvals_all = torch.cat([mv[1] for mv in masks])
+    tm = Timer(torch)
+    for j in range(W.KV_DECODE):
+        firsts = [p * R + j * tok for p in range(P)]
+        s0 = tm.start()
+        ibp.compress_segments(raw.ptr, S, firsts, firsts, [tok] * P, N, B, C, masks_all,
+                              bitvals_all, store, S, part, lengths)
+        tm.stop(s0)
+    write_seg_ms = tm.ms()
     L = lengths.cpu().numpy()
     out = torch.empty(R * B, dtype=torch.uint8, device="cuda")
     d_ids = [torch.arange(p * R, (p + 1) * R, dtype=torch.int64, device="cuda") for p in range(P)]
@@ -860,8 +871,6 @@ def run_kv_step(torch, ibp, W, args, pr, pairs=None):
     ibp_ms, _ = region_launches(torch, step_ibp, 2, steps)
     raw_ms, _ = region_launches(torch, step_raw, 2, steps)
     # the whole step in one launch: one segment per pair, each with its Mask
-    masks_all = torch.cat([mv[0] for mv in masks])
-    bitvals_all = torch.cat([mv[1] for mv in masks])
     d_all = torch.arange(N, dtype=torch.int64, device="cuda")
     seg = [p * R for p in range(P + 1)]
     out_all = torch.empty(N * B, dtype=torch.uint8, device="cuda")
@@ -902,6 +911,8 @@ def run_kv_step(torch, ibp, W, args, pr, pairs=None):
            "prefill_mask_over_decode_fetch": round(sum(meta_ms) / (W.KV_DECODE * ibp_ms), 4),
            "prefill_rows_per_pair": W.KV_PREFILL_ROWS,
            "compress_on_write_us_per_token": round(statistics.median(write_ms) * 1e3, 1),
+           "compress_on_write_one_launch_us_per_token": round(statistics.median(write_seg_ms) * 1e3,
+                                                              1),
            "device": torch.cuda.get_device_name(0)}
     raw.free()
     store.free()

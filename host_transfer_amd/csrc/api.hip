@@ -189,6 +189,48 @@ int ibp_compress(const void* rows, uint64_t row_stride, uint64_t n_rows, uint64_
   return ok();
 }
 
+int ibp_compress_segments(const void* rows, uint64_t row_stride, const uint64_t* seg_row,
+                          const uint64_t* seg_first, const uint64_t* seg_count,
+                          uint32_t n_segments, uint64_t n_tensors, uint32_t tensor_bytes,
+                          uint32_t chunk_bytes, const uint32_t* masks, const uint32_t* bitvals,
+                          void* store, uint64_t slot_bytes, uint32_t* part_bits,
+                          uint32_t* lengths, void* stream) {
+  const char* name = "ibp_compress_segments";
+  if (n_segments == 0 || n_segments > IBP_MAX_SEGMENTS)
+    return fail(IBP_ERR_SIZE, "%s: n_segments %u must be in [1, %u]", name, n_segments,
+                IBP_MAX_SEGMENTS);
+  if (!rows || !seg_row || !seg_first || !seg_count || !masks || !bitvals || !store || !part_bits)
+    return fail(IBP_ERR_NULL, "%s: a required pointer is null", name);
+  int r = check_tensor(tensor_bytes);
+  if (r) return r;
+  if ((r = check_chunk(chunk_bytes))) return r;
+  if (row_stride < tensor_bytes || row_stride % 4 != 0)
+    return fail(IBP_ERR_SIZE, "%s: row_stride must be >= tensor_bytes and %% 4", name);
+  for (uint32_t k = 0; k < n_segments; ++k) {
+    if (seg_count[k] > 0xFFFFFFFFull || seg_first[k] > n_tensors ||
+        seg_count[k] > n_tensors - seg_first[k])
+      return fail(IBP_ERR_SIZE, "%s: segment %u exceeds n_tensors", name, k);
+    if (seg_row[k] > UINT64_MAX / row_stride - seg_count[k])
+      return fail(IBP_ERR_SIZE, "%s: segment %u: rows past 2^64 bytes", name, k);
+  }
+  if (slot_bytes < tensor_bytes || slot_bytes % 16 != 0)
+    return fail(IBP_ERR_SIZE, "%s: slot_bytes must be >= tensor_bytes and %% 16", name);
+  const uint32_t n_c = (tensor_bytes + chunk_bytes - 1) / chunk_bytes;
+  if (n_tensors && (!bitmap_bits(n_tensors, n_c) || n_tensors > UINT64_MAX / slot_bytes))
+    return fail(IBP_ERR_SIZE, "%s: n_tensors too large", name);
+  if (!aligned(rows, 4) || !aligned(masks, 4) || !aligned(bitvals, 4) || !aligned(store, 16) ||
+      !aligned(part_bits, 4) || (lengths && !aligned(lengths, 4)))
+    return fail(IBP_ERR_ALIGN, "%s: misaligned pointer", name);
+  if ((r = require_device(name))) return r;
+  const ibp::Geometry g = ibp::make_geometry(tensor_bytes, chunk_bytes);
+  hipError_t e = ibp::launch_compress_segments(g, (const uint8_t*)rows, row_stride, seg_row,
+                                               seg_first, seg_count, n_segments, masks, bitvals,
+                                               (uint8_t*)store, slot_bytes, part_bits, lengths,
+                                               (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, name);
+  return ok();
+}
+
 int ibp_compact_offsets(const uint32_t* lengths, uint64_t n_tensors, uint64_t* offsets,
                         void* stream) {
   if (!lengths || !offsets)

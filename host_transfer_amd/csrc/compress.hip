@@ -53,8 +53,11 @@ struct CompressLds {
   __host__ __device__ uint32_t total(uint32_t groups) const { return group0 + groups * group_stride; }
 };
 
+// The body of the compress kernel for workgroup `block` of `blocks` (the
+// whole grid, or the workgroups of one segment of k_compress_seg).
 template <int J>
-__global__ __launch_bounds__(1024) void k_compress(CompressArgs a) {
+__device__ __forceinline__ void compress_body(const CompressArgs& a, uint32_t block,
+                                              uint32_t blocks) {
   extern __shared__ __align__(16) uint8_t smem[];
   const CompressLds L(a.sh.W, a.pbuf_bytes);
   uint32_t* s_pref = (uint32_t*)(smem + L.pref);
@@ -85,8 +88,8 @@ __global__ __launch_bounds__(1024) void k_compress(CompressArgs a) {
 
   const bool single = G == kWave;
   const uint32_t W = a.sh.W, n_c = a.sh.n_c;
-  const uint64_t step = (uint64_t)gridDim.x * a.groups;
-  for (uint64_t row = (uint64_t)blockIdx.x * a.groups + g; row < a.n_rows; row += step) {
+  const uint64_t step = (uint64_t)blocks * a.groups;
+  for (uint64_t row = (uint64_t)block * a.groups + g; row < a.n_rows; row += step) {
     const uint64_t t = a.first + row;
     const uint32_t* x32 = (const uint32_t*)(a.rows + row * a.row_stride);
 
@@ -160,6 +163,38 @@ __global__ __launch_bounds__(1024) void k_compress(CompressArgs a) {
 }
 
 template <int J>
+__global__ __launch_bounds__(1024) void k_compress(CompressArgs a) {
+  compress_body<J>(a, blockIdx.x, gridDim.x);
+}
+
+// Several compress calls of one tensor shape in one launch, each segment with
+// its own Mask/Bitval (compress-on-write of one decode token's K/V rows for
+// every (layer, K|V) pair).  Segment k compresses rows row0[k] + i of `rows`
+// as tensors first[k] + i, i < count[k].  Workgroup b serves segment
+// b / per_seg as workgroup b % per_seg of per_seg.
+constexpr uint32_t kCompressSegs = 128;  // segments per launch (kernel-argument space)
+
+struct CompressSegTable {
+  uint64_t row0[kCompressSegs];
+  uint64_t first[kCompressSegs];
+  uint32_t count[kCompressSegs];
+  uint32_t per_seg;
+};
+
+template <int J>
+__global__ __launch_bounds__(1024) void k_compress_seg(CompressArgs a, CompressSegTable t) {
+  const uint32_t seg = blockIdx.x / t.per_seg;  // < segments of this launch
+  if (t.count[seg] == 0) return;                // the whole workgroup, before any barrier
+  CompressArgs b = a;
+  b.rows = a.rows + t.row0[seg] * a.row_stride;
+  b.n_rows = t.count[seg];
+  b.first = t.first[seg];
+  b.mask = a.mask + (uint64_t)seg * a.sh.W;
+  b.bitval = a.bitval + (uint64_t)seg * a.sh.W;
+  compress_body<J>(b, blockIdx.x % t.per_seg, t.per_seg);
+}
+
+template <int J>
 static hipError_t launch_j(const Geometry& g, const CompressArgs& a, hipStream_t s) {
   const CompressLds L(g.W, a.pbuf_bytes);
   const uint32_t lds = L.total(g.groups);
@@ -176,6 +211,77 @@ static hipError_t launch_j(const Geometry& g, const CompressArgs& a, hipStream_t
   const uint32_t blocks = (uint32_t)(want < cap ? want : cap);
   hipLaunchKernelGGL(k_compress<J>, dim3(blocks), dim3(threads), lds, s, a);
   return hipGetLastError();
+}
+
+template <int J>
+static hipError_t launch_j_seg(const Geometry& g, const CompressArgs& a, CompressSegTable& t,
+                               uint32_t n_seg, uint64_t max_rows, hipStream_t s) {
+  const CompressLds L(g.W, a.pbuf_bytes);
+  const uint32_t lds = L.total(g.groups);
+  const uint32_t threads = g.group * g.groups;
+  DeviceInfo di;
+  hipError_t e = device_info(&di);
+  if (e != hipSuccess) return e;
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_compress_seg<J>, threads, lds);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) return hipErrorInvalidConfiguration;
+  const uint64_t cap = (uint64_t)per_cu * (uint64_t)di.cus;
+  uint64_t per = cap / n_seg;
+  const uint64_t need = (max_rows + g.groups - 1) / g.groups;
+  if (per > need) per = need;
+  if (per < 1) per = 1;
+  t.per_seg = (uint32_t)per;
+  hipLaunchKernelGGL(k_compress_seg<J>, dim3((uint32_t)(per * n_seg)), dim3(threads), lds, s, a,
+                     t);
+  return hipGetLastError();
+}
+
+hipError_t launch_compress_segments(const Geometry& g, const uint8_t* rows, uint64_t row_stride,
+                                    const uint64_t* seg_row, const uint64_t* seg_first,
+                                    const uint64_t* seg_count, uint32_t n_seg,
+                                    const uint32_t* masks, const uint32_t* bitvals,
+                                    uint8_t* store, uint64_t slot_bytes, uint32_t* part_bits,
+                                    uint32_t* lengths, hipStream_t s) {
+  CompressArgs a;
+  a.rows = rows;
+  a.row_stride = row_stride;
+  a.n_rows = 0;
+  a.first = 0;
+  a.store = store;
+  a.slot_bytes = slot_bytes;
+  a.part_bits = part_bits;
+  a.lengths = lengths;
+  a.sh = Shape{g.W, g.n_c, g.wpc_log2, g.last_bits, g.group};
+  a.groups = g.groups;
+  a.pbuf_bytes = ((g.tensor_bytes + 15u) & ~15u) + 16u;
+  for (uint32_t k0 = 0; k0 < n_seg; k0 += kCompressSegs) {
+    const uint32_t n = n_seg - k0 < kCompressSegs ? n_seg - k0 : kCompressSegs;
+    CompressSegTable t;
+    uint64_t max_rows = 0;
+    for (uint32_t k = 0; k < n; ++k) {
+      t.row0[k] = seg_row[k0 + k];
+      t.first[k] = seg_first[k0 + k];
+      t.count[k] = (uint32_t)seg_count[k0 + k];
+      if (seg_count[k0 + k] > max_rows) max_rows = seg_count[k0 + k];
+    }
+    t.per_seg = 1;
+    if (max_rows == 0) continue;
+    a.mask = masks + (uint64_t)k0 * g.W;
+    a.bitval = bitvals + (uint64_t)k0 * g.W;
+    hipError_t e;
+    switch (g.J) {
+      case 1: e = launch_j_seg<1>(g, a, t, n, max_rows, s); break;
+      case 2: e = launch_j_seg<2>(g, a, t, n, max_rows, s); break;
+      case 3: e = launch_j_seg<3>(g, a, t, n, max_rows, s); break;
+      case 4: e = launch_j_seg<4>(g, a, t, n, max_rows, s); break;
+      case 5: e = launch_j_seg<5>(g, a, t, n, max_rows, s); break;
+      case 6: e = launch_j_seg<6>(g, a, t, n, max_rows, s); break;
+      default: e = hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_compress(const Geometry& g, const uint8_t* rows, uint64_t row_stride,

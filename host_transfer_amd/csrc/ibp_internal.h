@@ -50,6 +50,13 @@ hipError_t launch_compact(const uint8_t* store, uint64_t slot_bytes, uint64_t n,
 // Most segments one ibp_gather_decompress_segments call takes (IBP_MAX_SEGMENTS).
 constexpr uint32_t kMaxSegments = 256;
 
+hipError_t launch_compress_segments(const Geometry& g, const uint8_t* rows, uint64_t row_stride,
+                                    const uint64_t* seg_row, const uint64_t* seg_first,
+                                    const uint64_t* seg_count, uint32_t n_seg,
+                                    const uint32_t* masks, const uint32_t* bitvals,
+                                    uint8_t* store, uint64_t slot_bytes, uint32_t* part_bits,
+                                    uint32_t* lengths, hipStream_t s);
+
 hipError_t launch_gather_segments(const Geometry& g, const uint8_t* store, uint64_t store_bytes,
                                   uint64_t slot_bytes, const uint64_t* offsets,
                                   const uint8_t* cache, uint64_t cache_bytes,

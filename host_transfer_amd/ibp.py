@@ -44,6 +44,8 @@ _SIGS = {
     "ibp_num_chunks": [_u32, _u32],
     "ibp_build_metadata": [_vp, _u64, _vp, _u64, _u32, ctypes.c_double, _vp, _vp, _vp, _vp],
     "ibp_compress": [_vp, _u64, _u64, _u64, _u64, _u32, _u32, _vp, _vp, _vp, _u64, _vp, _vp, _vp],
+    "ibp_compress_segments": [_vp, _u64, _vp, _vp, _vp, _u32, _u64, _u32, _u32, _vp, _vp, _vp, _u64,
+                              _vp, _vp, _vp],
     "ibp_compact_offsets": [_vp, _u64, _vp, _vp],
     "ibp_compact": [_vp, _u64, _u64, _vp, _vp, _u64, _vp],
     "ibp_gather_decompress": [_vp, _u64, _u64, _vp, _vp, _u64, _vp, _u64, _u32, _u32, _vp, _vp,
@@ -125,6 +127,21 @@ def compress(rows, row_stride, n_rows, first_tensor, n_tensors, tensor_bytes, ch
     _check(_lib.ibp_compress(_ptr(rows), row_stride, n_rows, first_tensor, n_tensors,
                              tensor_bytes, chunk_bytes, _ptr(mask), _ptr(bitval), _ptr(store),
                              slot_bytes, _ptr(part_bits), _ptr(lengths), _stream(stream)))
+
+
+def compress_segments(rows, row_stride, seg_row, seg_first, seg_count, n_tensors, tensor_bytes,
+                      chunk_bytes, masks, bitvals, store, slot_bytes, part_bits, lengths,
+                      stream=None):
+    """seg_row, seg_first, seg_count: host sequences of one entry per segment."""
+    arrs = [np.ascontiguousarray(np.asarray(x, dtype=np.uint64)) for x in (seg_row, seg_first,
+                                                                           seg_count)]
+    n = arrs[0].size
+    if any(a.size != n for a in arrs):
+        raise ValueError("seg_row, seg_first and seg_count must have one entry per segment")
+    _check(_lib.ibp_compress_segments(
+        _ptr(rows), row_stride, *[a.ctypes.data if n else None for a in arrs], n, n_tensors,
+        tensor_bytes, chunk_bytes, _ptr(masks), _ptr(bitvals), _ptr(store), slot_bytes,
+        _ptr(part_bits), _ptr(lengths), _stream(stream)))
 
 
 def compact_offsets(lengths, n_tensors, offsets, stream=None):

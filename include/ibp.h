@@ -146,6 +146,35 @@ int ibp_compress(const void *rows, uint64_t row_stride, uint64_t n_rows,
                  void *store, uint64_t slot_bytes,
                  uint32_t *part_bits, uint32_t *lengths, void *stream);
 
+/* Most segments one segmented call takes (ibp_compress_segments,
+ * ibp_gather_decompress_segments). */
+#define IBP_MAX_SEGMENTS 256u
+
+/*
+ * ibp_compress_segments -- several ibp_compress calls of one tensor shape in
+ * one launch, each segment with its own Mask and Bitval (compress-on-write of
+ * one decode token's new K/V rows for every (layer, K|V) pair, [JH] LLM
+ * paragraph).  Segment k compresses rows seg_row[k] + i of `rows` (at
+ * rows + (seg_row[k] + i) * row_stride) as tensors seg_first[k] + i,
+ * i < seg_count[k], with the Mask words at masks + k*W and the Bitval words
+ * at bitvals + k*W (W = tensor_bytes / 4).  Store, bitmap, lengths and slot
+ * layout as in ibp_compress.  Same bytes as one ibp_compress call per segment.
+ *   seg_row, seg_first, seg_count  HOST uint64[n_segments]; seg_count[k] <
+ *               2^32 and seg_first[k] + seg_count[k] <= n_tensors.  Empty
+ *               segments are allowed.  Segments that share a tensor race.
+ *   n_segments  1 .. IBP_MAX_SEGMENTS.
+ *   masks, bitvals  device uint32[n_segments * W] each.
+ * Errors: as ibp_compress; n_segments out of range or a segment past
+ * n_tensors (IBP_ERR_SIZE).
+ */
+int ibp_compress_segments(const void *rows, uint64_t row_stride,
+                          const uint64_t *seg_row, const uint64_t *seg_first,
+                          const uint64_t *seg_count, uint32_t n_segments,
+                          uint64_t n_tensors, uint32_t tensor_bytes,
+                          uint32_t chunk_bytes, const uint32_t *masks,
+                          const uint32_t *bitvals, void *store, uint64_t slot_bytes,
+                          uint32_t *part_bits, uint32_t *lengths, void *stream);
+
 /*
  * ibp_compact_offsets -- [G-EN] System Integration, cache compression.
  * offsets[0] = 0, offsets[t+1] = offsets[t] + roundup(lengths[t], 16) for
@@ -237,7 +266,6 @@ int ibp_gather_decompress_ex(const void *store, uint64_t store_bytes,
  * Errors: as ibp_gather_decompress; n_segments out of range, seg_ids[0] != 0
  * or decreasing (IBP_ERR_SIZE).
  */
-#define IBP_MAX_SEGMENTS 256u
 int ibp_gather_decompress_segments(const void *store, uint64_t store_bytes,
                                    uint64_t slot_bytes, const uint64_t *offsets,
                                    const uint32_t *part_bits, uint64_t n_tensors,

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(ibp):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     out = subprocess.run(["nm", "-D", "--defined-only", ibp.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (ibp_\w+)$", out, flags=re.M))
@@ -88,6 +88,18 @@ def test_compress_validation(ibp):
     _expect(ibp, ibp.ERR_SIZE, f, *args(slot=496))
     _expect(ibp, ibp.ERR_SIZE, f, *args(stride=508))
     _expect(ibp, ibp.ERR_ALIGN, f, *args(store=P + 8))
+    # ibp_compress_segments: the host segment tables
+    fs = ibp.compress_segments
+
+    def seg(row, first, count, nt=10, stride=512, slot=512, store=P):
+        return [P, stride, row, first, count, nt, 512, 256, P, P, store, slot, P, P]
+    _expect(ibp, ibp.ERR_SIZE, fs, *seg([], [], []))                 # no segment
+    _expect(ibp, ibp.ERR_SIZE, fs, *seg([0] * 257, [0] * 257, [1] * 257))
+    _expect(ibp, ibp.ERR_SIZE, fs, *seg([0, 5], [0, 8], [4, 3]))    # 8 + 3 > 10 tensors
+    _expect(ibp, ibp.ERR_SIZE, fs, *seg([0], [0], [4], stride=0))
+    _expect(ibp, ibp.ERR_SIZE, fs, *seg([0], [0], [4], slot=520))
+    _expect(ibp, ibp.ERR_ALIGN, fs, *seg([0], [0], [4], store=P + 8))
+    _expect(ibp, ibp.ERR_NULL, fs, *seg([0], [0], [4], store=0))
 
 
 def test_gather_validation(ibp):

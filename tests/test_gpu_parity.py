@@ -348,6 +348,48 @@ def test_segments():
         assert (got == want).all(), (key, "cache")
 
 
+@pytest.mark.parametrize("key", ["kv_opt13b", "dense_gnn"])
+def test_compress_segments(key):
+    """ibp_compress_segments: each segment compressed with its own Mask and
+    Bitval gives the oracle's payloads, bitmap bits and lengths for its
+    tensors; an empty segment; rows taken at any offset of a larger buffer."""
+    from host_transfer_amd import ibp
+    w = W.WORKLOADS[key]
+    R = 200
+    if key == "kv_opt13b":
+        rows = np.concatenate([W.rows(w, p * W.KV_ROWS_PER_PAIR, R) for p in range(3)])
+        samples = [W.kv_prefill_rows(w, p, 1500) for p in range(3)]
+        Ts = [w.threshold] * 3
+    else:
+        rows = W.rows(w, 0, 3 * R)
+        samples = [rows[:R], rows[R:2 * R], rows[2 * R:]]
+        Ts = [0.99, 0.9, 0.75]
+    n, B = rows.shape
+    C, S = w.chunk_bytes, w.slot_bytes
+    masks, bitvals = [], []
+    for p in range(3):
+        m, v = G.check_metadata(samples[p], Ts[p])
+        masks.append(m), bitvals.append(v)
+    # segments: tensors [p*R + 7, p*R + 7 + count) from rows at the same index, one empty
+    seg_row = [2 * R + 7, 0 * R + 7, 5, 1 * R + 7]
+    seg_first = [2 * R + 7, 0 * R + 7, 0, 1 * R + 7]
+    seg_count = [150, 120, 0, R - 7]
+    seg_mask = [2, 0, 0, 1]
+    store = torch.full((n * S,), 0xA5 - 256, dtype=torch.int8, device="cuda")
+    part = torch.zeros((n * ibp.num_chunks(B, C) + 31) // 32, dtype=torch.int32, device="cuda")
+    lengths = torch.zeros(n, dtype=torch.int32, device="cuda")
+    G.log(f"[parity] compress segments {key}: {len(seg_row)} segments")
+    ibp.compress_segments(G.dev(rows), B, seg_row, seg_first, seg_count, n, B, C,
+                          G.dev(np.concatenate([masks[k] for k in seg_mask])),
+                          G.dev(np.concatenate([bitvals[k] for k in seg_mask])), store, S, part,
+                          lengths)
+    torch.cuda.synchronize()
+    for r0, f, c, k in zip(seg_row, seg_first, seg_count, seg_mask):
+        if c:
+            G.check_store(rows[r0:r0 + c], masks[k], bitvals[k], C, S, store, part, lengths,
+                          first=f, n_tensors=n)
+
+
 def test_deterministic_and_store_bound():
     w = W.WORKLOADS["dense_gnn"].scaled(2000)
     rows = W.rows(w)
