@@ -47,8 +47,8 @@ HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E
 # and spacing aside) still hash to GATHER_SOURCES_SHA256, else traffic is null.
 GATHER_SOURCES = ("host_transfer_amd/csrc/gather.hip", "host_transfer_amd/csrc/ibp_plan.h",
                   "host_transfer_amd/csrc/ibp_device.h")
-GATHER_SOURCES_SHA256 = "0fb2a66d2489757f761ec5d2f41fe76be7a64be7c408dd59319584098fff5be8"
-TRAFFIC_FETCH_KIB, TRAFFIC_WRITE_KIB = 6168.5, 48514.9  # sparse_gnn, 8,192 ids
+GATHER_SOURCES_SHA256 = "82915d8512cbdecb9825bc13f3db66418629d2d5e4fff5594ceb6dd0d4dc623f"
+TRAFFIC_FETCH_KIB, TRAFFIC_WRITE_KIB = 6168.5, 48490.3  # sparse_gnn, 8,192 ids
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 
 
