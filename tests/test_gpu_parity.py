@@ -125,6 +125,53 @@ def test_geometry_sweep(B, C):
                                                                 np.array([n - 1])])
 
 
+@pytest.mark.parametrize("case", range(12))
+def test_random_shapes(case):
+    """Seeded random shapes across the kernel choices: tensor size (tile,
+    direct or group kernel), chunk size, threshold, value law, batch size
+    (short and long launches), ids with repeats and invalid entries; slots
+    (device or pinned) and the compacted cache, against the oracle."""
+    from host_transfer_amd import ibp
+    from oracle import oracle as O
+    rng = np.random.default_rng(1000 + case)
+    W_ = int(rng.choice([1, 17, 64, 100, 128, 200, 256, 257, 700, 1433, 2560, 4096]))
+    B = 4 * W_
+    C = int(rng.choice([256, 1024, 4096]))
+    T = float(rng.choice([0.6, 0.9, 0.99, 1.0]))
+    n = int(min(1500, max(8, 2_000_000 // B)))
+    law = rng.integers(0, 3)
+    if law == 0:
+        x = (rng.standard_normal((n, W_)) * rng.uniform(0.05, 2.0, W_)).astype(np.float32)
+    elif law == 1:
+        x = (rng.random((n, W_)) < 0.03).astype(np.float32)
+    else:
+        x = rng.uniform(-0.05, 0.05, (n, W_)).astype(np.float32)
+    rows = x.view(np.uint8).reshape(n, B)
+    slot = (B + 127) // 128 * 128
+    pinned = bool(rng.integers(0, 2))
+    nb = int(rng.choice([1, 333, 4096, 40000 if B <= 1024 else 3000]))
+    ids = rng.integers(-2, n + 2, nb)
+    G.log(f"[parity] random case {case}: B={B} C={C} T={T} n={n} ids={nb} pinned={pinned}")
+    mask, bitval = G.check_metadata(rows, T)
+    store, part, lens = G.gpu_compress(rows, mask, bitval, C, slot, pinned=pinned)
+    o_store, o_part, o_len = G.check_store(rows, mask, bitval, C, slot, store, part, lens)
+    want = G.expected_rows(rows, ids)
+    got = G.gpu_gather(store, n * slot, slot, None, part, n, ids, B, C, mask, bitval)
+    assert (got == want).all(), "slots"
+    ok = (ids >= 0) & (ids < n)
+    ora = O.gather_decompress(o_store, o_part, n, ids[ok], B, C, mask, bitval, slot_bytes=slot)
+    assert (got[ok] == ora).all(), "oracle"
+    offsets = torch.zeros(n + 1, dtype=torch.int64, device="cuda")
+    ibp.compact_offsets(lens, n, offsets)
+    total = int(offsets[-1].item())
+    cache = torch.zeros(max(total, 16), dtype=torch.uint8, device="cuda")
+    ibp.compact(store, slot, n, offsets, cache, total)
+    got = G.gpu_gather(cache, total, 0, offsets, part, n, ids, B, C, mask, bitval)
+    assert (got == want).all(), "cache"
+    if pinned:
+        store.free()
+
+
 # ------------------------------------------------------------ degenerate cases
 
 def test_mask_zero_and_all_ones():
