@@ -577,6 +577,65 @@ def measure_pinned(torch, ibp, W, key, flags, args, pr):
     return res, table
 
 
+def measure_multi_table(torch, ibp, W, table, args, n_tables=8):
+    """Embedding lookups in several tables at once ([JH] DLRM paragraph): the
+    workload's tensors split into n_tables tables of equal size, one Zipf batch
+    per table (the workload's batch size and law over that table), gathered in
+    one ibp_gather_decompress_segments launch (one segment per table, each
+    with its Mask) against one ibp_gather_decompress launch per table.  The
+    tables here share the workload's Mask, which changes no timing."""
+    import numpy as np
+    w = table.w
+    B, S, N = w.tensor_bytes, w.slot_bytes, w.n_tensors
+    per = N // n_tables
+    wt = w.scaled(per)
+    steps = max(3, min(args.steps, 20))
+    sets = []
+    for k in range(args.warmup + steps):
+        ids = [W.batch_ids(wt, k * n_tables + t) + t * per for t in range(n_tables)]
+        sets.append(ids)
+    d_all = [torch.from_numpy(np.concatenate(ids)).cuda() for ids in sets]
+    d_each = [[torch.from_numpy(i).cuda() for i in ids] for ids in sets]
+    nb = [len(i) for i in sets[0]]
+    seg = np.concatenate([[0], np.cumsum(nb)]).astype(np.uint64)
+    n_all = int(seg[-1])
+    masks = table.mask.repeat(n_tables)
+    bitvals = table.bitval.repeat(n_tables)
+    out = torch.empty(n_all * B, dtype=torch.uint8, device="cuda")
+
+    def one(k):
+        ibp.gather_decompress_segments(table.store, table.store_bytes, S, table.offsets, table.part,
+                                       N, d_all[k], seg, B, w.chunk_bytes, masks, bitvals, out)
+
+    def separate(k):
+        for t in range(n_tables):
+            ibp.gather_decompress(table.store, table.store_bytes, S, table.offsets, table.part, N,
+                                  d_each[k][t], nb[t], B, w.chunk_bytes, table.mask, table.bitval,
+                                  out[int(seg[t]) * B:])
+    def separate_routed(k):
+        for t in range(n_tables):
+            ibp.gather_decompress_ex(table.store, table.store_bytes, S, table.offsets, table.part,
+                                     N, d_each[k][t], nb[t], B, w.chunk_bytes, table.mask,
+                                     table.bitval, out[int(seg[t]) * B:], ibp.GATHER_ROUTE_XCD)
+    one_ms, _ = region_launches(torch, one, args.warmup, steps)
+    sep_ms, _ = region_launches(torch, separate, args.warmup, steps)
+    sepr_ms, _ = region_launches(torch, separate_routed, args.warmup, steps)
+    one(len(sets) - 1)
+    torch.cuda.synchronize()
+    ids_last = np.concatenate(sets[-1])
+    pick = np.linspace(0, n_all - 1, 128).astype(np.int64)
+    got = out.view(n_all, B)[torch.from_numpy(pick).cuda()].cpu().numpy()
+    want = table.raw.array.reshape(N, S)[ids_last[pick], :B]
+    if not (got == want).all():
+        raise SystemExit("bench: the multi-table gather differs from the original rows")
+    del out, d_all, d_each
+    return {"tables": n_tables, "rows_per_table": per, "ids_per_table": nb[0],
+            "one_launch_us": round(one_ms * 1e3, 2),
+            "separate_launches_us": round(sep_ms * 1e3, 2),
+            "speedup_one_launch": round(sep_ms / one_ms, 3),
+            "separate_routed_launches_us": round(sepr_ms * 1e3, 2)}
+
+
 def measure_hybrid(torch, ibp, table, batches, ids_host, args, budget_fraction):
     """Cache + store in one launch at a fixed HBM budget: compressed tensors
     against uncompressed ones (the same kernel with Mask = 0 over the raw
@@ -1170,6 +1229,9 @@ def main():
     pinned = [] if args.pinned_workloads == "none" else args.pinned_workloads.split(",")
     for key in pinned + [k for k in hbm if k not in pinned]:
         res, tb = measure_pinned(torch, ibp, W, key, flags, args, pr)
+        if key == "dlrm_1k" and key in pinned:
+            res["multi_table"] = measure_multi_table(torch, ibp, W, tb, args)
+            log(f"{key} multi-table: {res['multi_table']}")
         if key in pinned:
             result["pinned_path"].append(res)
         if key in hbm:

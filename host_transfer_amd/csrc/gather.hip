@@ -682,7 +682,7 @@ __device__ __forceinline__ void decode_full_tile(const GatherArgs& a, const Word
 // per lane: LPR >= the payload's units).  FULL: W == 64*J, so every lane has
 // a word in every j.
 template <int J, int T, int RPI, bool FULL>
-__global__ __launch_bounds__(256) void k_gather_tile(GatherArgs a) {
+__device__ __forceinline__ void tile_body(GatherArgs& a, uint32_t block, uint32_t blocks) {
   constexpr uint32_t LPR = kWave / RPI;
   constexpr int NL = T / RPI;  // load instructions per tile
   extern __shared__ __align__(16) uint8_t smem[];
@@ -699,8 +699,8 @@ __global__ __launch_bounds__(256) void k_gather_tile(GatherArgs a) {
   const uint32_t W = a.sh.W;
   const uint64_t n_tiles = (a.n_ids + T - 1) / T;
   const uint64_t n_full = a.n_ids / T;  // tiles whose T rows all exist
-  const uint64_t waves = (uint64_t)gridDim.x * (blockDim.x / kWave);
-  const uint64_t tile0 = (uint64_t)blockIdx.x * (blockDim.x / kWave) + wave;
+  const uint64_t waves = (uint64_t)blocks * (blockDim.x / kWave);
+  const uint64_t tile0 = (uint64_t)block * (blockDim.x / kWave) + wave;
   const uint32_t mrow = lane % T;  // the tile row this lane's metadata is for
 
   // Tile metadata runs ahead of the payloads: ids three tiles ahead, bitmap
@@ -833,6 +833,27 @@ __global__ __launch_bounds__(256) void k_gather_tile(GatherArgs a) {
 }
 
 template <int J, int T, int RPI, bool FULL>
+__global__ __launch_bounds__(256) void k_gather_tile(GatherArgs a) {
+  tile_body<J, T, RPI, FULL>(a, blockIdx.x, gridDim.x);
+}
+
+// The tile kernel over segments, as k_gather_decompress_seg (many embedding
+// tables, each with its own Mask, in one launch).
+template <int J, int T, int RPI, bool FULL>
+__global__ __launch_bounds__(256) void k_gather_tile_seg(GatherArgs a, SegTable t) {
+  const uint32_t seg = blockIdx.x / t.per_seg;  // < n_seg: the grid is n_seg * per_seg
+  const uint64_t o = t.off[seg], n = t.off[seg + 1] - o;
+  if (n == 0) return;  // the whole workgroup, before any barrier
+  GatherArgs b = a;
+  b.ids = a.ids + o;
+  b.n_ids = n;
+  b.out = a.out + o * a.sh.W;
+  b.mask = a.mask + (uint64_t)seg * a.sh.W;
+  b.bitval = a.bitval + (uint64_t)seg * a.sh.W;
+  tile_body<J, T, RPI, FULL>(b, blockIdx.x % t.per_seg, t.per_seg);
+}
+
+template <int J, int T, int RPI, bool FULL>
 static hipError_t launch_tile(const Geometry& g, GatherArgs a, hipStream_t s) {
   a.sh.group = kWave;  // lane l owns words l + 64j
   const uint32_t waves = 4;
@@ -854,6 +875,53 @@ static hipError_t launch_tile(const Geometry& g, GatherArgs a, hipStream_t s) {
   const uint32_t blocks = (uint32_t)(want < cap ? want : cap);
   hipLaunchKernelGGL((k_gather_tile<J, T, RPI, FULL>), dim3(blocks), dim3(waves * 64), lds, s, a);
   return hipGetLastError();
+}
+
+template <int J, int T, int RPI, bool FULL>
+static hipError_t launch_tile_seg(const Geometry& g, GatherArgs a, SegTable& t, uint64_t max_rows,
+                                  hipStream_t s) {
+  a.sh.group = kWave;
+  const uint32_t waves = 4;
+  const GatherLds L(g.W, a.pbuf_bytes);
+  const uint32_t shared_plan = T / RPI == 2 ? 20u * g.W : 0u;
+  const uint32_t lds = L.group0 + waves * (2 * T * (uint32_t)sizeof(TileHdr) + T * a.pbuf_bytes) +
+                       shared_plan;
+  DeviceInfo di;
+  hipError_t e = device_info(&di);
+  if (e != hipSuccess) return e;
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gather_tile_seg<J, T, RPI, FULL>,
+                                                   waves * 64, lds);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) return hipErrorInvalidConfiguration;
+  // the resident capacity shared evenly by the segments, but no more
+  // workgroups per segment than its largest one has tiles for
+  const uint64_t cap = (uint64_t)per_cu * (uint64_t)di.cus;
+  uint64_t per = cap / t.n_seg;
+  const uint64_t need = ((max_rows + T - 1) / T + waves - 1) / waves;
+  if (per > need) per = need;
+  if (per < 1) per = 1;
+  t.per_seg = (uint32_t)per;
+  hipLaunchKernelGGL((k_gather_tile_seg<J, T, RPI, FULL>), dim3((uint32_t)(per * t.n_seg)),
+                     dim3(waves * 64), lds, s, a, t);
+  return hipGetLastError();
+}
+
+// Segmented launches of small tensors: tiles of 8 loads when the whole
+// launch fills every CU with such tiles, else 2 (as launch_small).
+template <int J, int RPI>
+static hipError_t launch_small_seg(const Geometry& g, const GatherArgs& a, SegTable& t,
+                                   uint64_t max_rows, hipStream_t s) {
+  DeviceInfo di;
+  hipError_t e = device_info(&di);
+  if (e != hipSuccess) return e;
+  const bool full = g.W == (uint32_t)kWave * J;
+  const bool big = a.n_ids >= (uint64_t)8 * RPI * 8 * (uint64_t)di.cus;
+  if (big)
+    return full ? launch_tile_seg<J, IBP_BIG_NL * RPI, RPI, true>(g, a, t, max_rows, s)
+                : launch_tile_seg<J, IBP_BIG_NL * RPI, RPI, false>(g, a, t, max_rows, s);
+  return full ? launch_tile_seg<J, 2 * RPI, RPI, true>(g, a, t, max_rows, s)
+              : launch_tile_seg<J, 2 * RPI, RPI, false>(g, a, t, max_rows, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -1379,9 +1447,8 @@ hipError_t launch_gather_segments(const Geometry& g, const uint8_t* store, uint6
                                   hipStream_t s) {
   const uint64_t n_ids = seg_off[n_seg];
   if (n_ids == 0) return hipSuccess;
-  if (n_tensors == 0 || g.W <= 4 * (uint32_t)kWave) {
-    // no tensors (zero rows), or small tensors (tile kernels): one launch
-    // per non-empty segment
+  if (n_tensors == 0) {
+    // no tensors: every row is zero (one fill per non-empty segment)
     for (uint32_t k = 0; k < n_seg; ++k) {
       const uint64_t o = seg_off[k], n = seg_off[k + 1] - o;
       if (n == 0) continue;
@@ -1418,6 +1485,16 @@ hipError_t launch_gather_segments(const Geometry& g, const uint8_t* store, uint6
     max_rows = seg_off[k + 1] - seg_off[k] > max_rows ? seg_off[k + 1] - seg_off[k] : max_rows;
   t.n_seg = n_seg;
   t.per_seg = 1;
+  if (g.W <= 4 * (uint32_t)kWave) {
+    // small tensors: the tile kernel, lane l owns words l + 64j
+    switch ((g.W + kWave - 1) / kWave) {
+      case 1: return launch_small_seg<1, 4>(g, a, t, max_rows, s);
+      case 2: return launch_small_seg<2, 2>(g, a, t, max_rows, s);
+      case 3: return launch_small_seg<3, 1>(g, a, t, max_rows, s);
+      case 4: return launch_small_seg<4, 1>(g, a, t, max_rows, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (g.J) {
     case 1: return launch_j_seg<1>(g, a, t, max_rows, s);
     case 2: return launch_j_seg<2>(g, a, t, max_rows, s);

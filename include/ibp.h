@@ -255,9 +255,8 @@ int ibp_gather_decompress_ex(const void *store, uint64_t store_bytes,
  * The segments share the store or cache, the bitmap and n_tensors, as in
  * ibp_gather_decompress (store, store_bytes, slot_bytes, offsets, part_bits,
  * n_tensors: same meaning).  Same rows as one ibp_gather_decompress call
- * per segment; for tensors of more than 256 words the launch's fixed cost is
- * paid once for all segments (tensors of up to 256 words: one launch per
- * non-empty segment).
+ * per segment; the launch's fixed cost is paid once for all segments (also
+ * for many embedding tables with one Mask each: [JH] DLRM paragraph).
  *   seg_ids     HOST uint64[n_segments + 1], seg_ids[0] = 0, non-decreasing;
  *               n_ids = seg_ids[n_segments].  Empty segments are allowed.
  *   n_segments  1 .. IBP_MAX_SEGMENTS.

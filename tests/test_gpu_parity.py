@@ -321,7 +321,7 @@ def test_side_stream_and_graph_replay():
             del graph
 
 
-def _segment_case(rows, masks, bitvals, parts, B, C, S, n, rng, mode, cache=None):
+def _segment_case(rows, masks, bitvals, parts, B, C, S, n, rng, mode, per_seg=300):
     """One segmented gather over `parts` = [(first, count) of the tensors
     compressed with mask k]; segment order shuffled, plus an empty segment and
     invalid ids.  Returns (got, want)."""
@@ -335,7 +335,7 @@ def _segment_case(rows, masks, bitvals, parts, B, C, S, n, rng, mode, cache=None
             seg_ids.append(seg_ids[-1])
             continue
         first, count = parts[k]
-        x = rng.integers(first, first + count, 300)
+        x = rng.integers(first, first + count, per_seg)
         x[:3] = [first, first + count - 1, -1]
         ids.append(x)
         m_all.append(masks[k]), v_all.append(bitvals[k])
@@ -366,6 +366,13 @@ def test_segments():
     rows = W.rows(w, 0, 900)
     cases.append(("dense_gnn", rows, [rows[:300], rows[300:600], rows[600:]], [0.99, 0.9, 0.75],
                   w.chunk_bytes, w.slot_bytes))
+    w = W.WORKLOADS["dlrm_1k"]
+    rows = W.rows(w, 0, 900)
+    x = rows.view(np.float32).copy()
+    x[300:600] *= 16.0  # a second table with other exponents
+    rows = x.view(np.uint8)
+    cases.append(("dlrm_1k", rows, [rows[:300], rows[300:600], rows[600:]], [0.99, 0.99, 0.9],
+                  w.chunk_bytes, w.slot_bytes))
     for key, rows, samples, Ts, C, S in cases:
         n, B = rows.shape
         k = len(samples)
@@ -393,6 +400,11 @@ def test_segments():
         got, want = _segment_case(rows, masks, bitvals, parts, B, C, S, n, rng,
                                   (cache, part, offsets, total, 0))
         assert (got == want).all(), (key, "cache")
+        # long launches (the tile kernel's 8-load tiles for small tensors)
+        G.log(f"[parity] segments {key}: {k} masks, 15,000 ids per segment")
+        got, want = _segment_case(rows, masks, bitvals, parts, B, C, S, n, rng,
+                                  (store, part, None, n * S, S), per_seg=15000)
+        assert (got == want).all(), (key, "long")
 
 
 @pytest.mark.parametrize("key", ["kv_opt13b", "dense_gnn"])
