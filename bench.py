@@ -582,7 +582,8 @@ def measure_multi_table(torch, ibp, W, table, args, n_tables=8):
     workload's tensors split into n_tables tables of equal size, one Zipf batch
     per table (the workload's batch size and law over that table), gathered in
     one ibp_gather_decompress_segments launch (one segment per table, each
-    with its Mask) against one ibp_gather_decompress launch per table.  The
+    with its Mask) against one ibp_gather_decompress launch per table, each
+    way with and without XCD routing.  The
     tables here share the workload's Mask, which changes no timing."""
     import numpy as np
     w = table.w
@@ -603,9 +604,13 @@ def measure_multi_table(torch, ibp, W, table, args, n_tables=8):
     bitvals = table.bitval.repeat(n_tables)
     out = torch.empty(n_all * B, dtype=torch.uint8, device="cuda")
 
-    def one(k):
+    def one(k, flags=0):
         ibp.gather_decompress_segments(table.store, table.store_bytes, S, table.offsets, table.part,
-                                       N, d_all[k], seg, B, w.chunk_bytes, masks, bitvals, out)
+                                       N, d_all[k], seg, B, w.chunk_bytes, masks, bitvals, out,
+                                       flags)
+
+    def one_routed(k):
+        one(k, ibp.GATHER_ROUTE_XCD)
 
     def separate(k):
         for t in range(n_tables):
@@ -618,22 +623,27 @@ def measure_multi_table(torch, ibp, W, table, args, n_tables=8):
                                      N, d_each[k][t], nb[t], B, w.chunk_bytes, table.mask,
                                      table.bitval, out[int(seg[t]) * B:], ibp.GATHER_ROUTE_XCD)
     one_ms, _ = region_launches(torch, one, args.warmup, steps)
+    oner_ms, _ = region_launches(torch, one_routed, args.warmup, steps)
     sep_ms, _ = region_launches(torch, separate, args.warmup, steps)
     sepr_ms, _ = region_launches(torch, separate_routed, args.warmup, steps)
-    one(len(sets) - 1)
-    torch.cuda.synchronize()
     ids_last = np.concatenate(sets[-1])
     pick = np.linspace(0, n_all - 1, 128).astype(np.int64)
-    got = out.view(n_all, B)[torch.from_numpy(pick).cuda()].cpu().numpy()
     want = table.raw.array.reshape(N, S)[ids_last[pick], :B]
-    if not (got == want).all():
-        raise SystemExit("bench: the multi-table gather differs from the original rows")
+    for f in (one, one_routed):
+        out.zero_()
+        f(len(sets) - 1)
+        torch.cuda.synchronize()
+        got = out.view(n_all, B)[torch.from_numpy(pick).cuda()].cpu().numpy()
+        if not (got == want).all():
+            raise SystemExit("bench: the multi-table gather differs from the original rows")
     del out, d_all, d_each
     return {"tables": n_tables, "rows_per_table": per, "ids_per_table": nb[0],
             "one_launch_us": round(one_ms * 1e3, 2),
+            "one_launch_routed_us": round(oner_ms * 1e3, 2),
             "separate_launches_us": round(sep_ms * 1e3, 2),
             "speedup_one_launch": round(sep_ms / one_ms, 3),
-            "separate_routed_launches_us": round(sepr_ms * 1e3, 2)}
+            "separate_routed_launches_us": round(sepr_ms * 1e3, 2),
+            "speedup_one_launch_routed": round(sepr_ms / oner_ms, 3)}
 
 
 def measure_hybrid(torch, ibp, table, batches, ids_host, args, budget_fraction):

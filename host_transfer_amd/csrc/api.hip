@@ -325,9 +325,13 @@ int ibp_gather_decompress_segments(const void* store, uint64_t store_bytes, uint
                                    const uint64_t* seg_ids, uint32_t n_segments,
                                    uint32_t tensor_bytes, uint32_t chunk_bytes,
                                    const uint32_t* masks, const uint32_t* bitvals, void* out,
-                                   void* stream) {
+                                   unsigned flags, void* stream) {
   static_assert(ibp::kMaxSegments == IBP_MAX_SEGMENTS, "segment limit");
   const char* name = "ibp_gather_decompress_segments";
+  if (flags & ~IBP_GATHER_ROUTE_XCD) return fail(IBP_ERR_FLAGS, "%s: unknown flags", name);
+  const bool route = (flags & IBP_GATHER_ROUTE_XCD) != 0;
+  if (route && offsets)
+    return fail(IBP_ERR_FLAGS, "%s: routing applies to slot mode (no offsets)", name);
   if (!store || !part_bits || !ids || !seg_ids || !masks || !bitvals || !out)
     return fail(IBP_ERR_NULL, "%s: a required pointer is null", name);
   if (n_segments == 0 || n_segments > IBP_MAX_SEGMENTS)
@@ -351,6 +355,8 @@ int ibp_gather_decompress_segments(const void* store, uint64_t store_bytes, uint
       return fail(IBP_ERR_SIZE, "%s: store_bytes < n_tensors * slot_bytes", name);
   }
   if (n_ids > UINT64_MAX / tensor_bytes) return fail(IBP_ERR_SIZE, "%s: n_ids too large", name);
+  if (route && n_ids >= (1ull << 32))
+    return fail(IBP_ERR_SIZE, "%s: routing needs n_ids < 2^32", name);
   if (!aligned(store, 16) || !aligned(out, 16) || !aligned(ids, 8) || !aligned(masks, 4) ||
       !aligned(bitvals, 4) || !aligned(part_bits, 4) || (offsets && !aligned(offsets, 8)))
     return fail(IBP_ERR_ALIGN, "%s: misaligned pointer", name);
@@ -359,10 +365,10 @@ int ibp_gather_decompress_segments(const void* store, uint64_t store_bytes, uint
   hipError_t e = offsets
       ? ibp::launch_gather_segments(g, nullptr, 0, 0, offsets, (const uint8_t*)store, store_bytes,
                                     part_bits, n_tensors, ids, seg_ids, n_segments, masks,
-                                    bitvals, (uint32_t*)out, (hipStream_t)stream)
+                                    bitvals, (uint32_t*)out, false, (hipStream_t)stream)
       : ibp::launch_gather_segments(g, (const uint8_t*)store, store_bytes, slot_bytes, nullptr,
                                     nullptr, 0, part_bits, n_tensors, ids, seg_ids, n_segments,
-                                    masks, bitvals, (uint32_t*)out, (hipStream_t)stream);
+                                    masks, bitvals, (uint32_t*)out, route, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, name);
   return ok();
 }

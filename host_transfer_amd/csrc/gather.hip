@@ -354,17 +354,25 @@ struct SegTable {
   uint32_t per_seg;
 };
 
-template <int J>
-__global__ __launch_bounds__(1024) void k_gather_decompress_seg(GatherArgs a, SegTable t) {
-  const uint32_t seg = blockIdx.x / t.per_seg;  // < n_seg: the grid is n_seg * per_seg
+// The arguments of the segment that this workgroup serves (segment
+// blockIdx.x / per_seg; the grid is n_seg * per_seg); false when it is empty.
+__device__ __forceinline__ bool segment_args(const GatherArgs& a, const SegTable& t,
+                                             GatherArgs& b) {
+  const uint32_t seg = blockIdx.x / t.per_seg;
   const uint64_t o = t.off[seg], n = t.off[seg + 1] - o;
-  GatherArgs b = a;
+  b = a;
   b.ids = a.ids + o;
   b.n_ids = n;
   b.out = a.out + o * a.sh.W;
   b.mask = a.mask + (uint64_t)seg * a.sh.W;
   b.bitval = a.bitval + (uint64_t)seg * a.sh.W;
-  if (n == 0) return;  // the whole workgroup, before any barrier
+  return n != 0;
+}
+
+template <int J>
+__global__ __launch_bounds__(1024) void k_gather_decompress_seg(GatherArgs a, SegTable t) {
+  GatherArgs b;
+  if (!segment_args(a, t, b)) return;  // the whole workgroup, before any barrier
   gather_group_body<J>(b, blockIdx.x % t.per_seg, t.per_seg);
 }
 
@@ -379,8 +387,12 @@ __host__ __device__ constexpr uint32_t routed_group_list_bytes() {
   return (uint32_t)kWave * 12u + 16u;  // ids, rows, count
 }
 
+// Workgroup `block` of `blocks` (a multiple of 8) must run on XCD block % 8:
+// the whole grid, or one segment of k_gather_decompress_routed_seg whose
+// per_seg is a multiple of 8.
 template <int J>
-__global__ __launch_bounds__(1024) void k_gather_decompress_routed(GatherArgs a) {
+__device__ __forceinline__ void gather_group_routed_body(GatherArgs& a, uint32_t block,
+                                                         uint32_t blocks) {
   extern __shared__ __align__(16) uint8_t smem[];
   const GatherLds L(a.sh.W, a.pbuf_bytes);
   uint32_t* s_pref = (uint32_t*)(smem + L.pref);
@@ -400,9 +412,9 @@ __global__ __launch_bounds__(1024) void k_gather_decompress_routed(GatherArgs a)
   const bool first_wave = gl < kWave;
   const uint32_t W = a.sh.W;
 
-  const uint32_t xcd = blockIdx.x % kXcds;
-  const uint64_t wc = gridDim.x / kXcds;
-  const uint64_t wk = blockIdx.x / kXcds;
+  const uint32_t xcd = block % kXcds;
+  const uint64_t wc = blocks / kXcds;
+  const uint64_t wk = block / kXcds;
   const uint64_t seg = (a.n_ids + wc - 1) / wc;
   const uint64_t s0 = min(wk * seg, a.n_ids), s1 = min(s0 + seg, a.n_ids);
 
@@ -481,6 +493,20 @@ __global__ __launch_bounds__(1024) void k_gather_decompress_routed(GatherArgs a)
     }
     __syncthreads();  // the list and its count are rewritten by the next window
   }
+}
+
+template <int J>
+__global__ __launch_bounds__(1024) void k_gather_decompress_routed(GatherArgs a) {
+  gather_group_routed_body<J>(a, blockIdx.x, gridDim.x);
+}
+
+// Routed, over segments: per_seg is a multiple of 8, so a segment's workgroup
+// k runs on XCD k % 8.
+template <int J>
+__global__ __launch_bounds__(1024) void k_gather_decompress_routed_seg(GatherArgs a, SegTable t) {
+  GatherArgs b;
+  if (!segment_args(a, t, b)) return;  // the whole workgroup, before any barrier
+  gather_group_routed_body<J>(b, blockIdx.x % t.per_seg, t.per_seg);
 }
 
 // ---------------------------------------------------------------------------
@@ -841,15 +867,8 @@ __global__ __launch_bounds__(256) void k_gather_tile(GatherArgs a) {
 // tables, each with its own Mask, in one launch).
 template <int J, int T, int RPI, bool FULL>
 __global__ __launch_bounds__(256) void k_gather_tile_seg(GatherArgs a, SegTable t) {
-  const uint32_t seg = blockIdx.x / t.per_seg;  // < n_seg: the grid is n_seg * per_seg
-  const uint64_t o = t.off[seg], n = t.off[seg + 1] - o;
-  if (n == 0) return;  // the whole workgroup, before any barrier
-  GatherArgs b = a;
-  b.ids = a.ids + o;
-  b.n_ids = n;
-  b.out = a.out + o * a.sh.W;
-  b.mask = a.mask + (uint64_t)seg * a.sh.W;
-  b.bitval = a.bitval + (uint64_t)seg * a.sh.W;
+  GatherArgs b;
+  if (!segment_args(a, t, b)) return;  // the whole workgroup, before any barrier
   tile_body<J, T, RPI, FULL>(b, blockIdx.x % t.per_seg, t.per_seg);
 }
 
@@ -1146,8 +1165,10 @@ __host__ __device__ inline uint32_t routed_wave_bytes(uint32_t T, uint32_t pbuf_
   return T * (uint32_t)sizeof(TileHdr) + T * pbuf_bytes + ((routed_list_cap(T) * 12u + 15u) & ~15u);
 }
 
+// Workgroup `block` of `blocks` (a multiple of 8) must run on XCD block % 8,
+// as for gather_group_routed_body.
 template <int J, int T, int RPI, bool FULL>
-__global__ __launch_bounds__(256) void k_gather_tile_routed(GatherArgs a) {
+__device__ __forceinline__ void tile_routed_body(GatherArgs& a, uint32_t block, uint32_t blocks) {
   constexpr uint32_t LPR = kWave / RPI;
   constexpr int NL = T / RPI;
   static_assert(NL <= 8, "at most 8 load instructions per tile");
@@ -1167,9 +1188,9 @@ __global__ __launch_bounds__(256) void k_gather_tile_routed(GatherArgs a) {
   uint32_t* list_row = (uint32_t*)(list_id + kCap);                   // [kCap]
 
   // this wave's XCD and segment of the batch (the grid is a multiple of 8)
-  const uint32_t xcd = blockIdx.x % kXcds;
-  const uint64_t wc = (uint64_t)(gridDim.x / kXcds) * wpb;
-  const uint64_t wk = (uint64_t)(blockIdx.x / kXcds) * wpb + wave;
+  const uint32_t xcd = block % kXcds;
+  const uint64_t wc = (uint64_t)(blocks / kXcds) * wpb;
+  const uint64_t wk = (uint64_t)(block / kXcds) * wpb + wave;
   const uint64_t seg = (a.n_ids + wc - 1) / wc;
   const uint64_t s0 = min(wk * seg, a.n_ids), s1 = min(s0 + seg, a.n_ids);
 
@@ -1274,6 +1295,19 @@ __global__ __launch_bounds__(256) void k_gather_tile_routed(GatherArgs a) {
 }
 
 template <int J, int T, int RPI, bool FULL>
+__global__ __launch_bounds__(256) void k_gather_tile_routed(GatherArgs a) {
+  tile_routed_body<J, T, RPI, FULL>(a, blockIdx.x, gridDim.x);
+}
+
+// Routed, over segments (per_seg a multiple of 8, as k_gather_decompress_routed_seg).
+template <int J, int T, int RPI, bool FULL>
+__global__ __launch_bounds__(256) void k_gather_tile_routed_seg(GatherArgs a, SegTable t) {
+  GatherArgs b;
+  if (!segment_args(a, t, b)) return;  // the whole workgroup, before any barrier
+  tile_routed_body<J, T, RPI, FULL>(b, blockIdx.x % t.per_seg, t.per_seg);
+}
+
+template <int J, int T, int RPI, bool FULL>
 static hipError_t launch_tile_routed(const Geometry& g, GatherArgs a, hipStream_t s) {
   a.sh.group = kWave;
   const uint32_t waves = 4;
@@ -1295,6 +1329,47 @@ static hipError_t launch_tile_routed(const Geometry& g, GatherArgs a, hipStream_
   hipLaunchKernelGGL((k_gather_tile_routed<J, T, RPI, FULL>), dim3((uint32_t)blocks),
                      dim3(waves * 64), lds, s, a);
   return hipGetLastError();
+}
+
+// Workgroups per segment of a routed segmented launch: the resident capacity
+// shared evenly by the segments, no more than `need`, rounded down to a
+// multiple of 8 (every XCD class of a segment has the same workgroups), at
+// least 8.
+static uint32_t routed_per_seg(uint64_t cap, uint32_t n_seg, uint64_t need) {
+  uint64_t per = cap / n_seg;
+  if (per > need) per = need;
+  per = per / kXcds * kXcds;
+  return (uint32_t)(per < kXcds ? kXcds : per);
+}
+
+template <int J, int T, int RPI, bool FULL>
+static hipError_t launch_tile_routed_seg(const Geometry& g, GatherArgs a, SegTable& t,
+                                         uint64_t max_rows, hipStream_t s) {
+  a.sh.group = kWave;
+  const uint32_t waves = 4;
+  const GatherLds L(g.W, a.pbuf_bytes);
+  const uint32_t lds = L.group0 + waves * routed_wave_bytes(T, a.pbuf_bytes);
+  DeviceInfo di;
+  hipError_t e = device_info(&di);
+  if (e != hipSuccess) return e;
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      &per_cu, k_gather_tile_routed_seg<J, T, RPI, FULL>, waves * 64, lds);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) return hipErrorInvalidConfiguration;
+  const uint64_t need = ((max_rows + T - 1) / T + waves - 1) / waves;
+  t.per_seg = routed_per_seg((uint64_t)per_cu * (uint64_t)di.cus, t.n_seg, need);
+  hipLaunchKernelGGL((k_gather_tile_routed_seg<J, T, RPI, FULL>), dim3(t.per_seg * t.n_seg),
+                     dim3(waves * 64), lds, s, a, t);
+  return hipGetLastError();
+}
+
+template <int J, int RPI>
+static hipError_t launch_small_routed_seg(const Geometry& g, const GatherArgs& a, SegTable& t,
+                                          uint64_t max_rows, hipStream_t s) {
+  const bool full = g.W == (uint32_t)kWave * J;
+  return full ? launch_tile_routed_seg<J, 2 * RPI, RPI, true>(g, a, t, max_rows, s)
+              : launch_tile_routed_seg<J, 2 * RPI, RPI, false>(g, a, t, max_rows, s);
 }
 
 // Small tensors (W <= 256): rows per load instruction RPI from the payload's
@@ -1411,8 +1486,30 @@ hipError_t launch_gather(const Geometry& g, const uint8_t* store, uint64_t store
 }
 
 template <int J>
+static hipError_t launch_j_routed_seg(const Geometry& g, const GatherArgs& a, const SegTable& t0,
+                                      uint64_t max_rows, hipStream_t s) {
+  const GatherLds L(g.W, a.pbuf_bytes);
+  const uint32_t lds = L.total(1) + routed_group_list_bytes();
+  const uint32_t threads = g.group;
+  DeviceInfo di;
+  hipError_t e = device_info(&di);
+  if (e != hipSuccess) return e;
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gather_decompress_routed_seg<J>,
+                                                   threads, lds);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) return hipErrorInvalidConfiguration;
+  SegTable t = t0;
+  t.per_seg = routed_per_seg((uint64_t)per_cu * (uint64_t)di.cus, t.n_seg, max_rows);
+  hipLaunchKernelGGL(k_gather_decompress_routed_seg<J>, dim3(t.per_seg * t.n_seg), dim3(threads),
+                     lds, s, a, t);
+  return hipGetLastError();
+}
+
+template <int J>
 static hipError_t launch_j_seg(const Geometry& g, const GatherArgs& a, const SegTable& t0,
                                uint64_t max_rows, hipStream_t s) {
+  if (a.route && g.groups == 1) return launch_j_routed_seg<J>(g, a, t0, max_rows, s);
   const GatherLds L(g.W, a.pbuf_bytes);
   const uint32_t lds = L.total(g.groups);
   const uint32_t threads = g.group * g.groups;
@@ -1444,7 +1541,7 @@ hipError_t launch_gather_segments(const Geometry& g, const uint8_t* store, uint6
                                   const uint32_t* part_bits, uint64_t n_tensors,
                                   const int64_t* ids, const uint64_t* seg_off, uint32_t n_seg,
                                   const uint32_t* masks, const uint32_t* bitvals, uint32_t* out,
-                                  hipStream_t s) {
+                                  bool route, hipStream_t s) {
   const uint64_t n_ids = seg_off[n_seg];
   if (n_ids == 0) return hipSuccess;
   if (n_tensors == 0) {
@@ -1476,7 +1573,7 @@ hipError_t launch_gather_segments(const Geometry& g, const uint8_t* store, uint6
   a.out = out;
   a.sh = Shape{g.W, g.n_c, g.wpc_log2, g.last_bits, g.group};
   a.groups = g.groups;
-  a.route = 0;
+  a.route = route && offsets == nullptr && n_ids < (1ull << 32);
   a.pbuf_bytes = ((g.tensor_bytes + 15u) & ~15u) + 16u;
   SegTable t;
   uint64_t max_rows = 0;
@@ -1487,6 +1584,15 @@ hipError_t launch_gather_segments(const Geometry& g, const uint8_t* store, uint6
   t.per_seg = 1;
   if (g.W <= 4 * (uint32_t)kWave) {
     // small tensors: the tile kernel, lane l owns words l + 64j
+    if (a.route) {
+      switch ((g.W + kWave - 1) / kWave) {
+        case 1: return launch_small_routed_seg<1, 4>(g, a, t, max_rows, s);
+        case 2: return launch_small_routed_seg<2, 2>(g, a, t, max_rows, s);
+        case 3: return launch_small_routed_seg<3, 1>(g, a, t, max_rows, s);
+        case 4: return launch_small_routed_seg<4, 1>(g, a, t, max_rows, s);
+        default: return hipErrorInvalidValue;
+      }
+    }
     switch ((g.W + kWave - 1) / kWave) {
       case 1: return launch_small_seg<1, 4>(g, a, t, max_rows, s);
       case 2: return launch_small_seg<2, 2>(g, a, t, max_rows, s);

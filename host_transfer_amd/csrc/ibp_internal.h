@@ -63,7 +63,7 @@ hipError_t launch_gather_segments(const Geometry& g, const uint8_t* store, uint6
                                   const uint32_t* part_bits, uint64_t n_tensors,
                                   const int64_t* ids, const uint64_t* seg_off, uint32_t n_seg,
                                   const uint32_t* masks, const uint32_t* bitvals, uint32_t* out,
-                                  hipStream_t s);
+                                  bool route, hipStream_t s);
 
 hipError_t launch_gather(const Geometry& g, const uint8_t* store, uint64_t store_bytes,
                          uint64_t slot_bytes, const uint64_t* offsets, const uint8_t* cache,

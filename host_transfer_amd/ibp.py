@@ -53,7 +53,7 @@ _SIGS = {
     "ibp_gather_decompress_ex": [_vp, _u64, _u64, _vp, _vp, _u64, _vp, _u64, _u32, _u32, _vp,
                                  _vp, _vp, ctypes.c_uint, _vp],
     "ibp_gather_decompress_segments": [_vp, _u64, _u64, _vp, _vp, _u64, _vp, _vp, _u32, _u32,
-                                       _u32, _vp, _vp, _vp, _vp],
+                                       _u32, _vp, _vp, _vp, _u32, _vp],
     "ibp_cache_offsets": [_vp, _vp, _u64, _vp, _vp],
     "ibp_cache_fill": [_vp, _u64, _vp, _u64, _vp, _vp, _u64, _vp],
     "ibp_gather_decompress_hybrid": [_vp, _u64, _u64, _vp, _u64, _vp, _vp, _u64, _vp, _u64, _u32,
@@ -176,14 +176,15 @@ MAX_SEGMENTS = 256
 
 
 def gather_decompress_segments(store, store_bytes, slot_bytes, offsets, part_bits, n_tensors, ids,
-                               seg_ids, tensor_bytes, chunk_bytes, masks, bitvals, out,
+                               seg_ids, tensor_bytes, chunk_bytes, masks, bitvals, out, flags=0,
                                stream=None):
-    """seg_ids: host sequence of n_segments + 1 row offsets (numpy uint64 or a list)."""
+    """seg_ids: host sequence of n_segments + 1 row offsets (numpy uint64 or a list);
+    flags: 0 or GATHER_ROUTE_XCD."""
     seg = np.ascontiguousarray(np.asarray(seg_ids, dtype=np.uint64))
     _check(_lib.ibp_gather_decompress_segments(
         _ptr(store), store_bytes, slot_bytes, _ptr(offsets), _ptr(part_bits), n_tensors, _ptr(ids),
         seg.ctypes.data if seg.size else None, max(0, seg.size - 1), tensor_bytes, chunk_bytes,
-        _ptr(masks), _ptr(bitvals), _ptr(out), _stream(stream)))
+        _ptr(masks), _ptr(bitvals), _ptr(out), flags, _stream(stream)))
 
 
 def cache_offsets(lengths, select, n_tensors, offsets, stream=None):

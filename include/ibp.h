@@ -262,8 +262,10 @@ int ibp_gather_decompress_ex(const void *store, uint64_t store_bytes,
  *   n_segments  1 .. IBP_MAX_SEGMENTS.
  *   ids         device int64[n_ids];  out  device, n_ids*tensor_bytes bytes.
  *   masks, bitvals  device uint32[n_segments * W] each.
+ *   flags       0 or IBP_GATHER_ROUTE_XCD (as ibp_gather_decompress_ex, each
+ *               segment's rows routed by tensor index; slot mode only).
  * Errors: as ibp_gather_decompress; n_segments out of range, seg_ids[0] != 0
- * or decreasing (IBP_ERR_SIZE).
+ * or decreasing (IBP_ERR_SIZE); as ibp_gather_decompress_ex for flags.
  */
 int ibp_gather_decompress_segments(const void *store, uint64_t store_bytes,
                                    uint64_t slot_bytes, const uint64_t *offsets,
@@ -271,7 +273,8 @@ int ibp_gather_decompress_segments(const void *store, uint64_t store_bytes,
                                    const int64_t *ids, const uint64_t *seg_ids,
                                    uint32_t n_segments, uint32_t tensor_bytes,
                                    uint32_t chunk_bytes, const uint32_t *masks,
-                                   const uint32_t *bitvals, void *out, void *stream);
+                                   const uint32_t *bitvals, void *out, unsigned flags,
+                                   void *stream);
 
 /* ------------------------------------------------------ cache + store together
  * [G-EN] System Integration uses both placements at once: a compressed

@@ -141,6 +141,9 @@ def test_gather_validation(ibp):
     _expect(ibp, ibp.ERR_SIZE, fs, *seg([0, 4], sbytes=10 * 512 - 1))
     _expect(ibp, ibp.ERR_ALIGN, fs, *seg([0, 4], out=P + 4))
     _expect(ibp, ibp.ERR_CHUNK, fs, *seg([0, 4], cb=2048))
+    _expect(ibp, ibp.ERR_FLAGS, fs, *seg([0, 4]), 2)
+    _expect(ibp, ibp.ERR_FLAGS, fs, *seg([0, 4], offs=P), ibp.GATHER_ROUTE_XCD)
+    _expect(ibp, ibp.ERR_SIZE, fs, *seg([0, 1 << 31, 1 << 32]), ibp.GATHER_ROUTE_XCD)
 
 
 def test_other_validation(ibp):

@@ -321,10 +321,12 @@ def test_side_stream_and_graph_replay():
             del graph
 
 
-def _segment_case(rows, masks, bitvals, parts, B, C, S, n, rng, mode, per_seg=300):
+def _segment_case(rows, masks, bitvals, parts, B, C, S, n, rng, mode, per_seg=300, flags=0,
+                  hot=0):
     """One segmented gather over `parts` = [(first, count) of the tensors
     compressed with mask k]; segment order shuffled, plus an empty segment and
-    invalid ids.  Returns (got, want)."""
+    invalid ids.  hot > 0: every segment's ids drawn from its first `hot`
+    tensors only (many repeats, as Zipf lookups).  Returns (got, want)."""
     from host_transfer_amd import ibp
     store, part, offsets, store_bytes, slot = mode
     order = list(rng.permutation(len(parts)))
@@ -335,7 +337,7 @@ def _segment_case(rows, masks, bitvals, parts, B, C, S, n, rng, mode, per_seg=30
             seg_ids.append(seg_ids[-1])
             continue
         first, count = parts[k]
-        x = rng.integers(first, first + count, per_seg)
+        x = rng.integers(first, first + (min(hot, count) if hot else count), per_seg)
         x[:3] = [first, first + count - 1, -1]
         ids.append(x)
         m_all.append(masks[k]), v_all.append(bitvals[k])
@@ -344,16 +346,17 @@ def _segment_case(rows, masks, bitvals, parts, B, C, S, n, rng, mode, per_seg=30
     out = torch.full((len(ids) * B,), -1, dtype=torch.int8, device="cuda")
     ibp.gather_decompress_segments(store, store_bytes, slot, offsets, part, n, G.dev(ids), seg_ids,
                                    B, C, G.dev(np.concatenate(m_all)), G.dev(np.concatenate(v_all)),
-                                   out)
+                                   out, flags)
     got = G.host(out).view(np.uint8).reshape(len(ids), B)
     return got, G.expected_rows(rows, ids)
 
 
 def test_segments():
     """ibp_gather_decompress_segments: every segment decoded with its own
-    Mask/Bitval; one launch for the group kernel (K/V rows), one per segment
-    for the tile kernel (dense_gnn rows); from slots and from a compacted
-    cache; an empty segment and invalid ids."""
+    Mask/Bitval; the group kernel (K/V rows) and the tile kernel (dense_gnn,
+    dlrm_1k rows); from slots and from a compacted cache; XCD-routed from
+    slots (with few distinct ids per segment, and long); an empty segment and
+    invalid ids."""
     from host_transfer_amd import ibp
     rng = np.random.default_rng(31)
     cases = []
@@ -405,6 +408,13 @@ def test_segments():
         got, want = _segment_case(rows, masks, bitvals, parts, B, C, S, n, rng,
                                   (store, part, None, n * S, S), per_seg=15000)
         assert (got == want).all(), (key, "long")
+        route = ibp.GATHER_ROUTE_XCD
+        for per_seg, hot in ((300, 0), (2000, 40), (15000, 0)):
+            G.log(f"[parity] segments {key}: routed, {per_seg} ids per segment, hot {hot}")
+            got, want = _segment_case(rows, masks, bitvals, parts, B, C, S, n, rng,
+                                      (store, part, None, n * S, S), per_seg=per_seg,
+                                      flags=route, hot=hot)
+            assert (got == want).all(), (key, "routed", per_seg, hot)
 
 
 @pytest.mark.parametrize("key", ["kv_opt13b", "dense_gnn"])
