@@ -577,7 +577,7 @@ def measure_pinned(torch, ibp, W, key, flags, args, pr):
     return res, table
 
 
-def measure_multi_table(torch, ibp, W, table, args, n_tables=8):
+def measure_multi_table(torch, ibp, W, table, args, pr, n_tables=8):
     """Embedding lookups in several tables at once ([JH] DLRM paragraph): the
     workload's tensors split into n_tables tables of equal size, one Zipf batch
     per table (the workload's batch size and law over that table), gathered in
@@ -637,7 +637,15 @@ def measure_multi_table(torch, ibp, W, table, args, n_tables=8):
         if not (got == want).all():
             raise SystemExit("bench: the multi-table gather differs from the original rows")
     del out, d_all, d_each
+    # link-side bytes: each distinct tensor of a table's batch once (repeats
+    # are served from the GPU's caches), as for the single-table launches
+    uniq = statistics.mean(sum(float(table.len_host[np.unique(i)].sum()) for i in ids)
+                           for ids in sets[args.warmup:])
+    link = max(pr["h2d_dma_GBps"], pr["h2d_zero_copy_read_GBps"])
     return {"tables": n_tables, "rows_per_table": per, "ids_per_table": nb[0],
+            "unique_bytes_per_launch": round(uniq, 1),
+            "one_launch_routed_unique_frac_of_measured": round(uniq / (oner_ms * 1e-3) / 1e9 /
+                                                               link, 4),
             "one_launch_us": round(one_ms * 1e3, 2),
             "one_launch_routed_us": round(oner_ms * 1e3, 2),
             "separate_launches_us": round(sep_ms * 1e3, 2),
@@ -1240,7 +1248,7 @@ def main():
     for key in pinned + [k for k in hbm if k not in pinned]:
         res, tb = measure_pinned(torch, ibp, W, key, flags, args, pr)
         if key == "dlrm_1k" and key in pinned:
-            res["multi_table"] = measure_multi_table(torch, ibp, W, tb, args)
+            res["multi_table"] = measure_multi_table(torch, ibp, W, tb, args, pr)
             log(f"{key} multi-table: {res['multi_table']}")
         if key in pinned:
             result["pinned_path"].append(res)
