@@ -47,8 +47,8 @@ HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E
 # and spacing aside) still hash to GATHER_SOURCES_SHA256, else traffic is null.
 GATHER_SOURCES = ("host_transfer_amd/csrc/gather.hip", "host_transfer_amd/csrc/ibp_plan.h",
                   "host_transfer_amd/csrc/ibp_device.h")
-GATHER_SOURCES_SHA256 = "a617492361f815ede196d61b0b6e95095007fa3f8d828a60b71f3cf97984ccac"
-TRAFFIC_FETCH_KIB, TRAFFIC_WRITE_KIB = 6168.5, 48466.9  # sparse_gnn, 8,192 ids
+GATHER_SOURCES_SHA256 = "58b8af378d6fa2a51200dc6deab817e83de123c60703b06eddacee70737fb4f3"
+TRAFFIC_FETCH_KIB, TRAFFIC_WRITE_KIB = 6168.4, 48473.9  # sparse_gnn, 8,192 ids
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 
 

@@ -196,6 +196,54 @@ def test_mask_zero_and_all_ones():
     assert (got == same[:3]).all()
 
 
+# Large batches of one-chunk tensors gathered from an HBM cache take the
+# stream kernel (batches of at least 8 * RPI * 8 * 256 ids: 65,536 for 256 B
+# tensors, 32,768 for 512 B, 16,384 for 1 KB).  Ragged tails, repeated and
+# invalid ids, tensors that do and do not participate, and both degenerate
+# Masks (all zero: every tensor whole; all ones: empty payloads).
+STREAM_CASES = [("dense_gnn", 512, 1024, 3000, 40037), ("dlrm_1k", 1024, 4096, 2000, 20011),
+                ("tiny-256", 256, 256, 2500, 70001), ("dense_gnn", 512, 4096, 1500, 33000)]
+
+
+@pytest.mark.parametrize("key,B,C,n,nb", STREAM_CASES)
+@pytest.mark.parametrize("law", ["workload", "mask0", "mask1"])
+def test_stream_cache_large_batches(key, B, C, n, nb, law):
+    from host_transfer_amd import ibp
+    from oracle import oracle as O
+    rng = np.random.default_rng(B + n + nb)
+    if law == "workload" and key != "tiny-256":
+        w = W.WORKLOADS[key].scaled(n)
+        rows, T = W.rows(w), w.threshold
+    elif law == "workload":
+        rows = (rng.standard_normal((n, B // 4)) * 0.1).astype(np.float32).view(np.uint8)
+        T = 0.99
+    elif law == "mask0":
+        rows, T = rng.integers(0, 256, (n, B), dtype=np.uint8), 1.0
+    else:
+        rows, T = np.tile(rng.integers(0, 256, (1, B), dtype=np.uint8), (n, 1)), 0.99
+    slot = (B + 127) // 128 * 128
+    G.log(f"[parity] stream kernel: {key} {law} B={B} C={C} n={n} ids={nb}")
+    mask, bitval = G.check_metadata(rows, T)
+    if law == "mask0":
+        assert not mask.any()
+    if law == "mask1":
+        assert (mask == 0xFFFFFFFF).all()
+    store, part, lengths = G.gpu_compress(rows, mask, bitval, C, slot)
+    o_store, o_part, o_len = G.check_store(rows, mask, bitval, C, slot, store, part, lengths)
+    offsets = torch.zeros(n + 1, dtype=torch.int64, device="cuda")
+    ibp.compact_offsets(lengths, n, offsets)
+    total = int(G.host(offsets)[-1])
+    cache = torch.full((max(total, 16),), 0x3C, dtype=torch.int8, device="cuda")
+    ibp.compact(store, slot, n, offsets, cache, total)
+    ids = rng.integers(0, n, nb)
+    ids[rng.integers(0, nb, 64)] = rng.choice([-1, n, n + 7, 1 << 40], 64)
+    ids[-1] = n - 1
+    got = G.gpu_gather(cache, total, 0, offsets, part, n, ids, B, C, mask, bitval)
+    want = O.gather_decompress(o_store, o_part, n, ids, B, C, mask, bitval, slot_bytes=slot)
+    assert (got == want).all(), f"{key} {law}: stream gather differs from the oracle"
+    assert (got == G.expected_rows(rows, ids)).all()
+
+
 def test_batch_edges_and_invalid_ids():
     w = W.WORKLOADS["tiny"].scaled(1000)
     rows = W.rows(w)
