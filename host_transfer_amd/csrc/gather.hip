@@ -1385,8 +1385,8 @@ static hipError_t launch_small_routed_seg(const Geometry& g, const GatherArgs& a
 // Stream kernel: large batches of one-chunk tensors (W = 64 J words, J = 1, 2
 // or 4, chunk size >= tensor size) read from an HBM cache.  It keeps the shape
 // of a plain row copy: each lane moves one 16 B unit per step, L = 16 J lanes
-// per tensor and 64 / L tensors per step, the next step's payload in flight
-// while the current one is decoded.  With one chunk a tensor has no chunk scan
+// per tensor and 64 / L tensors per step, the payloads of the next
+// IBP_STREAM_DEPTH steps in flight while the current one is decoded.  With one chunk a tensor has no chunk scan
 // and no header: it is either packed (participation bit set, a payload of
 // exactly K bits, K the kept bits of the Mask) or stored whole, so its payload
 // length follows from that one bit.
@@ -1396,7 +1396,7 @@ static hipError_t launch_small_routed_seg(const Geometry& g, const GatherArgs& a
 // participation bit); the lanes of a step read their tensor's address and
 // unit count across lanes.  The next block's offsets and participation words
 // are loaded while the current block is decoded, its ids one block earlier,
-// and the last step of a block requests the first payload of the next.
+// and the last steps of a block request the first payloads of the next.
 // Lane u of a tensor's L lanes decodes words u + L q, q < 4, from the
 // payload staged in LDS (consecutive lanes read consecutive words, so the
 // window reads do not collide in LDS banks).
