@@ -242,6 +242,16 @@ def test_stream_cache_large_batches(key, B, C, n, nb, law):
     want = O.gather_decompress(o_store, o_part, n, ids, B, C, mask, bitval, slot_bytes=slot)
     assert (got == want).all(), f"{key} {law}: stream gather differs from the oracle"
     assert (got == G.expected_rows(rows, ids)).all()
+    # entries marked IBP_NOT_CACHED give zero rows, in large and short batches
+    gone = rng.choice(n, 16, replace=False)
+    offsets[torch.from_numpy(gone).cuda()] = -1
+    hit = np.isin(ids, gone)
+    want[hit] = 0
+    got = G.gpu_gather(cache, total, 0, offsets, part, n, ids, B, C, mask, bitval)
+    assert (got == want).all(), f"{key} {law}: uncached entries"
+    short = np.concatenate([ids[:500], gone[:4]])
+    got = G.gpu_gather(cache, total, 0, offsets, part, n, short, B, C, mask, bitval)
+    assert (got == np.concatenate([want[:500], np.zeros((4, B), np.uint8)])).all()
 
 
 def test_batch_edges_and_invalid_ids():
