@@ -72,6 +72,42 @@ DevCache g_dev[kMaxDevices];
 
 }  // namespace
 
+// Per-bit-position counters of ibp_build_metadata_noalloc: one uint32 per bit
+// of the largest tensor that call accepts.  Every GPU holds its own copy.  In
+// host code the name stands for a host-side placeholder, never a device
+// address: host code uses only the address hipGetSymbolAddress returns for
+// the current device (scratch_address below).
+static __device__ __align__(256) uint32_t scratch[8u * IBP_NOALLOC_MAX_TENSOR_BYTES];
+
+namespace {
+
+struct ScratchAddr {
+  std::once_flag once;
+  uint32_t* ptr;
+  hipError_t err;
+};
+ScratchAddr g_scratch[kMaxDevices];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+hipError_t scratch_address(uint32_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  ScratchAddr& s = g_scratch[dev];
+  std::call_once(s.once, [&] {
+    void* p = nullptr;
+    s.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    s.ptr = s.err == hipSuccess ? (uint32_t*)p : nullptr;
+    if (s.err == hipSuccess && !s.ptr) s.err = hipErrorInvalidSymbol;
+  });
+  *out = s.ptr;
+  return s.err;
+}
+
+}  // namespace
+
 namespace ibp {
 
 hipError_t device_info(DeviceInfo* out) {
@@ -117,6 +153,51 @@ Geometry make_geometry(uint32_t tensor_bytes, uint32_t chunk_bytes) {
 
 }  // namespace ibp
 
+namespace {
+
+// Argument checks shared by the two metadata entry points (counts aside).
+int check_metadata_args(const char* name, const void* rows, uint64_t row_stride,
+                        const int64_t* sample_ids, uint64_t n_samples, uint32_t tensor_bytes,
+                        double threshold, const uint32_t* mask, const uint32_t* bitval) {
+  if (!rows || !mask || !bitval)
+    return fail(IBP_ERR_NULL, "%s: rows, mask and bitval are required", name);
+  int r = check_tensor(tensor_bytes);
+  if (r) return r;
+  if (n_samples == 0 || n_samples > 0xFFFFFFFFull)
+    return fail(IBP_ERR_SIZE, "%s: n_samples %llu must be in [1, 2^32-1]", name,
+                (unsigned long long)n_samples);
+  if (row_stride < tensor_bytes || row_stride % 4 != 0)
+    return fail(IBP_ERR_SIZE, "%s: row_stride %llu must be >= tensor_bytes and %% 4", name,
+                (unsigned long long)row_stride);
+  if (!(threshold >= 0.5 && threshold <= 1.0))
+    return fail(IBP_ERR_THRESHOLD, "%s: threshold must be in [0.5, 1]", name);
+  if (!aligned(rows, 4) || !aligned(mask, 4) || !aligned(bitval, 4) ||
+      (sample_ids && !aligned(sample_ids, 8)))
+    return fail(IBP_ERR_ALIGN, "%s: misaligned pointer", name);
+  return IBP_OK;
+}
+
+// Checks the arguments, then counts into `counts` (device, 8 * tensor_bytes
+// words, cleared by the launch) and thresholds.
+int build_metadata_into(const char* name, const void* rows, uint64_t row_stride,
+                        const int64_t* sample_ids, uint64_t n_samples, uint32_t tensor_bytes,
+                        double threshold, uint32_t* mask, uint32_t* bitval, uint32_t* counts,
+                        void* stream) {
+  int r = check_metadata_args(name, rows, row_stride, sample_ids, n_samples, tensor_bytes,
+                              threshold, mask, bitval);
+  if (r) return r;
+  // cutoff m = ceil(T * n) in binary64
+  const uint64_t cutoff = (uint64_t)ceil(threshold * (double)n_samples);
+  if ((r = require_device(name))) return r;
+  hipError_t e = ibp::launch_build_metadata((const uint8_t*)rows, row_stride, sample_ids,
+                                            n_samples, tensor_bytes, cutoff, mask, bitval, counts,
+                                            (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, name);
+  return ok();
+}
+
+}  // namespace
+
 extern "C" {
 
 int ibp_version(void) { return IBP_VERSION; }
@@ -134,29 +215,30 @@ int ibp_num_chunks(uint32_t tensor_bytes, uint32_t chunk_bytes) {
 int ibp_build_metadata(const void* rows, uint64_t row_stride, const int64_t* sample_ids,
                        uint64_t n_samples, uint32_t tensor_bytes, double threshold,
                        uint32_t* mask, uint32_t* bitval, uint32_t* counts, void* stream) {
-  if (!rows || !mask || !bitval || !counts)
-    return fail(IBP_ERR_NULL, "ibp_build_metadata: rows, mask, bitval and counts are required");
-  int r = check_tensor(tensor_bytes);
+  const char* name = "ibp_build_metadata";
+  if (!counts) return fail(IBP_ERR_NULL, "%s: counts is required", name);
+  if (!aligned(counts, 4)) return fail(IBP_ERR_ALIGN, "%s: misaligned pointer", name);
+  return build_metadata_into(name, rows, row_stride, sample_ids, n_samples, tensor_bytes,
+                             threshold, mask, bitval, counts, stream);
+}
+
+int ibp_build_metadata_noalloc(const void* rows, uint64_t row_stride, const int64_t* sample_ids,
+                               uint64_t n_samples, uint32_t tensor_bytes, double threshold,
+                               uint32_t* mask, uint32_t* bitval, void* stream) {
+  const char* name = "ibp_build_metadata_noalloc";
+  static_assert(IBP_NOALLOC_MAX_TENSOR_BYTES <= IBP_MAX_TENSOR_BYTES, "scratch size");
+  if (tensor_bytes > IBP_NOALLOC_MAX_TENSOR_BYTES)
+    return fail(IBP_ERR_SIZE, "%s: tensor_bytes %u exceeds the %u the fixed counter array holds",
+                name, tensor_bytes, IBP_NOALLOC_MAX_TENSOR_BYTES);
+  int r = check_metadata_args(name, rows, row_stride, sample_ids, n_samples, tensor_bytes,
+                              threshold, mask, bitval);
   if (r) return r;
-  if (n_samples == 0 || n_samples > 0xFFFFFFFFull)
-    return fail(IBP_ERR_SIZE, "ibp_build_metadata: n_samples %llu must be in [1, 2^32-1]",
-                (unsigned long long)n_samples);
-  if (row_stride < tensor_bytes || row_stride % 4 != 0)
-    return fail(IBP_ERR_SIZE, "ibp_build_metadata: row_stride %llu must be >= tensor_bytes and %% 4",
-                (unsigned long long)row_stride);
-  if (!(threshold >= 0.5 && threshold <= 1.0))
-    return fail(IBP_ERR_THRESHOLD, "ibp_build_metadata: threshold must be in [0.5, 1]");
-  if (!aligned(rows, 4) || !aligned(mask, 4) || !aligned(bitval, 4) || !aligned(counts, 4) ||
-      (sample_ids && !aligned(sample_ids, 8)))
-    return fail(IBP_ERR_ALIGN, "ibp_build_metadata: misaligned pointer");
-  // cutoff m = ceil(T * n) in binary64
-  const uint64_t cutoff = (uint64_t)ceil(threshold * (double)n_samples);
-  if ((r = require_device("ibp_build_metadata"))) return r;
-  hipError_t e = ibp::launch_build_metadata((const uint8_t*)rows, row_stride, sample_ids,
-                                            n_samples, tensor_bytes, cutoff, mask, bitval, counts,
-                                            (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "ibp_build_metadata");
-  return ok();
+  if ((r = require_device(name))) return r;
+  uint32_t* counts = nullptr;
+  hipError_t e = scratch_address(&counts);
+  if (e != hipSuccess) return hip_fail(e, "ibp_build_metadata_noalloc: device address of the counters");
+  return build_metadata_into(name, rows, row_stride, sample_ids, n_samples, tensor_bytes,
+                             threshold, mask, bitval, counts, stream);
 }
 
 int ibp_compress(const void* rows, uint64_t row_stride, uint64_t n_rows, uint64_t first_tensor,

@@ -43,6 +43,7 @@ _SIGS = {
     "ibp_version": [],
     "ibp_num_chunks": [_u32, _u32],
     "ibp_build_metadata": [_vp, _u64, _vp, _u64, _u32, ctypes.c_double, _vp, _vp, _vp, _vp],
+    "ibp_build_metadata_noalloc": [_vp, _u64, _vp, _u64, _u32, ctypes.c_double, _vp, _vp, _vp],
     "ibp_compress": [_vp, _u64, _u64, _u64, _u64, _u32, _u32, _vp, _vp, _vp, _u64, _vp, _vp, _vp],
     "ibp_compress_segments": [_vp, _u64, _vp, _vp, _vp, _u32, _u64, _u32, _u32, _vp, _vp, _vp, _u64,
                               _vp, _vp, _vp],
@@ -120,6 +121,16 @@ def build_metadata(rows, row_stride, sample_ids, n_samples, tensor_bytes, thresh
     _check(_lib.ibp_build_metadata(_ptr(rows), row_stride, _ptr(sample_ids), n_samples,
                                    tensor_bytes, threshold, _ptr(mask), _ptr(bitval), _ptr(counts),
                                    _stream(stream)))
+
+
+NOALLOC_MAX_TENSOR_BYTES = 16384
+
+
+def build_metadata_noalloc(rows, row_stride, sample_ids, n_samples, tensor_bytes, threshold, mask,
+                           bitval, stream=None):
+    _check(_lib.ibp_build_metadata_noalloc(_ptr(rows), row_stride, _ptr(sample_ids), n_samples,
+                                           tensor_bytes, threshold, _ptr(mask), _ptr(bitval),
+                                           _stream(stream)))
 
 
 def compress(rows, row_stride, n_rows, first_tensor, n_tensors, tensor_bytes, chunk_bytes, mask,

@@ -122,6 +122,26 @@ int ibp_build_metadata(const void *rows, uint64_t row_stride,
                        void *stream);
 
 /*
+ * ibp_build_metadata_noalloc -- ibp_build_metadata without the counts
+ * workspace, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, meaning, Mask and Bitval as ibp_build_metadata.  The per-bit
+ * counters live in a fixed array of 8 * IBP_NOALLOC_MAX_TENSOR_BYTES uint32
+ * (512 KiB) inside the library, one per GPU, held until the process ends;
+ * the call allocates nothing (no hipMalloc, no hipFree) and clears the
+ * counters it uses with a kernel before counting.  Every call on one GPU
+ * uses that GPU's array: calls that overlap on one GPU (on different streams,
+ * or from different threads) race and give wrong Mask/Bitval.
+ * Errors: as ibp_build_metadata; tensor_bytes > IBP_NOALLOC_MAX_TENSOR_BYTES
+ * (IBP_ERR_SIZE); IBP_ERR_HIP if the array's device address cannot be found.
+ */
+#define IBP_NOALLOC_MAX_TENSOR_BYTES 16384u
+int ibp_build_metadata_noalloc(const void *rows, uint64_t row_stride,
+                               const int64_t *sample_ids, uint64_t n_samples,
+                               uint32_t tensor_bytes, double threshold,
+                               uint32_t *mask, uint32_t *bitval, void *stream);
+
+/*
  * ibp_compress -- [G-EN] Core Algorithm, Compression; System Integration,
  * PCIe transfer compression (in-place fixed-size buffers, GPU bitmask); the
  * GPU writes the store directly, also when it is host-mapped.

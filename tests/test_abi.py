@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(ibp):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     out = subprocess.run(["nm", "-D", "--defined-only", ibp.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (ibp_\w+)$", out, flags=re.M))
@@ -67,6 +67,22 @@ def test_build_metadata_validation(ibp):
         _expect(ibp, ibp.ERR_THRESHOLD, f, P, 512, None, 10, 512, T, P, P, P)
     _expect(ibp, ibp.ERR_ALIGN, f, P + 2, 512, None, 10, 512, 0.99, P, P, P)
     _expect(ibp, ibp.ERR_ALIGN, f, P, 512, P + 4, 10, 512, 0.99, P, P, P)
+
+
+def test_build_metadata_noalloc_validation(ibp):
+    f = ibp.build_metadata_noalloc
+    _expect(ibp, ibp.ERR_NULL, f, 0, 512, None, 10, 512, 0.99, P, P)
+    _expect(ibp, ibp.ERR_NULL, f, P, 512, None, 10, 512, 0.99, P, None)
+    _expect(ibp, ibp.ERR_SIZE, f, P, 512, None, 10, 510, 0.99, P, P)
+    _expect(ibp, ibp.ERR_SIZE, f, P, 1 << 20, None, 10, ibp.NOALLOC_MAX_TENSOR_BYTES + 4, 0.99,
+            P, P)
+    assert "16384" in ibp.last_error()
+    _expect(ibp, ibp.ERR_SIZE, f, P, 512, None, 0, 512, 0.99, P, P)
+    _expect(ibp, ibp.ERR_SIZE, f, P, 256, None, 10, 512, 0.99, P, P)
+    for T in (0.4999, 1.0001, float("nan")):
+        _expect(ibp, ibp.ERR_THRESHOLD, f, P, 512, None, 10, 512, T, P, P)
+    _expect(ibp, ibp.ERR_ALIGN, f, P + 2, 512, None, 10, 512, 0.99, P, P)
+    _expect(ibp, ibp.ERR_ALIGN, f, P, 512, P + 4, 10, 512, 0.99, P, P)
 
 
 def test_compress_validation(ibp):
