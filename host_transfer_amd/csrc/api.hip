@@ -56,6 +56,9 @@ int check_chunk(uint32_t chunk_bytes) {
   return IBP_OK;
 }
 
+// Entry alignment of a compacted cache: a power of two in [16, 4096].
+bool valid_align(uint32_t a) { return a >= 16 && a <= 4096 && (a & (a - 1)) == 0; }
+
 // Bitmap words for n tensors of n_c chunks, or 0 on overflow.
 uint64_t bitmap_bits(uint64_t n_tensors, uint32_t n_c) {
   if (n_tensors > (UINT64_MAX - 31) / n_c) return 0;
@@ -321,8 +324,74 @@ int ibp_compact_offsets(const uint32_t* lengths, uint64_t n_tensors, uint64_t* o
     return fail(IBP_ERR_ALIGN, "ibp_compact_offsets: misaligned pointer");
   int r;
   if ((r = require_device("ibp_compact_offsets"))) return r;
-  hipError_t e = ibp::launch_compact_offsets(lengths, n_tensors, offsets, (hipStream_t)stream);
+  hipError_t e = ibp::launch_compact_offsets(lengths, n_tensors, 16u, offsets, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "ibp_compact_offsets");
+  return ok();
+}
+
+int ibp_compact_offsets_aligned(const uint32_t* lengths, uint64_t n_tensors, uint32_t entry_align,
+                                uint64_t* offsets, void* stream) {
+  const char* name = "ibp_compact_offsets_aligned";
+  if (!lengths || !offsets) return fail(IBP_ERR_NULL, "%s: lengths and offsets are required", name);
+  if (!valid_align(entry_align))
+    return fail(IBP_ERR_ALIGN, "%s: entry_align %u must be a power of two in [16, 4096]", name,
+                entry_align);
+  if (!aligned(lengths, 4) || !aligned(offsets, 8))
+    return fail(IBP_ERR_ALIGN, "%s: misaligned pointer", name);
+  int r;
+  if ((r = require_device(name))) return r;
+  hipError_t e = ibp::launch_compact_offsets(lengths, n_tensors, entry_align, offsets,
+                                             (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, name);
+  return ok();
+}
+
+int ibp_cache_index(const uint32_t* part_bits, uint64_t n_tensors, uint64_t* index, void* stream) {
+  const char* name = "ibp_cache_index";
+  if (!part_bits || !index) return fail(IBP_ERR_NULL, "%s: part_bits and index are required", name);
+  if (n_tensors >= (1ull << 32))
+    return fail(IBP_ERR_SIZE, "%s: n_tensors must be below 2^32", name);
+  if (!aligned(part_bits, 4) || !aligned(index, 8))
+    return fail(IBP_ERR_ALIGN, "%s: misaligned pointer", name);
+  int r;
+  if ((r = require_device(name))) return r;
+  hipError_t e = ibp::launch_cache_index(part_bits, n_tensors, index, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, name);
+  return ok();
+}
+
+int ibp_gather_decompress_indexed(const void* cache, uint64_t cache_bytes, uint32_t entry_align,
+                                  const uint64_t* index, uint64_t n_tensors, const int64_t* ids,
+                                  uint64_t n_ids, uint32_t tensor_bytes, uint32_t chunk_bytes,
+                                  const uint32_t* mask, const uint32_t* bitval, void* out,
+                                  void* stream) {
+  const char* name = "ibp_gather_decompress_indexed";
+  if (!cache || !index || !ids || !mask || !bitval || !out)
+    return fail(IBP_ERR_NULL, "%s: cache, index, ids, mask, bitval and out are required", name);
+  int r = check_tensor(tensor_bytes);
+  if (r) return r;
+  if ((r = check_chunk(chunk_bytes))) return r;
+  if (chunk_bytes < tensor_bytes)
+    return fail(IBP_ERR_CHUNK, "%s: tensors must be one chunk (chunk_bytes >= tensor_bytes)", name);
+  if (tensor_bytes != 256 && tensor_bytes != 512 && tensor_bytes != 1024)
+    return fail(IBP_ERR_SIZE, "%s: tensor_bytes %u: 256, 512 or 1024 bytes", name, tensor_bytes);
+  if (!valid_align(entry_align))
+    return fail(IBP_ERR_ALIGN, "%s: entry_align %u must be a power of two in [16, 4096]", name,
+                entry_align);
+  if (n_tensors >= (1ull << 32))
+    return fail(IBP_ERR_SIZE, "%s: n_tensors must be below 2^32", name);
+  if (n_ids > UINT64_MAX / tensor_bytes) return fail(IBP_ERR_SIZE, "%s: n_ids too large", name);
+  if ((uint64_t)(uintptr_t)cache >= (1ull << 48) || cache_bytes > (1ull << 48) - (uintptr_t)cache)
+    return fail(IBP_ERR_SIZE, "%s: the cache must lie below 2^48 (a device address)", name);
+  if (!aligned(cache, 16) || !aligned(out, 16) || !aligned(ids, 8) || !aligned(index, 8) ||
+      !aligned(mask, 4) || !aligned(bitval, 4))
+    return fail(IBP_ERR_ALIGN, "%s: misaligned pointer", name);
+  if ((r = require_device(name))) return r;
+  const ibp::Geometry g = ibp::make_geometry(tensor_bytes, chunk_bytes);
+  hipError_t e = ibp::launch_gather_cache_index(g, (const uint8_t*)cache, cache_bytes, entry_align,
+                                                index, n_tensors, ids, n_ids, mask, bitval,
+                                                (uint32_t*)out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, name);
   return ok();
 }
 

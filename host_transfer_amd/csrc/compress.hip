@@ -316,19 +316,21 @@ hipError_t launch_compress(const Geometry& g, const uint8_t* rows, uint64_t row_
 
 // ---------------------------------------------------------------- compaction
 
-// offsets[t] = sum of roundup(lengths[u], 16) over the selected u < t;
+// offsets[t] = sum of roundup(lengths[u], align) over the selected u < t;
 // offsets[n] = total.  select: null (every tensor) or a flag per tensor; with
 // `mark`, an unselected tensor's entry is kNotCachedEntry.  One workgroup
 // walks the array in tiles of 4 x 1024 entries (off the critical path: a few
-// milliseconds for millions of tensors).
+// milliseconds for millions of tensors).  align: a power of two, 16..4096.
 constexpr uint64_t kNotCachedEntry = ~0ull;
 
 __global__ __launch_bounds__(1024) void k_compact_offsets(const uint32_t* __restrict__ lengths,
                                                            const uint32_t* __restrict__ select,
-                                                           uint64_t n, uint64_t* __restrict__ offsets,
+                                                           uint64_t n, uint32_t align,
+                                                           uint64_t* __restrict__ offsets,
                                                            bool mark) {
   __shared__ uint32_t s_wsum[16];
   const uint32_t tid = threadIdx.x;
+  const uint32_t am = align - 1u;
   uint64_t carry = 0;
   for (uint64_t base = 0; base < n; base += 4096) {
     uint32_t v[4];
@@ -338,7 +340,7 @@ __global__ __launch_bounds__(1024) void k_compact_offsets(const uint32_t* __rest
     for (int i = 0; i < 4; ++i) {
       const uint64_t t = base + 4u * tid + i;
       sel[i] = t < n && (select == nullptr || select[t] != 0u);
-      v[i] = sel[i] ? ((lengths[t] + 15u) & ~15u) : 0u;
+      v[i] = sel[i] ? ((lengths[t] + am) & ~am) : 0u;
       local += v[i];
     }
     uint32_t tot;
@@ -353,6 +355,41 @@ __global__ __launch_bounds__(1024) void k_compact_offsets(const uint32_t* __rest
     carry += tot;
   }
   if (tid == 0) offsets[n] = carry;
+}
+
+// index[w] = (participating chunks in bitmap words 0..w-1) << 32 |
+// part_bits[w], for w < ceil(n_bits / 32); bits at or past n_bits are
+// cleared.  One workgroup, tiles of 4 x 1024 words.  The count is exact
+// while n_bits < 2^32.
+__global__ __launch_bounds__(1024) void k_cache_index(const uint32_t* __restrict__ part_bits,
+                                                       uint64_t n_bits,
+                                                       uint64_t* __restrict__ index) {
+  __shared__ uint32_t s_wsum[16];
+  const uint32_t tid = threadIdx.x;
+  const uint64_t n_words = (n_bits + 31u) / 32u;
+  uint32_t carry = 0;
+  for (uint64_t base = 0; base < n_words; base += 4096) {
+    uint32_t wv[4];
+    uint32_t local = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint64_t w = base + 4u * tid + i;
+      uint32_t x = w < n_words ? part_bits[w] : 0u;
+      if (w + 1u == n_words && (n_bits & 31u)) x &= (1u << (n_bits & 31u)) - 1u;
+      wv[i] = x;
+      local += (uint32_t)__popc(x);
+    }
+    uint32_t tot;
+    const uint32_t incl = block_inclusive_sum(local, s_wsum, &tot);
+    uint32_t r = carry + (incl - local);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint64_t w = base + 4u * tid + i;
+      if (w < n_words) index[w] = ((uint64_t)r << 32) | wv[i];
+      r += (uint32_t)__popc(wv[i]);
+    }
+    carry += tot;
+  }
 }
 
 // One wave per cached tensor: copies its payload (rounded up to 16 B) from
@@ -398,17 +435,24 @@ __global__ __launch_bounds__(256) void k_compact_copy(const uint8_t* __restrict_
   }
 }
 
-hipError_t launch_compact_offsets(const uint32_t* lengths, uint64_t n, uint64_t* offsets,
-                                  hipStream_t s) {
+hipError_t launch_compact_offsets(const uint32_t* lengths, uint64_t n, uint32_t align,
+                                  uint64_t* offsets, hipStream_t s) {
   hipLaunchKernelGGL(k_compact_offsets, dim3(1), dim3(1024), 0, s, lengths,
-                     (const uint32_t*)nullptr, n, offsets, false);
+                     (const uint32_t*)nullptr, n, align, offsets, false);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_index(const uint32_t* part_bits, uint64_t n_bits, uint64_t* index,
+                              hipStream_t s) {
+  if (n_bits == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_cache_index, dim3(1), dim3(1024), 0, s, part_bits, n_bits, index);
   return hipGetLastError();
 }
 
 hipError_t launch_cache_offsets(const uint32_t* lengths, const uint32_t* select, uint64_t n,
                                 uint64_t* offsets, hipStream_t s) {
-  hipLaunchKernelGGL(k_compact_offsets, dim3(1), dim3(1024), 0, s, lengths, select, n, offsets,
-                     true);
+  hipLaunchKernelGGL(k_compact_offsets, dim3(1), dim3(1024), 0, s, lengths, select, n, 16u,
+                     offsets, true);
   return hipGetLastError();
 }
 

@@ -31,9 +31,8 @@
 // time (see its comment), with the same pipeline across tiles.
 // k_gather_direct: short batches of such tensors held in an HBM cache, read
 // in place without staging (see its comment).
-// k_gather_stream: large batches of one-chunk tensors (W = 64, 128 or 256
-// words) held in an HBM cache, moved 16 B per lane like a plain row copy
-// (see its comment).
+// One-chunk tensors of 64, 128 or 256 words held in an HBM cache take
+// k_gather_cache (gather_cache.hip) instead.
 //
 // Both have a routed variant (k_gather_decompress_routed, k_gather_tile_routed)
 // that sends every row to the XCD its tensor hashes to, for batches that
@@ -644,12 +643,6 @@ __device__ __forceinline__ void unpack_stages_n(uint32_t (&x)[N], const uint32_t
 #endif
 #ifndef IBP_DIRECT_TG
 #define IBP_DIRECT_TG 8   // tensors per tile of k_gather_direct (half when J >= 3)
-#endif
-#ifndef IBP_STREAM
-#define IBP_STREAM 1  // stream kernel for large one-chunk cache launches
-#endif
-#ifndef IBP_STREAM_DEPTH
-#define IBP_STREAM_DEPTH 8  // steps of payload in flight per wave in the stream kernel
 #endif
 #ifndef IBP_BIG_NL
 #define IBP_BIG_NL 8      // load instructions per tile on large batches
@@ -1381,233 +1374,6 @@ static hipError_t launch_small_routed_seg(const Geometry& g, const GatherArgs& a
               : launch_tile_routed_seg<J, 2 * RPI, RPI, false>(g, a, t, max_rows, s);
 }
 
-// ---------------------------------------------------------------------------
-// Stream kernel: large batches of one-chunk tensors (W = 64 J words, J = 1, 2
-// or 4, chunk size >= tensor size) read from an HBM cache.  It keeps the shape
-// of a plain row copy: each lane moves one 16 B unit per step, L = 16 J lanes
-// per tensor and 64 / L tensors per step, the payloads of the next
-// IBP_STREAM_DEPTH steps in flight while the current one is decoded.  With one chunk a tensor has no chunk scan
-// and no header: it is either packed (participation bit set, a payload of
-// exactly K bits, K the kept bits of the Mask) or stored whole, so its payload
-// length follows from that one bit.
-//
-// A wave takes blocks of 64 consecutive rows (grid stride).  Lane r of the
-// wave holds the metadata of row r of its block (offset-table entry and
-// participation bit); the lanes of a step read their tensor's address and
-// unit count across lanes.  The next block's offsets and participation words
-// are loaded while the current block is decoded, its ids one block earlier,
-// and the last steps of a block request the first payloads of the next.
-// Lane u of a tensor's L lanes decodes words u + L q, q < 4, from the
-// payload staged in LDS (consecutive lanes read consecutive words, so the
-// window reads do not collide in LDS banks).
-
-// Offset-table entry and participation word of one row, as loaded.
-struct StreamRaw {
-  uint64_t o;
-  uint32_t pw;
-  uint32_t bit;
-  bool valid;
-};
-
-__device__ __forceinline__ StreamRaw stream_raw(const GatherArgs& a, int64_t id) {
-  StreamRaw r;
-  r.valid = id >= 0 && (uint64_t)id < a.n_tensors;
-  const uint64_t t = r.valid ? (uint64_t)id : 0ull;
-  r.o = load_global(a.offsets + t);
-  r.pw = a.part_bits[t >> 5];  // one chunk: bit t
-  r.bit = (uint32_t)(t & 31u);
-  return r;
-}
-
-// Payload address and 16 B units of one row, and its participation.  Same
-// rules as source_of and make_tile_hdr for a cache-only launch: an entry of
-// kNotCached has no source (zero row); reads never pass the end of the cache.
-struct StreamMeta {
-  uint32_t lo, hi;  // payload address
-  uint32_t n16;     // 16 B units to read
-};
-
-__device__ __forceinline__ StreamMeta stream_resolve(const GatherArgs& a, const StreamRaw& r,
-                                                     uint32_t n16_packed, uint32_t n16_raw,
-                                                     bool* packed) {
-  const bool src = r.valid && r.o != kNotCached;
-  const bool p = src && ((r.pw >> r.bit) & 1u);
-  const uint64_t avail = r.o < a.cache_bytes ? (a.cache_bytes - r.o) >> 4 : 0ull;
-  const uint32_t want = src ? (p ? n16_packed : n16_raw) : 0u;
-  StreamMeta m;
-  const uint64_t addr = (uint64_t)a.cache + (src ? r.o : 0ull);
-  m.lo = (uint32_t)addr;
-  m.hi = (uint32_t)(addr >> 32);
-  m.n16 = (uint32_t)min((uint64_t)want, avail);
-  *packed = p;
-  return m;
-}
-
-// Lane (u, g) of a step loads unit u of the tensor in row i = step * TPS + g
-// of the block whose metadata m holds (row r's in lane r).
-__device__ __forceinline__ uint4 stream_load(const StreamMeta& m, uint32_t i, uint32_t u) {
-  const uint32_t lo = (uint32_t)__shfl((int)m.lo, (int)i, kWave);
-  const uint32_t hi = (uint32_t)__shfl((int)m.hi, (int)i, kWave);
-  const uint32_t n = (uint32_t)__shfl((int)m.n16, (int)i, kWave);
-  const uint64_t addr = ((uint64_t)hi << 32) | lo;
-  return load_global((const uint4*)(u < n ? addr + 16ull * u : (uint64_t)&g_zero16));
-}
-
-template <int J>
-__global__ __launch_bounds__(256) void k_gather_stream(GatherArgs a) {
-  constexpr uint32_t L = 16u * J;             // lanes (16 B units) per tensor
-  constexpr uint32_t TPS = (uint32_t)kWave / L;  // tensors per step
-  constexpr uint32_t SPB = (uint32_t)kWave / TPS;  // steps per block of 64 rows
-  constexpr uint32_t kSlot = 16u * L + 16u;   // LDS bytes per tensor, + the word a window reads past it
-  constexpr uint32_t kW = 4u * L;             // words per tensor
-  extern __shared__ __align__(16) uint8_t smem[];
-  const GatherLds Lds(kW, 0u);
-  uint32_t* s_pref = (uint32_t*)(smem + Lds.pref);
-  uint32_t* s_kc = (uint32_t*)(smem + Lds.kc);
-  uint32_t* s_wsum = (uint32_t*)(smem + Lds.wsum);
-  const uint32_t wave = uniform(threadIdx.x / kWave);
-  const uint32_t lane = threadIdx.x % kWave;
-  const uint32_t g = lane / L, u = lane % L;
-  uint32_t* slot = (uint32_t*)(smem + Lds.group0 + (wave * TPS + g) * kSlot);
-
-  const uint64_t n_blocks = (a.n_ids + 63u) / 64u;
-  const uint64_t waves = (uint64_t)gridDim.x * (blockDim.x / kWave);
-  const uint64_t b0 = (uint64_t)blockIdx.x * (blockDim.x / kWave) + wave;
-
-  // ids of the first two blocks, this lane's Mask/Bitval words, the offsets
-  // and participation words of the first block, then the kept-bit prefix
-  // (a workgroup scan: every thread takes part)
-  const int64_t id0 = load_id(a, b0 * 64u + lane);
-  int64_t id_n = load_id(a, (b0 + waves) * 64u + lane);
-  PlanRun run;
-  load_plan_run(a.mask, a.sh, run);
-  uint32_t mk[4], bv[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    mk[q] = a.mask[u + L * q];
-    bv[q] = a.bitval[u + L * q];
-  }
-  const StreamRaw r0 = stream_raw(a, id0);
-  load_plan_counts(run, a.sh, s_pref, s_kc, s_wsum);
-  if (b0 >= n_blocks) return;  // per wave; no workgroup barrier follows
-
-  // packed payload: K bits -> ceil(K / 8) bytes -> ceil(K / 128) units
-  const uint32_t n16_packed = (s_pref[kW] + 127u) >> 7;
-  bool p;
-  StreamMeta m_c = stream_resolve(a, r0, n16_packed, L, &p);
-  uint64_t pm_c = __ballot(p);
-  // payloads of the next D steps in flight (v[k % D] holds step k's)
-  constexpr uint32_t D = IBP_STREAM_DEPTH < SPB / 2 ? IBP_STREAM_DEPTH : SPB / 2;
-  static_assert(SPB % D == 0 && D <= SPB / 2, "pipeline depth");
-  uint4 v[D];
-#pragma unroll
-  for (uint32_t d = 0; d < D; ++d) v[d] = stream_load(m_c, d * TPS + g, u);
-
-  // per-word plan (while that payload is in flight)
-  uint32_t mv[4][5], pre[4];
-  uint32_t stages = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    move_masks(~mk[q], mv[q]);
-    bv[q] &= mk[q];
-    pre[q] = s_pref[u + L * q];
-#pragma unroll
-    for (int st = 0; st < 5; ++st) stages |= (__ballot(mv[q][st] != 0u) != 0ull ? 1u : 0u) << st;
-  }
-  stages = uniform(stages);
-
-  StreamMeta m_n = m_c;
-  uint64_t pm_n = 0;
-  for (uint64_t b = b0; b < n_blocks; b += waves) {
-    // next block's offsets and participation words; ids two blocks ahead
-    const StreamRaw r_n = stream_raw(a, id_n);
-    id_n = load_id(a, (b + 2u * waves) * 64u + lane);
-    for (uint32_t k0 = 0; k0 < SPB; k0 += D) {
-#pragma unroll
-    for (uint32_t d = 0; d < D; ++d) {
-      const uint32_t k = k0 + d;
-      // a. this step's payload -> LDS
-      ((uint4*)slot)[u] = v[d];
-      wave_sync();
-      // b. the next block's metadata, loaded half a block ago
-      if (k == SPB / 2) {
-        m_n = stream_resolve(a, r_n, n16_packed, L, &p);
-        pm_n = __ballot(p);
-      }
-      // c. the payload D steps ahead (in the next block near the end)
-      const bool wrap = k + D >= SPB;
-      StreamMeta m_s;
-      m_s.lo = wrap ? m_n.lo : m_c.lo;
-      m_s.hi = wrap ? m_n.hi : m_c.hi;
-      m_s.n16 = wrap ? m_n.n16 : m_c.n16;
-      v[d] = stream_load(m_s, (wrap ? k + D - SPB : k + D) * TPS + g, u);
-      // d. decode row k * TPS + g: packed -> window at the kept-bit prefix,
-      //    unpack, Bitval; whole -> the word itself
-      const uint32_t i = k * TPS + g;
-      const bool packed = ((uint32_t)(pm_c >> (k * TPS)) >> g) & 1u;
-      uint32_t x[4], y[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        x[q] = window32(slot, packed ? pre[q] : 32u * (u + L * q));
-        y[q] = x[q];
-      }
-      if (stages & 16u) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) y[q] = bfi_op(mv[q][4], y[q] << 16, y[q]);
-      }
-      if (stages & 8u) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) y[q] = bfi_op(mv[q][3], y[q] << 8, y[q]);
-      }
-      if (stages & 4u) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) y[q] = bfi_op(mv[q][2], y[q] << 4, y[q]);
-      }
-      if (stages & 2u) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) y[q] = bfi_op(mv[q][1], y[q] << 2, y[q]);
-      }
-      if (stages & 1u) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) y[q] = bfi_op(mv[q][0], y[q] << 1, y[q]);
-      }
-      // e. store the row
-      const uint64_t row = b * 64u + i;
-      if (row < a.n_ids) {
-        uint32_t* orow = a.out + row * kW + u;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) store_out(orow + L * q, packed ? bfi_op(mk[q], bv[q], y[q]) : x[q]);
-      }
-      wave_sync();
-    }
-    }
-    m_c = m_n;
-    pm_c = pm_n;
-  }
-}
-
-template <int J>
-static hipError_t launch_stream(const Geometry& g, GatherArgs a, hipStream_t s) {
-  constexpr uint32_t L = 16u * J, TPS = (uint32_t)kWave / L;
-  a.sh.group = kWave;
-  const uint32_t waves = 4;
-  const GatherLds Lds(g.W, 0u);
-  const uint32_t lds = Lds.group0 + waves * TPS * (16u * L + 16u);
-  DeviceInfo di;
-  hipError_t e = device_info(&di);
-  if (e != hipSuccess) return e;
-  int per_cu = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gather_stream<J>, waves * 64, lds);
-  if (e != hipSuccess) return e;
-  if (per_cu < 1) return hipErrorInvalidConfiguration;
-  const uint64_t n_blocks = (a.n_ids + 63u) / 64u;
-  const uint64_t want = (n_blocks + waves - 1) / waves;
-  const uint64_t cap = (uint64_t)per_cu * (uint64_t)di.cus;
-  const uint32_t blocks = (uint32_t)(want < cap ? want : cap);
-  hipLaunchKernelGGL(k_gather_stream<J>, dim3(blocks), dim3(waves * 64), lds, s, a);
-  return hipGetLastError();
-}
-
 // Small tensors (W <= 256): rows per load instruction RPI from the payload's
 // 16 B units (J fixes them: J = 1 -> <= 16 units, 2 -> <= 32, 3 and 4 ->
 // <= 64), and NL load instructions per tile: 8 when the batch gives every CU
@@ -1620,15 +1386,13 @@ static hipError_t launch_small(const Geometry& g, const GatherArgs& a, hipStream
   if (e != hipSuccess) return e;
   const bool full = g.W == (uint32_t)kWave * J;
   const bool big = a.n_ids >= (uint64_t)8 * RPI * 8 * (uint64_t)di.cus;
-  // short launches with every payload in HBM (no host slots): read in place
+  // one-chunk tensors of 64, 128 or 256 words, every payload in HBM
+  if (cache_kernel_fits(g) && a.offsets != nullptr && a.store == nullptr && !a.route)
+    return launch_gather_cache_table(g, a.cache, a.cache_bytes, a.offsets, a.part_bits,
+                                     a.n_tensors, a.ids, a.n_ids, a.mask, a.bitval, a.out, s);
+  // other short launches with every payload in HBM (no host slots): read in place
   if (full && !big && a.offsets != nullptr && a.store == nullptr && !a.route)
     return launch_direct<J, (J >= 3 ? IBP_DIRECT_TG / 2 : IBP_DIRECT_TG)>(g, a, s);
-  // large batches of one-chunk tensors, every payload in HBM
-  if constexpr (J != 3) {
-    if (IBP_STREAM && full && big && g.n_c == 1 && a.offsets != nullptr && a.store == nullptr &&
-        !a.route)
-      return launch_stream<J>(g, a, s);
-  }
   if (a.route)
     return full ? launch_tile_routed<J, 2 * RPI, RPI, true>(g, a, s)
                 : launch_tile_routed<J, 2 * RPI, RPI, false>(g, a, s);

@@ -1,0 +1,487 @@
+// gather_cache.hip -- gather + decompress of one-chunk tensors held in a
+// compacted HBM cache ([G-EN] System Integration, cache compression; Core
+// Algorithm, Decompression).  A one-chunk tensor (chunk size >= tensor size)
+// is either packed -- exactly K payload bits, K the kept (non-Mask) bits of
+// the Mask -- or stored whole, so its payload length follows from its
+// participation bit alone and it needs no chunk scan.
+//
+// Two ways to find an entry:
+//   table  offsets[t] (one u64 per tensor, kNotCached = zero row) and the
+//          participation bitmap, as ibp_gather_decompress takes them;
+//   index  one u64 per 32 tensors: the participation word (low half) and the
+//          number of participating tensors before it (high half).  With
+//          entries of size s_p (packed) and s_r (whole), each rounded up to
+//          the entry alignment A, entry t starts at
+//              t * s_r - r1(t) * (s_r - s_p),
+//          r1(t) the participating tensors before t.  The index is 1/32 of
+//          the bitmap's tensors in u64 words (2 MB for 2^23 tensors), so it
+//          stays in L2, where a per-tensor table costs a line per distinct
+//          tensor; with A = 128 every entry starts on a 128 B line and
+//          occupies the fewest lines its length allows.
+//
+// Launch shape: a wave takes blocks of br consecutive rows (grid stride; br =
+// 32, fewer on short batches so that they still spread over every CU).
+// Lane r of the wave resolves row r's entry (address, 16 B units to read,
+// packed or not) once per block.  A step moves TPS = 64 / L tensors, each
+// with L = 16 J lanes loading one 16 B unit each (a plain row copy's shape);
+// the payloads of the next D steps are in flight in registers while the
+// current one is decoded from LDS.  Lane u of a tensor decodes words
+// u + L q, q < 4, so consecutive lanes read consecutive LDS words and store
+// consecutive output words.
+//
+// Decode of one word w of a packed tensor: a 64-bit window of the payload at
+// the word's kept-bit offset pre_w (two LDS words, v_alignbit), then the kept
+// bits are spread to their positions and Bitval inserted under the Mask.
+// When the kept bits of every word form at most two runs (the common case for
+// float data: a run of invariant exponent bits splits the word), spreading is
+// two shifts and one bit-field insert; otherwise the five-stage expand of
+// ibp_device.h.  A whole (non-participating) tensor's word is its payload
+// word.  Every select is a per-lane select, with no divergent branch.
+#include "ibp_internal.h"
+#include "ibp_plan.h"
+
+#ifndef IBP_CACHE_BR_MAX
+#define IBP_CACHE_BR_MAX 32  // rows per block at most
+#endif
+#ifndef IBP_CACHE_DEPTH
+#define IBP_CACHE_DEPTH 4  // steps of payload in flight per wave
+#endif
+
+namespace ibp {
+
+namespace {
+
+// 1 KB of zeros: rows with no source (invalid id, no entry, an entry past the
+// end of the cache) read 16 B per lane from here.
+__device__ __align__(16) uint4 g_cache_zero[64];
+
+constexpr uint64_t kNoEntry = ~0ull;
+
+struct CacheArgs {
+  const uint8_t* cache;
+  uint64_t cache_bytes;
+  const uint64_t* offsets;   // table mode
+  const uint32_t* part_bits; // table mode
+  const uint64_t* index;     // index mode
+  uint64_t n_tensors;
+  const int64_t* ids;
+  uint64_t n_ids;
+  const uint32_t* mask;
+  const uint32_t* bitval;
+  uint32_t* out;
+  Shape sh;
+  uint32_t align;            // index mode: entry alignment (power of two)
+};
+
+__device__ __forceinline__ uint64_t ld_u64(const uint64_t* p) { return load_global(p); }
+
+__device__ __forceinline__ uint32_t ld_u32(const uint32_t* p) {
+  typedef __attribute__((address_space(1))) const uint32_t global_u32;
+  return *(global_u32*)(uintptr_t)p;
+}
+
+__device__ __forceinline__ int64_t row_id(const CacheArgs& a, uint64_t row) {
+  const int64_t id = (int64_t)ld_u64((const uint64_t*)a.ids + (row < a.n_ids ? row : a.n_ids - 1));
+  return row < a.n_ids ? id : -1;
+}
+
+// What lane r loads for row r of a block: the tensor's entry in the table
+// (offset + participation word) or in the index.  Unconditional loads (an
+// invalid id reads tensor 0's), resolved one step later.
+struct RowRaw {
+  uint64_t e;   // table: offset entry; index: index word
+  uint32_t pw;  // table: participation word
+  uint32_t t;   // tensor index mod 2^32 (bit position, rank)
+  bool valid;
+};
+
+template <bool INDEXED>
+__device__ __forceinline__ RowRaw row_raw(const CacheArgs& a, int64_t id) {
+  RowRaw r;
+  r.valid = id >= 0 && (uint64_t)id < a.n_tensors;
+  const uint64_t t = r.valid ? (uint64_t)id : 0ull;
+  r.t = (uint32_t)t;
+  if (INDEXED) {
+    r.e = ld_u64(a.index + (t >> 5));
+    r.pw = 0;
+  } else {
+    r.e = ld_u64(a.offsets + t);
+    r.pw = ld_u32(a.part_bits + (t >> 5));
+  }
+  return r;
+}
+
+// Row r's payload source, packed into two words for the lanes that read it:
+//   lo = address bits 0..31, hi = address bits 32..47 | (units - 1) << 16 |
+//   packed << 24.  A row with no source reads the zero block as a whole row.
+struct RowMeta {
+  uint32_t lo, hi;
+};
+
+template <bool INDEXED>
+__device__ __forceinline__ RowMeta row_resolve(const CacheArgs& a, const RowRaw& r, uint32_t n16p,
+                                               uint32_t n16r, uint64_t s_p, uint64_t s_r) {
+  uint64_t off;
+  bool p;
+  if (INDEXED) {
+    const uint32_t word = (uint32_t)r.e, rank = (uint32_t)(r.e >> 32);
+    const uint32_t bit = r.t & 31u;
+    p = (word >> bit) & 1u;
+    const uint64_t r1 = (uint64_t)rank + (uint64_t)__popc(word & ((1u << bit) - 1u));
+    off = (uint64_t)r.t * s_r - r1 * (s_r - s_p);
+  } else {
+    off = r.e;
+    p = (r.pw >> (r.t & 31u)) & 1u;
+  }
+  const uint32_t want = p ? n16p : n16r;
+  // the entry's units must lie inside the cache, else a zero row; a packed
+  // entry of no units (every bit invariant) reads nothing and decodes to Bitval
+  const bool empty = want == 0u;
+  const bool inside = off < a.cache_bytes && (a.cache_bytes - off) >> 4 >= want;
+  const bool src = r.valid && off != kNoEntry && (empty || inside);
+  const bool rd = src && !empty;
+  const uint64_t addr = rd ? (uint64_t)a.cache + off : (uint64_t)&g_cache_zero[0];
+  const uint32_t units = rd ? want : 64u;
+  RowMeta m;
+  m.lo = (uint32_t)addr;
+  m.hi = (uint32_t)(addr >> 32) | ((units - 1u) << 16) | ((uint32_t)(src && p) << 24);
+  return m;
+}
+
+// Per-lane decode constants of one output word.
+struct WordDec {
+  uint32_t mk, bv;  // Mask, Bitval & Mask
+  uint32_t ap, sp;  // LDS byte address and bit shift of the packed window
+  uint32_t c[5];    // two-run: c[0] = first-run shift, c[1] = second-run shift, c[2] = first run;
+                    // else the five move masks
+};
+
+// Kept bits of a word in at most two runs: first run (lowest kept bits) from
+// packed bit 0 to position s1; second run from packed bit n1 to position s2.
+__device__ __forceinline__ bool two_runs(uint32_t keep, uint32_t c[5]) {
+  const uint32_t low = keep & (0u - keep);
+  const uint32_t run1 = keep & ~(keep + low);
+  const uint32_t rest = keep & ~run1;
+  const uint32_t low2 = rest & (0u - rest);
+  const bool ok = (rest & (rest + low2)) == 0u;  // rest is one run (or empty)
+  const uint32_t s1 = keep ? (uint32_t)__builtin_ctz(keep) : 0u;
+  const uint32_t n1 = (uint32_t)__popc(run1);
+  const uint32_t s2 = rest ? (uint32_t)__builtin_ctz(rest) : n1;
+  c[0] = s1;
+  c[1] = s2 - n1;
+  c[2] = run1;
+  c[3] = 0;
+  c[4] = 0;
+  return ok;
+}
+
+template <bool RUNS>
+__device__ __forceinline__ uint32_t spread(uint32_t p, const WordDec& d) {
+  if (RUNS) return bfi_op(d.c[2], p << d.c[0], p << d.c[1]);
+  uint32_t y = p;
+  y = bfi_op(d.c[4], y << 16, y);
+  y = bfi_op(d.c[3], y << 8, y);
+  y = bfi_op(d.c[2], y << 4, y);
+  y = bfi_op(d.c[1], y << 2, y);
+  y = bfi_op(d.c[0], y << 1, y);
+  return y;
+}
+
+constexpr uint32_t kCacheWaves = 4;
+
+template <int J>
+struct CacheGeo {
+  static constexpr uint32_t L = 16u * J;                 // lanes (16 B units) per tensor
+  static constexpr uint32_t TPS = (uint32_t)kWave / L;   // tensors per step
+  static constexpr uint32_t kW = 4u * L;                 // words per tensor
+  static constexpr uint32_t kSlot = 16u * L + 16u;       // LDS bytes per tensor + the word a window reads past
+  static constexpr uint32_t D = IBP_CACHE_DEPTH;
+  // blocks hold a power-of-two number of steps >= 2 D (cache_rows_per_block),
+  // so D steps divide every block
+  static_assert(D >= 1 && (D & (D - 1)) == 0, "pipeline depth: a power of two");
+  static_assert(2u * D * TPS <= (uint32_t)kWave, "a block of at most 64 rows holds 2 D steps");
+  static_assert(IBP_CACHE_BR_MAX <= 64 && (IBP_CACHE_BR_MAX & (IBP_CACHE_BR_MAX - 1)) == 0,
+                "rows per block: a power of two, at most one per lane");
+  // LDS: kept-bit prefix (W + 1 words, padded), chunk sums, scan scratch, slots
+  static constexpr uint32_t pref = 0;
+  static constexpr uint32_t kc = ((4u * (kW + 1u)) + 15u) & ~15u;
+  static constexpr uint32_t wsum = kc + 256u;
+  static constexpr uint32_t slots = wsum + 64u;
+  static constexpr uint32_t bytes = slots + kCacheWaves * TPS * kSlot;
+};
+
+// The kernel's LDS (static, so LDS addresses fold into instruction offsets).
+template <int J>
+struct CacheLds {
+  uint8_t b[CacheGeo<J>::bytes];
+};
+
+// Decodes row `orow` of a packed tensor in its LDS slot (this lane's words
+// u + L q, from the windows at their kept-bit offsets) and writes the words
+// back over the slot, then stores the row 16 B per lane from the slot.  A whole
+// tensor's slot already holds its words in order.  Consecutive lanes read and
+// write consecutive LDS words (no bank conflicts), and each lane stores 16
+// contiguous bytes, so a row leaves in whole-line 16 B stores like a plain copy.
+template <int J, bool RUNS>
+__device__ __forceinline__ void decode_store(uint8_t* lds, uint32_t slot, uint32_t u,
+                                             const WordDec (&dw)[4], bool packed,
+                                             uint32_t* orow) {
+  constexpr uint32_t L = CacheGeo<J>::L;
+  if (packed) {
+    uint32_t z[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const WordDec& d = dw[q];
+      const uint32_t d0 = *(const uint32_t*)(lds + d.ap);
+      const uint32_t d1 = *(const uint32_t*)(lds + d.ap + 4u);
+      const uint32_t p = __builtin_amdgcn_alignbit(d1, d0, d.sp);
+      z[q] = bfi_op(d.mk, d.bv, spread<RUNS>(p, d));
+    }
+    // every window of the slot has been read (LDS accesses of a wave run in
+    // order) before the words overwrite it
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *(uint32_t*)(lds + slot + 4u * (u + L * q)) = z[q];
+  }
+  wave_sync();
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 row = *(const u32x4*)(lds + slot + 16u * u);
+  __builtin_nontemporal_store(row, (u32x4*)orow);
+}
+
+// One block of `br` rows (rows row0 .. row0 + br - 1, the last block possibly
+// short): SPB = br / TPS steps, payloads D steps ahead, the next block's
+// entries resolved half-way.
+template <int J, bool INDEXED, bool RUNS, bool FULL>
+__device__ __forceinline__ void cache_block(const CacheArgs& a, uint8_t* lds,
+                                            uint32_t slot, uint32_t g,
+                                            uint32_t u, uint32_t spb, uint64_t row0,
+                                            const WordDec (&dw)[4], uint4 (&v)[CacheGeo<J>::D],
+                                            uint32_t (&pk)[CacheGeo<J>::D], const RowMeta& m_c,
+                                            RowMeta& m_n, const RowRaw& r_n, uint32_t n16p,
+                                            uint64_t s_p, uint64_t s_r) {
+  using G = CacheGeo<J>;
+  constexpr uint32_t L = G::L, TPS = G::TPS, kW = G::kW, D = G::D;
+  uint32_t* orow = a.out + (row0 + g) * kW + 4u * u;
+  const uint32_t left = (uint32_t)min((uint64_t)spb * TPS, a.n_ids - row0);
+  for (uint32_t k0 = 0; k0 < spb; k0 += D) {
+#pragma unroll
+    for (uint32_t d = 0; d < D; ++d) {
+      const uint32_t k = k0 + d;
+      // a. this step's payload -> LDS
+      *(uint4*)(lds + slot + 16u * u) = v[d];
+      const bool packed = pk[d] != 0u;
+      wave_sync();
+      // b. the next block's entries, loaded half a block ago
+      if (k == spb / 2) m_n = row_resolve<INDEXED>(a, r_n, n16p, L, s_p, s_r);
+      // c. the payload D steps ahead (in the next block near the end)
+      {
+        const bool wrap = k + D >= spb;
+        const uint32_t i = (wrap ? k + D - spb : k + D) * TPS + g;
+        const uint32_t lo = (uint32_t)__shfl((int)(wrap ? m_n.lo : m_c.lo), (int)i, kWave);
+        const uint32_t hi = (uint32_t)__shfl((int)(wrap ? m_n.hi : m_c.hi), (int)i, kWave);
+        const uint32_t un = min(u, (hi >> 16) & 63u);
+        v[d] = load_global((const uint4*)((((uint64_t)(hi & 0xFFFFu) << 32) | lo) + 16ull * un));
+        pk[d] = hi >> 24;
+      }
+      // d. decode and store row k * TPS + g
+      if (FULL || k * TPS + g < left) decode_store<J, RUNS>(lds, slot, u, dw, packed, orow);
+      orow += TPS * kW;
+      wave_sync();
+    }
+  }
+}
+
+template <int J, bool INDEXED>
+__global__ __launch_bounds__(256) void k_gather_cache(CacheArgs a, uint32_t br) {
+  using G = CacheGeo<J>;
+  constexpr uint32_t L = G::L, TPS = G::TPS, kW = G::kW, D = G::D;
+  __shared__ __align__(16) CacheLds<J> s_lds;
+  uint8_t* lds = s_lds.b;
+  uint32_t* s_pref = (uint32_t*)(s_lds.b + G::pref);
+  uint32_t* s_kc = (uint32_t*)(s_lds.b + G::kc);
+  uint32_t* s_wsum = (uint32_t*)(s_lds.b + G::wsum);
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  const uint32_t lane = threadIdx.x % kWave;
+  const uint32_t g = lane / L, u = lane % L;
+  const uint32_t slot = G::slots + (wave * TPS + g) * G::kSlot;
+  const uint32_t spb = br / TPS;  // steps per block
+
+  const uint64_t n_blocks = (a.n_ids + br - 1u) / br;
+  const uint64_t waves = (uint64_t)gridDim.x * kCacheWaves;
+  const uint64_t b0 = (uint64_t)blockIdx.x * kCacheWaves + wave;
+
+  // ids of the first two blocks, this lane's Mask/Bitval words, the first
+  // block's entries, then the kept-bit prefix (a workgroup scan)
+  const uint32_t r = lane < br ? lane : br - 1u;
+  const int64_t id0 = row_id(a, b0 * br + r);
+  int64_t id_n = row_id(a, (b0 + waves) * br + r);
+  PlanRun run;
+  load_plan_run(a.mask, a.sh, run);
+  WordDec dw[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    dw[q].mk = ld_u32(a.mask + u + L * q);
+    dw[q].bv = ld_u32(a.bitval + u + L * q);
+  }
+  const RowRaw r0 = row_raw<INDEXED>(a, id0);
+  load_plan_counts(run, a.sh, s_pref, s_kc, s_wsum);
+  if (b0 >= n_blocks) return;  // per wave; no workgroup barrier follows
+
+  // packed payload: K bits -> ceil(K / 128) units; entry sizes (index mode)
+  const uint32_t K = s_pref[kW];
+  const uint32_t n16p = (K + 127u) >> 7;
+  const uint64_t amask = (uint64_t)a.align - 1u;
+  const uint64_t s_p = (((uint64_t)K + 7u) / 8u + amask) & ~amask;
+  const uint64_t s_r = ((uint64_t)(4u * kW) + amask) & ~amask;
+  RowMeta m_c = row_resolve<INDEXED>(a, r0, n16p, L, s_p, s_r);
+
+  // payloads of the first D steps (a block of br rows has br / TPS >= D steps)
+  uint4 v[D];
+  uint32_t pk[D];
+#pragma unroll
+  for (uint32_t d = 0; d < D; ++d) {
+    const uint32_t i = d * TPS + g;
+    const uint32_t lo = (uint32_t)__shfl((int)m_c.lo, (int)i, kWave);
+    const uint32_t hi = (uint32_t)__shfl((int)m_c.hi, (int)i, kWave);
+    const uint32_t un = min(u, (hi >> 16) & 63u);
+    v[d] = load_global((const uint4*)((((uint64_t)(hi & 0xFFFFu) << 32) | lo) + 16ull * un));
+    pk[d] = hi >> 24;
+  }
+
+  // per-word constants (while those payloads are in flight)
+  bool runs_ok = true;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    WordDec& d = dw[q];
+    const uint32_t pre = s_pref[u + L * q];
+    d.bv &= d.mk;
+    d.ap = slot + 4u * (pre >> 5);
+    d.sp = pre & 31u;
+    runs_ok = two_runs(~d.mk, d.c) && runs_ok;
+  }
+  const bool runs = __ballot(!runs_ok) == 0ull;
+  if (!runs) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) move_masks(~dw[q].mk, dw[q].c);
+  }
+
+  RowMeta m_n = m_c;
+  for (uint64_t b = b0; b < n_blocks; b += waves) {
+    // next block's entries; ids two blocks ahead
+    const RowRaw r_n = row_raw<INDEXED>(a, id_n);
+    id_n = row_id(a, (b + 2u * waves) * br + r);
+    const uint64_t row0 = b * br;
+    const bool full = row0 + br <= a.n_ids;
+    if (runs) {
+      if (full)
+        cache_block<J, INDEXED, true, true>(a, lds, slot, g, u, spb, row0, dw, v, pk,
+                                            m_c, m_n, r_n, n16p, s_p, s_r);
+      else
+        cache_block<J, INDEXED, true, false>(a, lds, slot, g, u, spb, row0, dw, v, pk,
+                                             m_c, m_n, r_n, n16p, s_p, s_r);
+    } else {
+      if (full)
+        cache_block<J, INDEXED, false, true>(a, lds, slot, g, u, spb, row0, dw, v, pk,
+                                             m_c, m_n, r_n, n16p, s_p, s_r);
+      else
+        cache_block<J, INDEXED, false, false>(a, lds, slot, g, u, spb, row0, dw, v, pk,
+                                              m_c, m_n, r_n, n16p, s_p, s_r);
+    }
+    m_c = m_n;
+  }
+}
+
+// Rows per block: 64 while the batch still gives every SIMD a few waves of
+// such blocks, fewer on short batches (down to 2 D steps' worth), so that
+// short launches spread over the whole GPU.
+template <int J>
+uint32_t cache_rows_per_block(uint64_t n_ids, int cus) {
+  using G = CacheGeo<J>;
+  uint32_t br = IBP_CACHE_BR_MAX;
+  const uint32_t min_br = 2u * G::D * G::TPS;
+  while (br > min_br && n_ids / br < (uint64_t)cus * 16u) br /= 2;
+  return br < min_br ? min_br : br;
+}
+
+template <int J, bool INDEXED>
+hipError_t launch_cache_j(const CacheArgs& a, hipStream_t s) {
+  DeviceInfo di;
+  hipError_t e = device_info(&di);
+  if (e != hipSuccess) return e;
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gather_cache<J, INDEXED>,
+                                                   kCacheWaves * kWave, 0);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) return hipErrorInvalidConfiguration;
+  const uint32_t br = cache_rows_per_block<J>(a.n_ids, di.cus);
+  const uint64_t n_blocks = (a.n_ids + br - 1) / br;
+  const uint64_t cap = (uint64_t)per_cu * (uint64_t)di.cus;
+  // as many workgroups as fit, but each wave gets the same number of blocks
+  const uint64_t per_wave = (n_blocks + cap * kCacheWaves - 1) / (cap * kCacheWaves);
+  const uint64_t want = (n_blocks + per_wave * kCacheWaves - 1) / (per_wave * kCacheWaves);
+  hipLaunchKernelGGL((k_gather_cache<J, INDEXED>), dim3((uint32_t)want), dim3(kCacheWaves * kWave),
+                     0, s, a, br);
+  return hipGetLastError();
+}
+
+template <bool INDEXED>
+hipError_t launch_cache(const Geometry& g, const CacheArgs& a, hipStream_t s) {
+  switch (g.W) {
+    case 64: return launch_cache_j<1, INDEXED>(a, s);
+    case 128: return launch_cache_j<2, INDEXED>(a, s);
+    case 256: return launch_cache_j<4, INDEXED>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+CacheArgs cache_args(const Geometry& g, const uint8_t* cache, uint64_t cache_bytes,
+                     const int64_t* ids, uint64_t n_ids, uint64_t n_tensors,
+                     const uint32_t* mask, const uint32_t* bitval, uint32_t* out) {
+  CacheArgs a;
+  a.cache = cache;
+  a.cache_bytes = cache_bytes;
+  a.offsets = nullptr;
+  a.part_bits = nullptr;
+  a.index = nullptr;
+  a.n_tensors = n_tensors;
+  a.ids = ids;
+  a.n_ids = n_ids;
+  a.mask = mask;
+  a.bitval = bitval;
+  a.out = out;
+  a.sh = Shape{g.W, g.n_c, g.wpc_log2, g.last_bits, kCacheWaves * kWave};
+  a.align = 16;
+  return a;
+}
+
+}  // namespace
+
+bool cache_kernel_fits(const Geometry& g) {
+  return g.n_c == 1 && (g.W == 64 || g.W == 128 || g.W == 256);
+}
+
+hipError_t launch_gather_cache_table(const Geometry& g, const uint8_t* cache, uint64_t cache_bytes,
+                                     const uint64_t* offsets, const uint32_t* part_bits,
+                                     uint64_t n_tensors, const int64_t* ids, uint64_t n_ids,
+                                     const uint32_t* mask, const uint32_t* bitval, uint32_t* out,
+                                     hipStream_t s) {
+  if (n_ids == 0) return hipSuccess;
+  CacheArgs a = cache_args(g, cache, cache_bytes, ids, n_ids, n_tensors, mask, bitval, out);
+  a.offsets = offsets;
+  a.part_bits = part_bits;
+  return launch_cache<false>(g, a, s);
+}
+
+hipError_t launch_gather_cache_index(const Geometry& g, const uint8_t* cache, uint64_t cache_bytes,
+                                     uint32_t entry_align, const uint64_t* index,
+                                     uint64_t n_tensors, const int64_t* ids, uint64_t n_ids,
+                                     const uint32_t* mask, const uint32_t* bitval, uint32_t* out,
+                                     hipStream_t s) {
+  if (n_ids == 0) return hipSuccess;
+  CacheArgs a = cache_args(g, cache, cache_bytes, ids, n_ids, n_tensors, mask, bitval, out);
+  a.index = index;
+  a.align = entry_align;
+  return launch_cache<true>(g, a, s);
+}
+
+}  // namespace ibp

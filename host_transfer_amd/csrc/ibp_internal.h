@@ -38,8 +38,28 @@ hipError_t launch_compress(const Geometry& g, const uint8_t* rows, uint64_t row_
                            const uint32_t* bitval, uint8_t* store, uint64_t slot_bytes,
                            uint32_t* part_bits, uint32_t* lengths, hipStream_t s);
 
-hipError_t launch_compact_offsets(const uint32_t* lengths, uint64_t n, uint64_t* offsets,
-                                  hipStream_t s);
+hipError_t launch_compact_offsets(const uint32_t* lengths, uint64_t n, uint32_t align,
+                                  uint64_t* offsets, hipStream_t s);
+
+hipError_t launch_cache_index(const uint32_t* part_bits, uint64_t n_bits, uint64_t* index,
+                              hipStream_t s);
+
+// One-chunk tensors of 64, 128 or 256 words from a compacted HBM cache
+// (gather_cache.hip): entries found through the offset table + bitmap, or
+// through the rank index (entry alignment `entry_align`).
+bool cache_kernel_fits(const Geometry& g);
+
+hipError_t launch_gather_cache_table(const Geometry& g, const uint8_t* cache, uint64_t cache_bytes,
+                                     const uint64_t* offsets, const uint32_t* part_bits,
+                                     uint64_t n_tensors, const int64_t* ids, uint64_t n_ids,
+                                     const uint32_t* mask, const uint32_t* bitval, uint32_t* out,
+                                     hipStream_t s);
+
+hipError_t launch_gather_cache_index(const Geometry& g, const uint8_t* cache, uint64_t cache_bytes,
+                                     uint32_t entry_align, const uint64_t* index,
+                                     uint64_t n_tensors, const int64_t* ids, uint64_t n_ids,
+                                     const uint32_t* mask, const uint32_t* bitval, uint32_t* out,
+                                     hipStream_t s);
 
 hipError_t launch_compact(const uint8_t* store, uint64_t slot_bytes, uint64_t n,
                           const uint64_t* offsets, uint8_t* cache, uint64_t cache_bytes,

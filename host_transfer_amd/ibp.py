@@ -49,6 +49,10 @@ _SIGS = {
                               _vp, _vp, _vp],
     "ibp_compact_offsets": [_vp, _u64, _vp, _vp],
     "ibp_compact": [_vp, _u64, _u64, _vp, _vp, _u64, _vp],
+    "ibp_compact_offsets_aligned": [_vp, _u64, _u32, _vp, _vp],
+    "ibp_cache_index": [_vp, _u64, _vp, _vp],
+    "ibp_gather_decompress_indexed": [_vp, _u64, _u32, _vp, _u64, _vp, _u64, _u32, _u32, _vp, _vp,
+                                      _vp, _vp],
     "ibp_gather_decompress": [_vp, _u64, _u64, _vp, _vp, _u64, _vp, _u64, _u32, _u32, _vp, _vp,
                               _vp, _vp],
     "ibp_gather_decompress_ex": [_vp, _u64, _u64, _vp, _vp, _u64, _vp, _u64, _u32, _u32, _vp,
@@ -157,6 +161,23 @@ def compress_segments(rows, row_stride, seg_row, seg_first, seg_count, n_tensors
 
 def compact_offsets(lengths, n_tensors, offsets, stream=None):
     _check(_lib.ibp_compact_offsets(_ptr(lengths), n_tensors, _ptr(offsets), _stream(stream)))
+
+
+def compact_offsets_aligned(lengths, n_tensors, entry_align, offsets, stream=None):
+    _check(_lib.ibp_compact_offsets_aligned(_ptr(lengths), n_tensors, entry_align, _ptr(offsets),
+                                            _stream(stream)))
+
+
+def cache_index(part_bits, n_tensors, index, stream=None):
+    _check(_lib.ibp_cache_index(_ptr(part_bits), n_tensors, _ptr(index), _stream(stream)))
+
+
+def gather_decompress_indexed(cache, cache_bytes, entry_align, index, n_tensors, ids, n_ids,
+                              tensor_bytes, chunk_bytes, mask, bitval, out, stream=None):
+    _check(_lib.ibp_gather_decompress_indexed(_ptr(cache), cache_bytes, entry_align, _ptr(index),
+                                              n_tensors, _ptr(ids), n_ids, tensor_bytes,
+                                              chunk_bytes, _ptr(mask), _ptr(bitval), _ptr(out),
+                                              _stream(stream)))
 
 
 def compact(store, slot_bytes, n_tensors, offsets, cache, cache_bytes, stream=None):

@@ -205,6 +205,36 @@ int ibp_compact_offsets(const uint32_t *lengths, uint64_t n_tensors,
                         uint64_t *offsets, void *stream);
 
 /*
+ * ibp_compact_offsets_aligned -- as ibp_compact_offsets with each entry
+ * rounded up to entry_align bytes: offsets[t+1] = offsets[t] +
+ * roundup(lengths[t], entry_align).  With entry_align = 128 every entry starts
+ * on a 128 B line, so a payload of len bytes occupies ceil(len / 128) lines,
+ * the fewest its length allows (the GPU reads HBM in whole 128 B lines; with
+ * 16 B alignment a payload crosses one line more on average).  Fill the cache
+ * with ibp_cache_fill (it copies each payload, rounded up to 16 B; the bytes
+ * after it, up to the next entry, are left as they were).
+ *   entry_align  a power of two in [16, 4096] (IBP_ERR_ALIGN otherwise).
+ *   lengths  device uint32[n_tensors];  offsets  device uint64[n_tensors + 1].
+ */
+int ibp_compact_offsets_aligned(const uint32_t *lengths, uint64_t n_tensors,
+                                uint32_t entry_align, uint64_t *offsets, void *stream);
+
+/*
+ * ibp_cache_index -- rank index of a participation bitmap, for one-chunk
+ * tensors (chunk_bytes >= tensor_bytes, so bit t of part_bits is tensor t):
+ *     index[w] = (number of set bits of part_bits[0 .. w-1]) << 32
+ *                | part_bits[w]          for w < ceil(n_tensors / 32),
+ * with bits t >= n_tensors of the last word cleared.  A tensor's entry in a
+ * cache compacted with ibp_compact_offsets_aligned follows from it (see
+ * ibp_gather_decompress_indexed), so a gather reads one 8-byte index word
+ * per 32 tensors instead of one 8-byte offset per tensor.
+ *   part_bits  device uint32[ceil(n_tensors / 32)];  index  device
+ *   uint64[ceil(n_tensors / 32)].  n_tensors < 2^32 (IBP_ERR_SIZE).
+ */
+int ibp_cache_index(const uint32_t *part_bits, uint64_t n_tensors, uint64_t *index,
+                    void *stream);
+
+/*
  * ibp_compact -- copies entry t (offsets[t+1] - offsets[t] bytes from the
  * start of slot t) to cache + offsets[t] for every t < n_tensors.  Entries
  * that would end past cache_bytes are not copied.
@@ -295,6 +325,34 @@ int ibp_gather_decompress_segments(const void *store, uint64_t store_bytes,
                                    uint32_t chunk_bytes, const uint32_t *masks,
                                    const uint32_t *bitvals, void *out, unsigned flags,
                                    void *stream);
+
+/*
+ * ibp_gather_decompress_indexed -- ibp_gather_decompress from a compacted
+ * cache of one-chunk tensors, with entries found through the rank index
+ * instead of an offset table ([G-EN] System Integration, cache compression;
+ * Core Algorithm, Decompression).  The cache must hold every tensor, compacted
+ * with ibp_compact_offsets_aligned(entry_align) from the lengths ibp_compress
+ * wrote with this Mask: a one-chunk tensor's payload is ceil(K / 8) bytes
+ * when it participates (K = bits not set in the Mask) and tensor_bytes
+ * otherwise, so with s_p = roundup(ceil(K / 8), entry_align) and
+ * s_r = roundup(tensor_bytes, entry_align) entry t starts at
+ *     t * s_r - r1(t) * (s_r - s_p),   r1(t) = participating tensors before t.
+ * Same rows as ibp_gather_decompress with the matching offset table.
+ *   cache        device, cache_bytes bytes, 16 B aligned, below address 2^48.
+ *                Reads never go past cache_bytes (an entry that would, and an
+ *                id outside [0, n_tensors), yield a row of zero bytes).
+ *   entry_align  the alignment the cache was compacted with.
+ *   index        device, from ibp_cache_index; n_tensors < 2^32.
+ *   tensor_bytes 256, 512 or 1024 (IBP_ERR_SIZE otherwise); chunk_bytes >=
+ *                tensor_bytes (IBP_ERR_CHUNK otherwise).
+ *   ids, mask, bitval, out  as ibp_gather_decompress.
+ */
+int ibp_gather_decompress_indexed(const void *cache, uint64_t cache_bytes,
+                                  uint32_t entry_align, const uint64_t *index,
+                                  uint64_t n_tensors, const int64_t *ids, uint64_t n_ids,
+                                  uint32_t tensor_bytes, uint32_t chunk_bytes,
+                                  const uint32_t *mask, const uint32_t *bitval, void *out,
+                                  void *stream);
 
 /* ------------------------------------------------------ cache + store together
  * [G-EN] System Integration uses both placements at once: a compressed

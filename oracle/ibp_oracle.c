@@ -224,6 +224,64 @@ ORC_API int orc_compact(const uint8_t *store, uint64_t slot_bytes,
 }
 
 /*
+ * The same compacted layout with every entry rounded up to a multiple of
+ * `align` bytes instead of 16: offsets[t+1] = offsets[t] + lengths[t] rounded
+ * up to a multiple of align (align >= 1).  With align = 128 each entry starts
+ * at a multiple of 128 bytes.  If `cache` is given, entry t receives the
+ * lengths[t] payload bytes of slot t followed by zero bytes up to the next
+ * entry.
+ */
+ORC_API int orc_compact_aligned(const uint8_t *store, uint64_t slot_bytes,
+                                const uint32_t *lengths, uint64_t n_tensors,
+                                uint32_t align, uint64_t *offsets, uint8_t *cache)
+{
+    if (!lengths || !offsets || align == 0)
+        return -1;
+    offsets[0] = 0;
+    for (uint64_t t = 0; t < n_tensors; t++) {
+        uint64_t size = 0;
+        while (size < lengths[t])
+            size += align;
+        offsets[t + 1] = offsets[t] + size;
+    }
+    if (cache) {
+        if (!store)
+            return -1;
+        for (uint64_t t = 0; t < n_tensors; t++) {
+            uint64_t e = offsets[t + 1] - offsets[t];
+            memset(cache + offsets[t], 0, e);
+            memcpy(cache + offsets[t], store + t * slot_bytes, lengths[t]);
+        }
+    }
+    return 0;
+}
+
+/*
+ * Rank index of a participation bitmap of n_bits bits: for each 32-bit word
+ * w, index[w] = (number of set bits among bitmap bits 0 .. 32w-1) * 2^32 +
+ * (word w with every bit at or past n_bits cleared).  Counted one bit at a
+ * time.
+ */
+ORC_API int orc_cache_index(const uint32_t *part_bits, uint64_t n_bits, uint64_t *index)
+{
+    if (!part_bits || !index)
+        return -1;
+    uint64_t before = 0;
+    for (uint64_t w = 0; w * 32 < n_bits; w++) {
+        uint64_t word = 0;
+        for (unsigned b = 0; b < 32; b++) {
+            const uint64_t j = w * 32 + b;
+            if (j < n_bits && get_map_bit(part_bits, j))
+                word |= (uint64_t)1 << b;
+        }
+        index[w] = (before << 32) | word;
+        for (unsigned b = 0; b < 32; b++)
+            before += (word >> b) & 1;
+    }
+    return 0;
+}
+
+/*
  * Gather + decompress ([G-EN] Core Algorithm, Decompression).  Output row r
  * is tensor t = ids[r]: walking the chunks in order with one cursor into the
  * payload of t, a participating chunk takes Bitval at its Mask positions and

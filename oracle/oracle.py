@@ -51,6 +51,11 @@ class Oracle:
                                    _c.c_uint32, _u8p, _u8p, _u8p, _c.c_uint64, _u32p, _u32p]
         L.orc_compact.restype = _c.c_int
         L.orc_compact.argtypes = [_u8p, _c.c_uint64, _u32p, _c.c_uint64, _u64p, _u8p]
+        L.orc_compact_aligned.restype = _c.c_int
+        L.orc_compact_aligned.argtypes = [_u8p, _c.c_uint64, _u32p, _c.c_uint64, _c.c_uint32,
+                                          _u64p, _u8p]
+        L.orc_cache_index.restype = _c.c_int
+        L.orc_cache_index.argtypes = [_u32p, _c.c_uint64, _u64p]
         L.orc_gather_decompress.restype = _c.c_int
         L.orc_gather_decompress.argtypes = [_u8p, _c.c_uint64, _u64p, _u32p, _c.c_uint64, _i64p,
                                             _c.c_uint64, _c.c_uint32, _c.c_uint32, _u8p, _u8p,
@@ -126,6 +131,33 @@ class Oracle:
             raise ValueError("orc_compact rejected its arguments")
         return offsets, cache
 
+    def compact_aligned(self, store, slot_bytes, lengths, align, with_cache=True):
+        """As compact(), each entry rounded up to a multiple of `align` bytes."""
+        lengths = np.ascontiguousarray(lengths, dtype=np.uint32)
+        n = lengths.shape[0]
+        offsets = np.zeros(n + 1, np.uint64)
+        rc = self.lib.orc_compact_aligned(None, slot_bytes, _p(lengths, _u32p), n, align,
+                                          _p(offsets, _u64p), None)
+        if rc != 0:
+            raise ValueError("orc_compact_aligned rejected its arguments")
+        if not with_cache:
+            return offsets, None
+        cache = np.zeros(int(offsets[-1]), np.uint8)
+        rc = self.lib.orc_compact_aligned(_p(store, _u8p), slot_bytes, _p(lengths, _u32p), n,
+                                          align, _p(offsets, _u64p), _p(cache, _u8p))
+        if rc != 0:
+            raise ValueError("orc_compact_aligned rejected its arguments")
+        return offsets, cache
+
+    def cache_index(self, part_bits, n_bits):
+        """Rank index (ceil(n_bits / 32),) uint64 of a participation bitmap."""
+        pb = np.ascontiguousarray(part_bits, dtype=np.uint32)
+        index = np.zeros((n_bits + 31) // 32, np.uint64)
+        rc = self.lib.orc_cache_index(_p(pb, _u32p), n_bits, _p(index, _u64p))
+        if rc != 0:
+            raise ValueError("orc_cache_index rejected its arguments")
+        return index
+
     def gather_decompress(self, store, part_bits, n_tensors, ids, tensor_bytes, chunk_bytes,
                           mask, bitval, slot_bytes=None, offsets=None, out=None):
         """Returns the (n_ids, tensor_bytes) uint8 array of decompressed rows."""
@@ -179,6 +211,14 @@ def compress(*a, **k):
 
 def compact(*a, **k):
     return default().compact(*a, **k)
+
+
+def compact_aligned(*a, **k):
+    return default().compact_aligned(*a, **k)
+
+
+def cache_index(*a, **k):
+    return default().cache_index(*a, **k)
 
 
 def gather_decompress(*a, **k):

@@ -291,6 +291,54 @@ def pin_compact(orc, rng):
     assert (y1 == rows.view(np.uint8)[ids]).all()
 
 
+def pin_compact_aligned(orc, rng):
+    """Aligned compaction ([G-EN] System Integration, cache compression, laid
+    out on 128 B lines) and the rank index: every entry starts at a multiple of
+    the alignment and is the smallest such multiple that holds its payload;
+    with 16 it is the 16 B layout above; the cache round-trips; and for
+    one-chunk tensors the entry offset follows from the index alone,
+    t * s_r - r1(t) * (s_r - s_p), with s_p / s_r the aligned sizes of a
+    packed payload (ceil(K / 8) bytes, K = bits not in the Mask) and of a
+    whole tensor."""
+    B, C, n = 512, 1024, 77
+    rows = _random_case(rng, n, B // 4, "float")
+    mask, bitval = orc.build_metadata(rows, 0.9)
+    slot = 512
+    store, pb, lens = orc.compress(rows, mask, bitval, C, slot_bytes=slot)
+    o16, _ = orc.compact(store, slot, lens, with_cache=False)
+    K = int(np.unpackbits(np.ascontiguousarray(~mask).view(np.uint8)).sum())
+    P = _bits_le(pb)[:n].astype(bool)
+    assert 0 < P.sum() < n, "the case should mix packed and whole tensors"
+    # one-chunk tensors: a packed payload is ceil(K / 8) bytes, a whole one B
+    assert (lens[P] == (K + 7) // 8).all() and (lens[~P] == B).all()
+    for A in (16, 48, 64, 128, 256):
+        offs, cache = orc.compact_aligned(store, slot, lens, A)
+        size = np.diff(offs).astype(np.int64)
+        assert (offs[:-1] % A == 0).all()
+        assert (size >= lens).all() and (size - A < lens).all()
+        if A == 16:
+            assert (offs == o16).all()
+        for t in range(n):
+            o, L = int(offs[t]), int(lens[t])
+            assert cache[o:o + L].tobytes() == store[t * slot:t * slot + L].tobytes()
+            assert not cache[o + L:int(offs[t + 1])].any()
+        ids = rng.integers(0, n, 40)
+        y = orc.gather_decompress(cache, pb, n, ids, B, C, mask, bitval, offsets=offs)
+        assert (y == rows.view(np.uint8)[ids]).all()
+        # offsets from the rank index
+        pb_dirty = pb.copy()
+        pb_dirty[-1] |= np.uint32(0xFFFFFFFF << (n % 32) & 0xFFFFFFFF)  # bits past n are ignored
+        index = orc.cache_index(pb_dirty, n)
+        assert index.shape == ((n + 31) // 32,)
+        assert ((index & np.uint64(0xFFFFFFFF)).astype(np.uint32) == pb).all()
+        s_p = -(-((K + 7) // 8) // A) * A
+        s_r = -(-B // A) * A
+        for t in range(n):
+            word, rank = int(index[t // 32]) & 0xFFFFFFFF, int(index[t // 32]) >> 32
+            r1 = rank + bin(word & ((1 << (t % 32)) - 1)).count("1")
+            assert int(offs[t]) == t * s_r - r1 * (s_r - s_p), (A, t)
+
+
 def pin_invalid_ids(orc, rng):
     B, C, n = 64, 256, 5
     rows = _random_case(rng, n, B // 4, "float")
@@ -334,6 +382,7 @@ def run_all(orc, bmi2, seed=1234):
     pin_mask_zero_is_plain_gather(orc, rng)
     pin_full_participation_independent_of_chunk(orc, bmi2, rng)
     pin_compact(orc, rng)
+    pin_compact_aligned(orc, rng)
     pin_invalid_ids(orc, rng)
     pin_brute_force(orc, rng)
     pin_roundtrip_and_format(orc, bmi2, rng)

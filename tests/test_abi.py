@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(ibp):
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 22, names
     out = subprocess.run(["nm", "-D", "--defined-only", ibp.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (ibp_\w+)$", out, flags=re.M))
@@ -182,3 +182,91 @@ def test_other_validation(ibp):
         ibp.host_alloc(0)
     assert e.value.code == ibp.ERR_SIZE
     ibp.host_free(0)
+
+
+def test_cache_and_hybrid_validation(ibp):
+    # ibp_cache_offsets / ibp_cache_fill (partial cache)
+    _expect(ibp, ibp.ERR_NULL, ibp.cache_offsets, P, 0, 10, P)
+    _expect(ibp, ibp.ERR_NULL, ibp.cache_offsets, 0, P, 10, P)
+    _expect(ibp, ibp.ERR_ALIGN, ibp.cache_offsets, P, P, 10, P + 4)
+    _expect(ibp, ibp.ERR_ALIGN, ibp.cache_offsets, P + 2, P, 10, P)
+    _expect(ibp, ibp.ERR_NULL, ibp.cache_fill, P, 512, P, 10, P, 0, 100)
+    _expect(ibp, ibp.ERR_SIZE, ibp.cache_fill, P, 500, P, 10, P, P, 100)
+    _expect(ibp, ibp.ERR_SIZE, ibp.cache_fill, P, 0, P, 10, P, P, 100)
+    _expect(ibp, ibp.ERR_ALIGN, ibp.cache_fill, P, 512, P, 10, P, P + 8, 100)
+    _expect(ibp, ibp.ERR_ALIGN, ibp.cache_fill, P, 512, P, 10, P + 4, P, 100)
+    # ibp_gather_decompress_hybrid
+    f = ibp.gather_decompress_hybrid
+    ok = [P, 10 * 512, 512, P, 4096, P, P, 10, P, 4, 512, 256, P, P, P]
+    names = ["store", "sbytes", "slot", "cache", "cbytes", "offs", "pb", "nt", "ids", "nids",
+             "tb", "cb", "mask", "bv", "out"]
+
+    def args(**kw):
+        a = list(ok)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return a
+    _expect(ibp, ibp.ERR_NULL, f, *args(cache=0))
+    _expect(ibp, ibp.ERR_NULL, f, *args(offs=0))
+    _expect(ibp, ibp.ERR_NULL, f, *args(store=0))
+    _expect(ibp, ibp.ERR_SIZE, f, *args(sbytes=10 * 512 - 1))
+    _expect(ibp, ibp.ERR_SIZE, f, *args(slot=500))
+    _expect(ibp, ibp.ERR_SIZE, f, *args(tb=6))
+    _expect(ibp, ibp.ERR_CHUNK, f, *args(cb=100))
+    _expect(ibp, ibp.ERR_ALIGN, f, *args(cache=P + 8))
+    _expect(ibp, ibp.ERR_ALIGN, f, *args(offs=P + 4))
+    _expect(ibp, ibp.ERR_ALIGN, f, *args(out=P + 4))
+
+
+def test_indexed_cache_validation(ibp):
+    fa = ibp.compact_offsets_aligned
+    _expect(ibp, ibp.ERR_NULL, fa, 0, 10, 128, P)
+    for bad in (0, 8, 96, 8192):
+        _expect(ibp, ibp.ERR_ALIGN, fa, P, 10, bad, P)
+    _expect(ibp, ibp.ERR_ALIGN, fa, P, 10, 128, P + 4)
+    fi = ibp.cache_index
+    _expect(ibp, ibp.ERR_NULL, fi, 0, 10, P)
+    _expect(ibp, ibp.ERR_SIZE, fi, P, 1 << 32, P)
+    _expect(ibp, ibp.ERR_ALIGN, fi, P, 10, P + 4)
+    f = ibp.gather_decompress_indexed
+    ok = [P, 1 << 20, 128, P, 10, P, 4, 512, 1024, P, P, P]
+    names = ["cache", "cbytes", "align", "index", "nt", "ids", "nids", "tb", "cb", "mask", "bv",
+             "out"]
+
+    def args(**kw):
+        a = list(ok)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return a
+    _expect(ibp, ibp.ERR_NULL, f, *args(index=0))
+    _expect(ibp, ibp.ERR_NULL, f, *args(cache=0))
+    _expect(ibp, ibp.ERR_CHUNK, f, *args(cb=256))            # two chunks
+    _expect(ibp, ibp.ERR_SIZE, f, *args(tb=768, cb=1024))    # no kernel shape for 768 B
+    _expect(ibp, ibp.ERR_ALIGN, f, *args(align=100))
+    _expect(ibp, ibp.ERR_SIZE, f, *args(nt=1 << 32))
+    _expect(ibp, ibp.ERR_SIZE, f, *args(cache=(1 << 48) - 4096, cbytes=8192))
+    _expect(ibp, ibp.ERR_ALIGN, f, *args(out=P + 4))
+    _expect(ibp, ibp.ERR_ALIGN, f, *args(index=P + 4))
+
+
+def test_valid_call_without_a_device_reports_hip_error(ibp):
+    """With no GPU visible, a call whose arguments are valid fails with
+    IBP_ERR_HIP (and the HIP runtime's message) instead of crashing.  The
+    calls used enqueue nothing even when a device is present (zero rows or
+    bytes), so the test is safe to run anywhere; it only asserts the error
+    where no device exists."""
+    import torch
+    has_device = torch.cuda.device_count() > 0
+    calls = [
+        (ibp.gather_decompress, (P, 10 * 512, 512, None, P, 10, P, 0, 512, 256, P, P, P)),
+        (ibp.raw_gather, (P, 512, 10, P, 0, 512, P)),
+        (ibp.stream_read, (P, 0, 0, P)),
+    ]
+    for fn, a in calls:
+        if has_device:
+            fn(*a, stream=0)
+            continue
+        with pytest.raises(ibp.IbpError) as e:
+            fn(*a, stream=0)
+        assert e.value.code == ibp.ERR_HIP, (fn.__name__, e.value.code, ibp.last_error())
+        assert "HIP error" in ibp.last_error()

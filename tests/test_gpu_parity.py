@@ -196,11 +196,11 @@ def test_mask_zero_and_all_ones():
     assert (got == same[:3]).all()
 
 
-# Large batches of one-chunk tensors gathered from an HBM cache take the
-# stream kernel (batches of at least 8 * RPI * 8 * 256 ids: 65,536 for 256 B
-# tensors, 32,768 for 512 B, 16,384 for 1 KB).  Ragged tails, repeated and
-# invalid ids, tensors that do and do not participate, and both degenerate
-# Masks (all zero: every tensor whole; all ones: empty payloads).
+# One-chunk tensors of 256 B, 512 B or 1 KB gathered from an HBM cache through
+# the offset table take k_gather_cache (any batch size; large batches here, short
+# ones at the end).  Ragged tails, repeated and invalid ids, tensors that do and
+# do not participate, and both degenerate Masks (all zero: every tensor whole;
+# all ones: empty payloads).
 STREAM_CASES = [("dense_gnn", 512, 1024, 3000, 40037), ("dlrm_1k", 1024, 4096, 2000, 20011),
                 ("tiny-256", 256, 256, 2500, 70001), ("dense_gnn", 512, 4096, 1500, 33000)]
 
@@ -222,7 +222,7 @@ def test_stream_cache_large_batches(key, B, C, n, nb, law):
     else:
         rows, T = np.tile(rng.integers(0, 256, (1, B), dtype=np.uint8), (n, 1)), 0.99
     slot = (B + 127) // 128 * 128
-    G.log(f"[parity] stream kernel: {key} {law} B={B} C={C} n={n} ids={nb}")
+    G.log(f"[parity] one-chunk cache gather: {key} {law} B={B} C={C} n={n} ids={nb}")
     mask, bitval = G.check_metadata(rows, T)
     if law == "mask0":
         assert not mask.any()
@@ -240,7 +240,7 @@ def test_stream_cache_large_batches(key, B, C, n, nb, law):
     ids[-1] = n - 1
     got = G.gpu_gather(cache, total, 0, offsets, part, n, ids, B, C, mask, bitval)
     want = O.gather_decompress(o_store, o_part, n, ids, B, C, mask, bitval, slot_bytes=slot)
-    assert (got == want).all(), f"{key} {law}: stream gather differs from the oracle"
+    assert (got == want).all(), f"{key} {law}: cache gather differs from the oracle"
     assert (got == G.expected_rows(rows, ids)).all()
     # entries marked IBP_NOT_CACHED give zero rows, in large and short batches
     gone = rng.choice(n, 16, replace=False)
@@ -627,3 +627,101 @@ def test_hybrid_cache_and_store(key, n, frac):
     cached[inr] = select[ids[inr]] != 0
     assert (got2[cached] == got[cached]).all() and not got2[~cached].any()
     store.free()
+
+
+# ------------------------------------------- aligned cache, rank index, indexed gather
+
+def _scattered_rows(rng, n, B):
+    """Rows whose invariant bits are scattered over each word (kept bits in
+    three or more runs), so the indexed gather takes its five-stage expand."""
+    W = B // 4
+    fixed = rng.integers(0, 1 << 32, W, dtype=np.uint64).astype(np.uint32) & np.uint32(0x5A5A5A5A)
+    vals = rng.integers(0, 1 << 32, W, dtype=np.uint64).astype(np.uint32)
+    x = rng.integers(0, 1 << 32, (n, W), dtype=np.uint64).astype(np.uint32)
+    x = (x & ~fixed) | (vals & fixed)
+    flip = rng.random(n) < 0.1  # some tensors break the pattern and stay whole
+    x[flip] ^= fixed
+    return x.view(np.uint8)
+
+
+INDEXED_CASES = [("dense_gnn", 512, 1024, 3000), ("dlrm_1k", 1024, 4096, 2000),
+                 ("tiny-256", 256, 256, 2500), ("dense_gnn", 512, 4096, 1500)]
+
+
+@pytest.mark.parametrize("key,B,C,n", INDEXED_CASES)
+@pytest.mark.parametrize("law", ["workload", "mask0", "mask1", "scattered"])
+def test_indexed_cache(key, B, C, n, law):
+    """ibp_compact_offsets_aligned and ibp_cache_index against the oracle, bit
+    for bit; ibp_gather_decompress_indexed (and the offset-table gather over
+    the same aligned cache) against the oracle's gather and the original rows,
+    on short and large batches with ragged tails, repeats and invalid ids."""
+    from host_transfer_amd import ibp
+    from oracle import oracle as O
+    rng = np.random.default_rng(3 * B + n)
+    if law == "workload" and key != "tiny-256":
+        w = W.WORKLOADS[key].scaled(n)
+        rows, T = W.rows(w), w.threshold
+    elif law == "workload":
+        rows = (rng.standard_normal((n, B // 4)) * 0.1).astype(np.float32).view(np.uint8)
+        T = 0.99
+    elif law == "mask0":
+        rows, T = rng.integers(0, 256, (n, B), dtype=np.uint8), 1.0
+    elif law == "mask1":
+        rows, T = np.tile(rng.integers(0, 256, (1, B), dtype=np.uint8), (n, 1)), 0.99
+    else:
+        rows, T = _scattered_rows(rng, n, B), 0.85
+    slot = (B + 127) // 128 * 128
+    G.log(f"[parity] indexed cache: {key} {law} B={B} C={C} n={n}")
+    mask, bitval = G.check_metadata(rows, T)
+    store, part, lengths = G.gpu_compress(rows, mask, bitval, C, slot)
+    o_store, o_part, o_len = G.check_store(rows, mask, bitval, C, slot, store, part, lengths)
+    # rank index
+    index = torch.full(((n + 31) // 32,), -1, dtype=torch.int64, device="cuda")
+    ibp.cache_index(part, n, index)
+    assert (G.host(index).view(np.uint64) == O.cache_index(o_part, n)).all(), "rank index differs"
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rpi = {256: 4, 512: 2, 1024: 1}[B]
+    big = 8 * rpi * 8 * cus  # offset-table launches of at least this many ids take k_gather_cache
+    for A in (16, 128):
+        offsets = torch.zeros(n + 1, dtype=torch.int64, device="cuda")
+        ibp.compact_offsets_aligned(lengths, n, A, offsets)
+        o_off, o_cache = O.compact_aligned(o_store, slot, o_len, A)
+        g_off = G.host(offsets).view(np.uint64)
+        assert (g_off == o_off).all(), f"aligned offsets differ (A={A})"
+        total = int(g_off[-1])
+        cache = torch.full((max(total, 16),), 0x3C, dtype=torch.int8, device="cuda")
+        ibp.cache_fill(store, slot, lengths, n, offsets, cache, total)
+        g_cache = G.host(cache).view(np.uint8)
+        for t in rng.choice(n, min(n, 300), replace=False):
+            o, L = int(o_off[t]), int(o_len[t])
+            assert (g_cache[o:o + L] == o_cache[o:o + L]).all(), f"cache entry {t} differs"
+        d_mask, d_bv = G.dev(mask), G.dev(bitval)
+        for nb in (1, 63, 65, 500, 4097, max(big + 1237, 40037)):
+            ids = rng.integers(0, n, nb)
+            if nb > 3:
+                ids[rng.integers(0, nb, max(1, nb // 50))] = rng.choice([-1, n, n + 7, 1 << 40])
+                ids[-1] = n - 1
+            want = O.gather_decompress(o_cache, o_part, n, ids, B, C, mask, bitval,
+                                       offsets=o_off)
+            assert (want == G.expected_rows(rows, ids)).all()
+            out = torch.full((nb * B,), -1, dtype=torch.int8, device="cuda")
+            d_ids = G.dev(ids.astype(np.int64))
+            ibp.gather_decompress_indexed(cache, total, A, index, n, d_ids, nb, B, C, d_mask,
+                                          d_bv, out)
+            got = G.host(out).view(np.uint8).reshape(nb, B)
+            assert (got == want).all(), f"{key} {law} A={A} nb={nb}: indexed gather differs"
+            # the offset-table gather over the same aligned cache
+            got = G.gpu_gather(cache, total, 0, offsets, part, n, ids, B, C, mask, bitval)
+            assert (got == want).all(), f"{key} {law} A={A} nb={nb}: table gather differs"
+        # a cache_bytes that cuts the last entries: their rows are zero, no read past it
+        cut = max(16, total - 3 * slot)
+        ids = np.concatenate([np.arange(n - 8, n), rng.integers(0, n, 200)])
+        out = torch.full((len(ids) * B,), -1, dtype=torch.int8, device="cuda")
+        ibp.gather_decompress_indexed(cache, cut, A, index, n, G.dev(ids), len(ids), B, C, d_mask,
+                                      d_bv, out)
+        got = G.host(out).view(np.uint8).reshape(len(ids), B)
+        units = (o_len[ids].astype(np.int64) + 15) // 16
+        inside = o_off[ids].astype(np.int64) + 16 * units <= cut
+        want = G.expected_rows(rows, ids)
+        want[~inside & (units > 0)] = 0
+        assert (got == want).all(), f"{key} {law} A={A}: cut cache"

@@ -44,6 +44,9 @@ MUTANTS = [
     ("decode ignores participation", [("if (p && get_bit(mask, b))", "if (get_bit(mask, b))")]),
     ("compact aligns to 8 bytes", [("(((uint64_t)lengths[t] + 15) / 16) * 16",
                                     "(((uint64_t)lengths[t] + 7) / 8) * 8")]),
+    ("aligned entry one unit too large", [("while (size < lengths[t])", "while (size <= lengths[t])")]),
+    ("rank counts its own word", [("index[w] = (before << 32) | word;\n        for (unsigned b = 0; b < 32; b++)\n            before += (word >> b) & 1;",
+                                   "for (unsigned b = 0; b < 32; b++)\n            before += (word >> b) & 1;\n        index[w] = (before << 32) | word;")]),
     ("last byte not cleared", [("memset(out, 0, tensor_bytes);", "(void)0;")]),
     ("partial last chunk dropped", [("return (tensor_bytes + chunk_bytes - 1) / chunk_bytes;",
                                      "return tensor_bytes / chunk_bytes;")]),

@@ -38,6 +38,10 @@ def test_compact(orc, rng):
     P.pin_compact(orc, rng)
 
 
+def test_compact_aligned(orc, rng):
+    P.pin_compact_aligned(orc, rng)
+
+
 def test_invalid_ids(orc, rng):
     P.pin_invalid_ids(orc, rng)
 
