@@ -9,18 +9,31 @@ over PCIe with GPU-initiated loads.
 
 Prints ONE JSON line.  `value` is decompressed GB/s (ids x tensor bytes per
 second of wall time over the timed steps, inputs already resident).  Extra
-objects: `roofline` (the gather kernel against the host-link peak),
-`cpu_baseline` (the CPU oracle on a bounded sample of the same batches),
-`pinned_path` (the other workloads from pinned host memory, and the K/V decode
-step), `hbm_path` (the same kernel reading a compressed cache in HBM), `hybrid_path`
-(cache hits from HBM and misses over PCIe in one launch, at a fixed HBM budget,
-compressed against uncompressed tensors), probes of the link, and the transfer
-speedup over an uncompressed GPU gather of the same rows ([JH] Table 1
-discussion: transfer speedup against plain transfers).
+objects:
+  roofline           the gather kernel against the host-link peak (63 GB/s
+                     published; the measured DMA and zero-copy peaks beside it),
+                     with the link bytes rocprofv3 counted per launch as traffic;
+  cpu_baseline       the CPU oracle on a bounded sample of the same batches;
+  hybrid_path        cache hits from HBM and misses over PCIe in one launch, at a
+                     fixed HBM budget, compressed against uncompressed tensors;
+  configs            the tiny table as an HBM cache (config 1) and the sparse
+                     table at T = 0.95 (config 2);
+  pinned_path        dense GNN and DLRM tables from pinned host memory (link
+                     fractions on the bytes of each batch's distinct tensors);
+  hbm_path           the same tables as compressed caches in HBM: the workload's
+                     batch, 1M Zipf ids and 1M distinct ids, three cache layouts,
+                     against the uncompressed gather of the same ids;
+  kv_step            the OPT-13B K/V decode step, all 80 (layer, K|V) pairs;
+  sampled_metadata   Masks from 1 %, 5 %, 10 % samples against all tensors;
+  weight_stream      one OPT-13B decoder layer's BF16 weights streamed in;
+  saving_sweep       throughput against space saving (0-90 %) and chunk size;
+  transfer_ablation  small random tensors by transfer method;
+and the transfer speedup over an uncompressed GPU gather of the same rows
+([JH] Table 1 discussion: transfer speedup against plain transfers).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sparse_gnn]
-       [--pinned-workloads dense_gnn,dlrm_1k,dlrm_2k|none] [--kv-pairs-default 8]
-       [--hbm-workloads dense_gnn,dlrm_1k|none] [--hbm-large-batch N]
+       [--pinned-workloads dense_gnn,dlrm_1k,dlrm_2k|none] [--kv-pairs-default 80]
+       [--hbm-workloads dense_gnn,dlrm_1k|none] [--hbm-large-batch N] [--no-extras]
        [--mode default|ablation|sweep|kv-step|configs]
        [--host-flags default|coherent|noncoherent] [--no-cpu-baseline] [--threshold T]
 """
@@ -40,16 +53,39 @@ if ROOT not in sys.path:
 PCIE5_X16_GBPS = 63.0      # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes x 128/130 / 8
 HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E
 
-# HBM/host traffic of the headline launch from rocprofv3 FETCH_SIZE and
-# WRITE_SIZE (KiB per dispatch), scaled by what the same counters read for
-# transfers of known size (factors below).  Valid only for the gather code
-# they were measured on: bench.py reports them while the sources (comments
-# and spacing aside) still hash to GATHER_SOURCES_SHA256, else traffic is null.
+# Traffic of the headline launch (8,192 sparse_gnn ids) from rocprofv3 counter
+# runs of this benchmark, bytes per dispatch, each counter calibrated by a
+# transfer of known size in the same run: host-link reads
+# (TCC_EA0_RDREQ_IO_32B x 32 B, a 1 GiB zero-copy read reads as 1.000), HBM reads
+# and writes (TCC_EA0_RDREQ_DRAM_32B and TCC_EA0_WRREQ_WRITE_DRAM_32B x 32 B, a 4
+# GiB read and a 1 GiB fill read as 1.000), and FETCH_SIZE / WRITE_SIZE in KiB
+# (factors 2.000 / 1.000).  Valid only for the gather code they were measured
+# on: bench.py reports them while the sources (comments and spacing aside)
+# still hash to GATHER_SOURCES_SHA256, else traffic is null.
 GATHER_SOURCES = ("host_transfer_amd/csrc/gather.hip", "host_transfer_amd/csrc/ibp_plan.h",
                   "host_transfer_amd/csrc/ibp_device.h")
-GATHER_SOURCES_SHA256 = "58b8af378d6fa2a51200dc6deab817e83de123c60703b06eddacee70737fb4f3"
-TRAFFIC_FETCH_KIB, TRAFFIC_WRITE_KIB = 6168.4, 48473.9  # sparse_gnn, 8,192 ids
+GATHER_SOURCES_SHA256 = "097c9a51496424eb6d8f62f48259248eb101f057aa5c4df73a099b1f54f285e7"
+HEADLINE_COUNTERS = {"link_read": 10632448, "hbm_read": 1695341, "hbm_write": 49653440,
+                     "fetch_size_kib": 6168.5, "write_size_kib": 48480.7}
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+# HBM bytes (read, written) per 1M-id cache launch, from the same runs (the
+# summary in profiles/k_gather_cache__dense_gnn_dlrm_1k_hbm.md), for the code
+# of gather_cache.hip they were measured on (CACHE_SOURCES_SHA256).
+CACHE_SOURCES = ("host_transfer_amd/csrc/gather_cache.hip", "host_transfer_amd/csrc/ibp_plan.h",
+                 "host_transfer_amd/csrc/ibp_device.h")
+CACHE_SOURCES_SHA256 = "8b0747f508c8b869821d2c6e13105203611541ec050690e868556990da092725"
+HBM_COUNTERS = {
+    ("dense_gnn", "zipf"): {"index_128B": (184.05e6, 536.87e6), "index_16B": (222.36e6, 536.87e6),
+                            "table_16B": (261.42e6, 536.87e6), "raw": (178.79e6, 536.87e6)},
+    ("dense_gnn", "distinct"): {"index_128B": (579.23e6, 536.87e6),
+                                "index_16B": (684.54e6, 536.87e6),
+                                "table_16B": (793.85e6, 536.87e6), "raw": (553.66e6, 536.88e6)},
+    ("dlrm_1k", "zipf"): {"index_128B": (509.97e6, 1073.74e6), "index_16B": (510.41e6, 1073.74e6),
+                          "table_16B": (571.11e6, 1073.74e6), "raw": (542.20e6, 1073.74e6)},
+    ("dlrm_1k", "distinct"): {"index_128B": (1063.59e6, 1073.75e6),
+                              "index_16B": (1063.62e6, 1073.76e6),
+                              "table_16B": (1180.57e6, 1073.76e6), "raw": (1107.31e6, 1073.75e6)},
+}
 
 
 def code_text(src):
@@ -61,10 +97,10 @@ def code_text(src):
     return " ".join(src.split())
 
 
-def gather_sources_sha256(read=None):
+def gather_sources_sha256(read=None, sources=GATHER_SOURCES):
     import hashlib
     h = hashlib.sha256()
-    for rel in GATHER_SOURCES:
+    for rel in sources:
         if read is None:
             with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
                 text = f.read()
@@ -75,10 +111,24 @@ def gather_sources_sha256(read=None):
 
 
 def profiled_traffic():
-    """Scaled bytes per launch from the committed counters, or None."""
+    """Counter bytes of the headline launch (see HEADLINE_COUNTERS), or None
+    when the gather code has changed since they were taken."""
     if GATHER_SOURCES_SHA256 is None or gather_sources_sha256() != GATHER_SOURCES_SHA256:
         return None
-    return round(TRAFFIC_FETCH_KIB * 1024 * FETCH_SCALE + TRAFFIC_WRITE_KIB * 1024 * WRITE_SCALE)
+    c = HEADLINE_COUNTERS
+    return {"link_read": c["link_read"], "hbm_read": c["hbm_read"], "hbm_write": c["hbm_write"],
+            "fetch_size": round(c["fetch_size_kib"] * 1024 * FETCH_SCALE),
+            "write_size": round(c["write_size_kib"] * 1024 * WRITE_SCALE)}
+
+
+def profiled_hbm_bytes(key, kind):
+    """Counter HBM bytes {launch: [read, written]} of a 1M-id cache launch, or
+    None when gather_cache.hip has changed since they were taken."""
+    if (CACHE_SOURCES_SHA256 is None or
+            gather_sources_sha256(sources=CACHE_SOURCES) != CACHE_SOURCES_SHA256):
+        return None
+    c = HBM_COUNTERS.get((key, kind))
+    return None if c is None else {k: [round(v[0]), round(v[1])] for k, v in c.items()}
 
 
 def log(msg):
@@ -107,8 +157,12 @@ def parse():
     p.add_argument("--kv-pairs", type=int, default=80, help="(layer, K|V) pairs in --mode kv-step")
     p.add_argument("--pinned-workloads", default="dense_gnn,dlrm_1k,dlrm_2k",
                    help="other workloads measured from pinned host memory, or 'none'")
-    p.add_argument("--kv-pairs-default", type=int, default=8,
+    p.add_argument("--kv-pairs-default", type=int, default=80,
                    help="(layer, K|V) pairs of the K/V decode step in the default run (0: skip)")
+    p.add_argument("--no-extras", dest="extras", action="store_false",
+                   help="skip the other configurations and rows of the default run (tiny and "
+                        "T=0.95 configs, sampled metadata, weight stream, saving sweep, "
+                        "transfer ablation)")
     return p.parse_args()
 
 
@@ -468,71 +522,134 @@ def measure_workload(torch, ibp, W, key, T, where, host_flags, steps, warmup, wi
     return res
 
 
+def lines_bytes(lengths):
+    """Bytes of the 128 B lines that payloads of these lengths occupy when
+    each starts on a line (the cache compacted with 128 B entries)."""
+    import numpy as np
+    return float(((np.asarray(lengths, np.int64) + 127) // 128 * 128).sum())
+
+
 def measure_hbm(torch, ibp, W, table, args, pr):
-    """The gather kernel on a compacted HBM cache (the table's pinned store
-    compacted into HBM): the workload's batch and a large batch, with the
-    uncompressed HBM gather of the same ids beside it."""
+    """The workload's table as compressed caches in HBM, gathered with the
+    workload's batch, a 1M-id batch of the same Zipf law and a 1M-id batch of
+    distinct ids (uniform, no repeats), against the uncompressed gather of the
+    same ids from the rows in HBM.  Two layouts of the same payloads: entries
+    on 128 B lines found through the rank index (ibp_gather_decompress_indexed)
+    and entries at 16 B found through the offset table (ibp_gather_decompress).
+    Bytes per launch, counted without the GPU's caches: the payloads of the
+    distinct tensors (in whole 128 B lines), the dense rows written and the
+    ids read."""
     import numpy as np
     w = table.w
     key = w.key
-    table.to_hbm(torch, ibp)
-    B, S, N = w.tensor_bytes, w.slot_bytes, w.n_tensors
+    B, C, S, N = w.tensor_bytes, w.chunk_bytes, w.slot_bytes, w.n_tensors
     raw_dev = torch.from_numpy(table.raw.array).cuda()   # uncompressed rows in HBM
-    table.raw.free()
-    res = {"workload": f"{key}: {N} x {B} B, compacted cache of {table.store_bytes / 1e9:.2f} GB in "
-                       f"HBM (mean payload {table.len_host.mean() / B:.4f} of the tensor)",
+    # 128 B entries + rank index, and 16 B entries + offset table
+    off128 = torch.zeros(N + 1, dtype=torch.int64, device="cuda")
+    ibp.compact_offsets_aligned(table.lengths, N, 128, off128)
+    tot128 = int(off128[-1].item())
+    cache128 = torch.empty(max(tot128, 16), dtype=torch.uint8, device="cuda")
+    tm = Timer(torch)
+    s0 = tm.start()
+    ibp.cache_fill(table.store, S, table.lengths, N, off128, cache128, tot128)
+    index = torch.zeros((N + 31) // 32, dtype=torch.int64, device="cuda")
+    ibp.cache_index(table.part, N, index)
+    tm.stop(s0)
+    del off128
+    off16 = torch.zeros(N + 1, dtype=torch.int64, device="cuda")
+    ibp.compact_offsets(table.lengths, N, off16)
+    tot16 = int(off16[-1].item())
+    cache16 = torch.empty(max(tot16, 16), dtype=torch.uint8, device="cuda")
+    ibp.compact(table.store, S, N, off16, cache16, tot16)
+    torch.cuda.synchronize()
+    build_ms = tm.ms()[0]
+    res = {"workload": f"{key}: {N} x {B} B, {C} B chunks, T={w.threshold}, Mask from "
+                       f"{w.sample_fraction:.0%} of the tensors",
+           "cache_128B_entries": {"GB": round(tot128 / 1e9, 3),
+                                  "tensors_per_GB_over_raw": round(N * B / tot128, 4),
+                                  "fill_and_index_ms": round(build_ms, 2)},
+           "cache_16B_entries": {"GB": round(tot16 / 1e9, 3),
+                                 "tensors_per_GB_over_raw": round(N * B / tot16, 4)},
            "batches": []}
-    for nb in (w.batch, args.hbm_large_batch):
-        nbatches = (nb + w.batch - 1) // w.batch
+    rng = np.random.default_rng(20261203)
+    perm = rng.permutation(N)
+    big = args.hbm_large_batch
+    for kind, nb in (("workload batch", w.batch), ("zipf", big), ("distinct", big)):
         steps = max(3, min(args.steps, (64 << 20) // max(1, nb)))
         seqs = []
         for k in range(args.warmup + steps):
-            ids = np.concatenate([W.batch_ids(w, k * nbatches + i) for i in range(nbatches)])[:nb]
-            seqs.append(ids)
+            if kind == "distinct":
+                o = (k * 40503) % (N - nb + 1)
+                seqs.append(perm[o:o + nb].astype(np.int64))
+            else:
+                nbatches = (nb + w.batch - 1) // w.batch
+                seqs.append(np.concatenate([W.batch_ids(w, k * nbatches + i)
+                                            for i in range(nbatches)])[:nb])
         d = [torch.from_numpy(i).cuda() for i in seqs]
         out = torch.empty(nb * B, dtype=torch.uint8, device="cuda")
 
-        def run_ibp(k):
-            ibp.gather_decompress(table.store, table.store_bytes, S, table.offsets, table.part, N,
-                                  d[k], nb, B, w.chunk_bytes, table.mask, table.bitval, out)
+        def run_idx(k):
+            ibp.gather_decompress_indexed(cache128, tot128, 128, index, N, d[k], nb, B, C,
+                                          table.mask, table.bitval, out)
+
+        def run_idx16(k):
+            ibp.gather_decompress_indexed(cache16, tot16, 16, index, N, d[k], nb, B, C,
+                                          table.mask, table.bitval, out)
+
+        def run_tab(k):
+            ibp.gather_decompress(cache16, tot16, S, off16, table.part, N, d[k], nb, B, C,
+                                  table.mask, table.bitval, out)
 
         def run_raw(k):
             ibp.raw_gather(raw_dev, S, N, d[k], nb, B, out)
-        km, _ = region_launches(torch, run_ibp, args.warmup, steps)
-        rm, _ = region_launches(torch, run_raw, args.warmup, steps)
-        kiso = statistics.mean(timed_launches(torch, run_ibp, 0, steps))
-        graph = None
-        if nb == w.batch:
-            graph = graph_launches(torch, run_ibp, min(16, len(d)), max(3, steps // 4))
+        # each launch kind timed twice, alternating, the faster region kept
+        # (short launches vary from one region to the next)
+        fns = {"idx": run_idx, "idx16": run_idx16, "tab": run_tab, "raw": run_raw}
+        best = {k: float("inf") for k in fns}
+        for _ in range(2):
+            for name, f in fns.items():
+                best[name] = min(best[name], region_launches(torch, f, args.warmup, steps)[0])
+        km, km16, tm16, rm = best["idx"], best["idx16"], best["tab"], best["raw"]
         last = seqs[-1]
-        run_ibp(len(seqs) - 1)
-        torch.cuda.synchronize()
         pick = np.linspace(0, nb - 1, 256).astype(np.int64)
-        got = out.view(nb, B)[torch.from_numpy(pick).cuda()].cpu().numpy()
         want = raw_dev.view(N, S)[torch.from_numpy(last[pick]).cuda(), :B].cpu().numpy()
-        if not (got == want).all():
-            raise SystemExit(f"bench: {key} HBM gather differs from the original rows")
-        comp = statistics.mean(float(table.len_host[i].sum()) for i in seqs[args.warmup:])
-        traffic = comp + nb * (B + 16)
-        res["batches"].append({
-            "ids": nb, "kernel_us": round(km * 1e3, 2), "isolated_launch_us": round(kiso * 1e3, 2),
-            "decompressed_GBps": round(nb * B / (km * 1e-3) / 1e9, 1),
-            "roofline": {"bound": "hbm", "achieved": round(traffic / (km * 1e-3) / 1e9, 1),
-                         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": round(traffic / (km * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                         "frac_of_measured_read": round(traffic / (km * 1e-3) / 1e9 /
-                                                        pr["hbm_stream_read_GBps"], 4),
-                         "frac_of_measured_copy": round(traffic / (km * 1e-3) / 1e9 /
-                                                        pr["hbm_copy_read_plus_write_GBps"], 4)},
-            "raw_hbm_gather_us": round(rm * 1e3, 2),
-            "speedup_vs_raw_hbm_gather": round(rm / km, 3),
-            "unique_ids": int(len(np.unique(last))),
-        })
-        if graph is not None:
-            res["batches"][-1]["hip_graph"] = graph
+        for f in (run_idx, run_idx16, run_tab):
+            out.zero_()
+            f(len(seqs) - 1)
+            torch.cuda.synchronize()
+            got = out.view(nb, B)[torch.from_numpy(pick).cuda()].cpu().numpy()
+            if not (got == want).all():
+                raise SystemExit(f"bench: {key} HBM gather differs from the original rows")
+        uniq = [np.unique(i) for i in seqs[args.warmup:]]
+        upay = statistics.mean(lines_bytes(table.len_host[u]) for u in uniq)
+        traffic = upay + nb * (B + 8)
+        achieved = traffic / (km * 1e-3) / 1e9
+        r = {"ids": nb, "id_law": "uniform, no repeats" if kind == "distinct" else
+             f"{w.id_law} alpha={w.zipf_alpha}",
+             "unique_ids": round(statistics.mean(len(u) for u in uniq), 1),
+             "kernel": "k_gather_cache (rank index, 128 B entries)",
+             "kernel_us": round(km * 1e3, 2),
+             "decompressed_GBps": round(nb * B / (km * 1e-3) / 1e9, 1),
+             "raw_hbm_gather_us": round(rm * 1e3, 2),
+             "speedup_vs_raw_hbm_gather": round(rm / km, 3),
+             "index_16B_entries_us": round(km16 * 1e3, 2),
+             "index_16B_speedup_vs_raw": round(rm / km16, 3),
+             "table_16B_entries_us": round(tm16 * 1e3, 2),
+             "table_16B_speedup_vs_raw": round(rm / tm16, 3),
+             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                          "bytes_per_launch": round(traffic, 1),
+                          "bytes": "distinct tensors' payload lines + rows written + ids",
+                          "frac_of_measured_copy": round(achieved /
+                                                         pr["hbm_copy_read_plus_write_GBps"], 4)}}
+        if kind == "workload batch":
+            r["hip_graph"] = graph_launches(torch, run_idx, min(16, len(d)), max(3, steps // 4))
+        else:
+            r["counter_hbm_bytes_read_written"] = profiled_hbm_bytes(key, kind)
+        res["batches"].append(r)
+        log(f"{key} HBM {kind}: {r}")
         del out, d
-    res["compact_ms"] = round(table.compact_ms, 3)
-    del raw_dev
+    del raw_dev, cache128, cache16, off16, index
     torch.cuda.empty_cache()
     return res
 
@@ -559,12 +676,11 @@ def measure_pinned(torch, ibp, W, key, flags, args, pr):
                        f"T={w.threshold}, {w.batch} {w.id_law} ids per launch",
            "kernel_us": round(km * 1e3, 2),
            "decompressed_GBps": round(w.batch * w.tensor_bytes / (km * 1e-3) / 1e9, 2),
-           "compressed_GBps_over_link": round(achieved, 2),
-           "frac_of_measured": round(achieved / link, 4),
-           "frac_of_zero_copy_read": round(achieved / pr["h2d_zero_copy_read_GBps"], 4),
+           "payload_all_ids_GBps": round(achieved, 2),
            "unique_ids": round(statistics.mean(len(np.unique(i)) for i in m["ids_host"][args.warmup:]), 1),
            "unique_payload_GBps_over_link": round(achieved_u, 2),
            "unique_frac_of_measured": round(achieved_u / link, 4),
+           "unique_frac_of_zero_copy_read": round(achieved_u / pr["h2d_zero_copy_read_GBps"], 4),
            "batch_payload_over_dense": round(comp / (w.batch * w.tensor_bytes), 5),
            "raw_gather_us": round(rm * 1e3, 2),
            "transfer_speedup_vs_raw_gpu_gather": round(rm / km, 3),
@@ -730,7 +846,7 @@ def hip_runtime():
     return hip
 
 
-def run_ablation(torch, ibp, args, pr):
+def run_ablation(torch, ibp, args, pr, pool_bytes=4 << 30):
     """Copy throughput of small random tensors from pinned host memory to the
     GPU by transfer method ([JH] Figure 5 and aligned-copy paragraphs):
     per-tensor DMA issued by the CPU, a CPU gather into a staging buffer
@@ -741,7 +857,6 @@ def run_ablation(torch, ibp, args, pr):
     import numpy as np
     hip = hip_runtime()
     H2D = 1
-    pool_bytes = 4 << 30
     hb = ibp.HostBuffer(pool_bytes + 4096)
     rng = np.random.default_rng(5)
     view64 = hb.array[:(pool_bytes // 8) * 8].view(np.uint64)
@@ -805,11 +920,10 @@ def run_ablation(torch, ibp, args, pr):
         log(f"ablation {r}")
         del out, d_ids
     hb.free()
-    print(json.dumps({"metric": "CPU-to-GPU copy throughput of 8,192 random tensors by transfer "
-                                "method", "unit": "GB/s", "higher_is_better": True,
-                      "limit": {"pcie5_x16_GBps": PCIE5_X16_GBPS, **pr}, "results": rows,
-                      "host_threads": threads, "device": torch.cuda.get_device_name(0)}),
-          flush=True)
+    return {"metric": "CPU-to-GPU copy throughput of 8,192 random tensors by transfer method",
+            "unit": "GB/s", "higher_is_better": True, "pool_GiB": pool_bytes / (1 << 30),
+            "limit": {"pcie5_x16_GBps": PCIE5_X16_GBPS, **pr}, "results": rows,
+            "host_threads": threads}
 
 
 def run_sweep(torch, ibp, args, pr):
@@ -856,7 +970,7 @@ def run_sweep(torch, ibp, args, pr):
         log(f"sweep {r}")
 
     words = raw.array.reshape(N, S).view(np.uint32)
-    for k in (32, 28, 24, 20, 16, 12, 8, 4):
+    for k in (32, 28, 24, 20, 16, 12, 8, 4, 3):
         hi = rng.integers(0, 1 << 32, B // 4, dtype=np.uint64).astype(np.uint32)
         low = (1 << k) - 1
         for i in range(0, N, 8192):
@@ -864,19 +978,127 @@ def run_sweep(torch, ibp, args, pr):
             words[i:i + 8192] = (r.astype(np.uint32) & np.uint32(low)) | (hi & np.uint32(~low & 0xFFFFFFFF))
         for C in (256, 1024, 4096):
             measure(f"kept {k} of 32 bits", C, {"kept_bits": k})
-    # BF16 weights: 2,048 values N(0, 0.02) per 4 KB tensor
-    for i in range(0, N, 8192):
-        x = (rng.standard_normal((min(8192, N - i), B // 2)) * 0.02).astype(np.float32)
-        # bfloat16 = the high half of the float32 encoding (truncated)
-        words[i:i + 8192] = (x.view(np.uint32) >> 16).astype(np.uint16).view(np.uint32)
-    for C in (256, 1024, 4096):
-        measure("bf16 weights N(0, 0.02)", C, {"dtype": "bf16"})
     raw.free()
     store.free()
-    print(json.dumps({"metric": "decompressed GB/s against space saving (pinned host store)",
-                      "unit": "GB/s", "higher_is_better": True, "link_peak_GBps": link,
-                      "ids": n, "tensors": N, "tensor_bytes": B, "results": results,
-                      "device": torch.cuda.get_device_name(0)}), flush=True)
+    return {"metric": "decompressed GB/s against space saving (pinned host store)",
+            "unit": "GB/s", "higher_is_better": True, "link_peak_GBps": link,
+            "ids": n, "tensors": N, "tensor_bytes": B, "results": results}
+
+
+def bf16_rne(x):
+    """bfloat16 encodings (uint16) of float32 values, rounded to nearest even."""
+    import numpy as np
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def run_weight_stream(torch, ibp, args, pr):
+    """BF16 weight offloading ([G-EN] Results: BF16 weights offloaded to CPU
+    memory compress by up to 27 % and cut latency by 22 %): the weight matrices
+    of one OPT-13B decoder layer (hidden 5,120, MLP 20,480: four 5,120 x 5,120
+    attention matrices and two 5,120 x 20,480 MLP matrices, 314.6 M bf16
+    values, 629 MB) held in pinned host memory as 10,240 B rows (5,120 bf16;
+    an MLP row of 20,480 values is four such rows), values N(0, s^2) with
+    s = 0.02 (attention) and 0.014 (MLP), Mask from a 1 % sample of the rows,
+    256 B chunks.  A step fetches the whole layer in row order (a contiguous
+    stream) in one gather + decompress launch, against one DMA of the raw
+    weights and the raw GPU gather of the same rows."""
+    import numpy as np
+    B, C = 10240, 256
+    H, F = 5120, 20480
+    n_attn = 4 * H * H // (B // 2)           # 20,480 rows
+    n_mlp = 2 * H * F // (B // 2)            # 40,960 rows
+    N = n_attn + n_mlp
+    S = B
+    rng = np.random.default_rng(13)
+    raw = ibp.HostBuffer(N * S)
+    rows = raw.array.reshape(N, S).view(np.uint16)
+    blk = 2048
+    for i in range(0, N, blk):
+        k = min(blk, N - i)
+        sd = 0.02 if i < n_attn else 0.014
+        rows[i:i + k] = bf16_rne(rng.standard_normal((k, B // 2), dtype=np.float32) * sd)
+    sample = np.sort(rng.choice(N, N // 100, replace=False)).astype(np.int64)
+    mask = torch.zeros(B // 4, dtype=torch.int32, device="cuda")
+    bitval = torch.zeros_like(mask)
+    counts = torch.zeros(8 * B, dtype=torch.int32, device="cuda")
+    ibp.build_metadata(raw, S, torch.from_numpy(sample).cuda(), len(sample), B, 0.99, mask,
+                       bitval, counts)
+    store = ibp.HostBuffer(N * S)
+    n_c = ibp.num_chunks(B, C)
+    part = torch.zeros((N * n_c + 31) // 32, dtype=torch.int32, device="cuda")
+    lengths = torch.zeros(N, dtype=torch.int32, device="cuda")
+    ibp.compress(raw, S, N, 0, N, B, C, mask, bitval, store, S, part, lengths)
+    ids = torch.arange(N, dtype=torch.int64, device="cuda")
+    out = torch.empty(N * B, dtype=torch.uint8, device="cuda")
+    steps = max(3, min(args.steps, 10))
+    km, _ = region_launches(torch, lambda k: ibp.gather_decompress(
+        store, N * S, S, None, part, N, ids, N, B, C, mask, bitval, out), 2, steps)
+    pick = np.linspace(0, N - 1, 97).astype(np.int64)
+    got = out.view(N, B)[torch.from_numpy(pick).cuda()].cpu().numpy()
+    if not (got == raw.array.reshape(N, S)[pick]).all():
+        raise SystemExit("bench: the weight stream is not lossless")
+    rm, _ = region_launches(torch, lambda k: ibp.raw_gather(raw, S, N, ids, N, B, out), 2, steps)
+    hip = hip_runtime()
+    stream = torch.cuda.current_stream().cuda_stream
+    dm, _ = region_launches(torch, lambda k: hip.hipMemcpyAsync(out.data_ptr(), raw.ptr, N * B, 1,
+                                                                stream), 2, steps)
+    L = lengths.cpu().numpy().view(np.uint32).astype(np.float64)
+    comp = float(L.sum())
+    link = max(pr["h2d_dma_GBps"], pr["h2d_zero_copy_read_GBps"])
+    res = {"workload": f"OPT-13B decoder layer weights, bf16, {N} rows x {B} B ({N * B / 1e6:.0f} MB), "
+                       f"{C} B chunks, T=0.99, Mask from 1 % of the rows, pinned host",
+           "saving": round(1 - comp / (N * B), 4),
+           "kernel_ms": round(km, 3), "dma_ms": round(dm, 3), "raw_gather_ms": round(rm, 3),
+           "latency_cut_vs_dma": round(1 - km / dm, 4),
+           "speedup_vs_dma": round(dm / km, 3), "speedup_vs_raw_gather": round(rm / km, 3),
+           "decompressed_GBps": round(N * B / (km * 1e-3) / 1e9, 1),
+           "payload_GBps_over_link": round(comp / (km * 1e-3) / 1e9, 2),
+           "frac_of_measured_link": round(comp / (km * 1e-3) / 1e9 / link, 4)}
+    raw.free()
+    store.free()
+    del out, ids
+    torch.cuda.empty_cache()
+    log(f"weight stream: {res}")
+    return res
+
+
+def measure_sampling(torch, ibp, table, fractions=(0.01, 0.05, 0.10, 1.0)):
+    """Mask/Bitval from samples of 1 %, 5 % and 10 % of the tensors against all
+    of them ([JH] sampling paragraph: compression ratios from such samples
+    stay close to those of the full data): for each, the Mask words that
+    differ from the full-data Mask and the mean payload of the whole table
+    compressed with it."""
+    import numpy as np
+    w = table.w
+    B, C, S, N = w.tensor_bytes, w.chunk_bytes, w.slot_bytes, w.n_tensors
+    rng = np.random.default_rng(31)
+    n_c = ibp.num_chunks(B, C)
+    part = torch.zeros((N * n_c + 31) // 32, dtype=torch.int32, device="cuda")
+    lengths = torch.zeros(N, dtype=torch.int32, device="cuda")
+    store = torch.empty(N * S, dtype=torch.uint8, device="cuda")
+    counts = torch.zeros(8 * B, dtype=torch.int32, device="cuda")
+    out = []
+    masks = {}
+    for f in sorted(fractions, reverse=True):
+        n = max(1, int(round(f * N)))
+        sid = None if n == N else torch.from_numpy(
+            np.sort(rng.choice(N, n, replace=False)).astype(np.int64)).cuda()
+        m = torch.zeros(B // 4, dtype=torch.int32, device="cuda")
+        v = torch.zeros_like(m)
+        ibp.build_metadata(table.raw, S, sid, n, B, w.threshold, m, v, counts)
+        ibp.compress(table.raw, S, N, 0, N, B, C, m, v, store, S, part, lengths)
+        L = lengths.cpu().numpy().view(np.uint32).astype(np.float64)
+        masks[f] = m.cpu().numpy().view(np.uint32)
+        out.append({"sample": f, "rows": n,
+                    "mask_words_differing_from_full": int((masks[f] != masks[1.0]).sum()),
+                    "mean_payload_over_tensor": round(float(L.mean()) / B, 5)})
+    del store, part, lengths
+    torch.cuda.empty_cache()
+    full = out[0]["mean_payload_over_tensor"]
+    for r in out:
+        r["payload_over_full_data_payload"] = round(r["mean_payload_over_tensor"] / full, 5)
+    return {"workload": w.key, "T": w.threshold, "results": sorted(out, key=lambda r: r["sample"])}
 
 
 def run_kv_step(torch, ibp, W, args, pr, pairs=None):
@@ -1107,6 +1329,70 @@ def run_configs(torch, ibp, W, args, pr):
             "configs": rows_out, "device": torch.cuda.get_device_name(0), "host": host_info()}
 
 
+def measure_tiny(torch, ibp, W, args):
+    """Config 1: 4,096 tensors of 512 B held as a compacted cache in HBM
+    (about 1.8 MB, so it sits in the 256 MB last-level cache: a latency point,
+    not an HBM-bandwidth one), gathered in a seeded permutation of all ids,
+    against the uncompressed gather of the same rows from HBM."""
+    import numpy as np
+    w = W.WORKLOADS["tiny"]
+    table = Table(torch, ibp, W, w, w.threshold, "hbm", ibp.HOST_DEFAULT, keep_raw=True)
+    B, S, N = w.tensor_bytes, w.slot_bytes, w.n_tensors
+    raw_dev = torch.from_numpy(table.raw.array).cuda()
+    steps = max(5, args.steps)
+    seqs = [W.batch_ids(w, k) for k in range(args.warmup + steps)]
+    d = [torch.from_numpy(i).cuda() for i in seqs]
+    out = torch.empty(w.batch * B, dtype=torch.uint8, device="cuda")
+    km, _ = region_launches(torch, lambda k: table.gather(ibp, d[k], w.batch, out), args.warmup,
+                            steps)
+    check_rows(table, seqs[-1], out)
+    rm, _ = region_launches(torch, lambda k: ibp.raw_gather(raw_dev, S, N, d[k], w.batch, B, out),
+                            args.warmup, steps)
+    res = {"workload": f"tiny: {N} x {B} B, {w.chunk_bytes} B chunks, T={w.threshold}, Mask from "
+                       f"all tensors, compacted cache of {table.store_bytes / 1e6:.2f} MB in HBM",
+           "ids": w.batch, "id_law": "a permutation of all ids",
+           "mean_payload_over_tensor": round(float(table.len_host.mean()) / B, 5),
+           "kernel_us": round(km * 1e3, 2),
+           "decompressed_GBps": round(w.batch * B / (km * 1e-3) / 1e9, 1),
+           "raw_hbm_gather_us": round(rm * 1e3, 2), "speedup_vs_raw_hbm_gather": round(rm / km, 3),
+           "offline": {"metadata_ms": round(table.meta_ms, 3),
+                       "compress_ms": round(table.compress_ms, 3),
+                       "compact_ms": round(table.compact_ms, 3)},
+           "note": "cache and rows fit the 256 MB last-level cache: launch latency, not bandwidth"}
+    table.raw.free()
+    del table, raw_dev, out, d
+    torch.cuda.empty_cache()
+    log(f"tiny: {res}")
+    return res
+
+
+def measure_sparse_t95(torch, ibp, W, args, flags, pr):
+    """Config 2 at T = 0.95 (the same sparse features and batches as the
+    headline, a lower threshold)."""
+    import numpy as np
+    m = measure_workload(torch, ibp, W, "sparse_gnn", 0.95, "pinned", flags, args.steps,
+                         args.warmup, with_raw=True)
+    t, w = m["table"], W.WORKLOADS["sparse_gnn"]
+    km = m["kernel_ms"]
+    comp = statistics.mean(m["comp_bytes"])
+    link = max(pr["h2d_dma_GBps"], pr["h2d_zero_copy_read_GBps"])
+    res = {"workload": f"sparse_gnn: {w.n_tensors} x {w.tensor_bytes} B, {w.chunk_bytes} B chunks, "
+                       f"T=0.95, Mask from 1 % of the tensors, pinned host, {w.batch} uniform ids",
+           "mean_payload_over_tensor": round(float(t.len_host.mean()) / w.tensor_bytes, 5),
+           "kernel_us": round(km * 1e3, 2),
+           "decompressed_GBps": round(w.batch * w.tensor_bytes / (km * 1e-3) / 1e9, 2),
+           "payload_GBps_over_link": round(comp / (km * 1e-3) / 1e9, 2),
+           "frac_of_measured_link": round(comp / (km * 1e-3) / 1e9 / link, 4),
+           "raw_gather_us": round(m["raw_kernel_ms"] * 1e3, 2),
+           "transfer_speedup_vs_raw_gpu_gather": round(m["raw_kernel_ms"] / km, 3)}
+    t.raw.free()
+    t.store.free()
+    del t, m
+    torch.cuda.empty_cache()
+    log(f"sparse_gnn T=0.95: {res}")
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -1127,9 +1413,12 @@ def main():
     pr = probes(torch, ibp, flags)
     log(f"probes {pr}")
     if args.mode == "ablation":
-        return run_ablation(torch, ibp, args, pr)
+        print(json.dumps(run_ablation(torch, ibp, args, pr)), flush=True)
+        return
     if args.mode == "sweep":
-        return run_sweep(torch, ibp, args, pr)
+        print(json.dumps({"sweep": run_sweep(torch, ibp, args, pr),
+                          "weight_stream": run_weight_stream(torch, ibp, args, pr)}), flush=True)
+        return
     if args.mode == "kv-step":
         print(json.dumps(run_kv_step(torch, ibp, W, args, pr)), flush=True)
         return
@@ -1153,6 +1442,7 @@ def main():
     achieved = comp / (kern_ms * 1e-3) / 1e9
     raw_ms = m["raw_kernel_ms"]
     link_peak = max(pr["h2d_dma_GBps"], pr["h2d_zero_copy_read_GBps"])
+    traffic = profiled_traffic()
     log(f"{key}: {value:.1f} GB/s decompressed, kernel {kern_ms * 1e3:.1f} us, "
         f"{achieved:.1f} GB/s compressed over the link, raw gather {raw_ms * 1e3:.1f} us")
 
@@ -1184,7 +1474,9 @@ def main():
             "peak": PCIE5_X16_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / PCIE5_X16_GBPS, 4),
-            "traffic": profiled_traffic(),
+            "traffic": None if traffic is None else traffic["link_read"],
+            "traffic_unit": "bytes per launch read over the host link (rocprofv3 counters)",
+            "traffic_counters": traffic,
             "peak_measured": round(link_peak, 2),
             "frac_of_measured": round(achieved / link_peak, 4),
             "peak_zero_copy_read": pr["h2d_zero_copy_read_GBps"],
@@ -1233,6 +1525,7 @@ def main():
         result["cpu_baseline"] = cpu_baseline(table, m["ids_host"][args.warmup:], args.cpu_seconds)
     else:
         result["cpu_baseline"] = None
+    sampling = [measure_sampling(torch, ibp, table)] if args.extras else []
     table.raw.free()
     table.store.free()
     del table, m
@@ -1241,6 +1534,9 @@ def main():
     # --- the other pinned-host workloads (their own batch sizes), then
     #     the same tables compacted into HBM caches: the workload's batch and a
     #     large batch (1M ids) that fills the GPU
+    if args.extras:
+        result["configs"] = {"tiny_hbm": measure_tiny(torch, ibp, W, args),
+                             "sparse_gnn_T095": measure_sparse_t95(torch, ibp, W, args, flags, pr)}
     result["pinned_path"] = []
     result["hbm_path"] = []
     hbm = [] if args.hbm_workloads == "none" else args.hbm_workloads.split(",")
@@ -1252,6 +1548,9 @@ def main():
             log(f"{key} multi-table: {res['multi_table']}")
         if key in pinned:
             result["pinned_path"].append(res)
+        if args.extras:
+            sampling.append(measure_sampling(torch, ibp, tb))
+            log(f"{key} sampling: {sampling[-1]}")
         if key in hbm:
             result["hbm_path"].append(measure_hbm(torch, ibp, W, tb, args, pr))
         if tb.raw is not None:
@@ -1261,8 +1560,12 @@ def main():
         del tb
         torch.cuda.empty_cache()
     if args.kv_pairs_default > 0:
-        result["pinned_path"].append(run_kv_step(torch, ibp, W, args, pr,
-                                                 pairs=args.kv_pairs_default))
+        result["kv_step"] = run_kv_step(torch, ibp, W, args, pr, pairs=args.kv_pairs_default)
+    if args.extras:
+        result["sampled_metadata"] = sampling
+        result["weight_stream"] = run_weight_stream(torch, ibp, args, pr)
+        result["saving_sweep"] = run_sweep(torch, ibp, args, pr)
+        result["transfer_ablation"] = run_ablation(torch, ibp, args, pr, pool_bytes=1 << 30)
     print(json.dumps(result), flush=True)
 
 
