@@ -725,3 +725,107 @@ def test_indexed_cache(key, B, C, n, law):
         want = G.expected_rows(rows, ids)
         want[~inside & (units > 0)] = 0
         assert (got == want).all(), f"{key} {law} A={A}: cut cache"
+
+
+@pytest.mark.parametrize("n_seg", [80, 130, 256])
+@pytest.mark.parametrize("B,C", [(256, 256), (1040, 256)])
+def test_many_segments(n_seg, B, C):
+    """ibp_compress_segments and ibp_gather_decompress_segments with 80, 130
+    (the compressor splits launches at 128 segments) and 256 segments (the
+    most one call takes), each segment with its own Mask and Bitval, empty
+    segments among them; tile kernel (256 B tensors) and group kernel
+    (1,040 B, five chunks); from slots (plain and XCD-routed) and from a
+    compacted cache; element by element against the oracle."""
+    from host_transfer_amd import ibp
+    from oracle import oracle as O
+    rng = np.random.default_rng(n_seg * 7 + B)
+    per = 6
+    n = n_seg * per
+    S = (B + 127) // 128 * 128
+    # segment k: floats with exponents shifted by k % 9, so the Masks differ
+    x = (rng.standard_normal((n, B // 4)) * 0.1).astype(np.float32)
+    x *= (2.0 ** (np.arange(n) // per % 9 - 4)).astype(np.float32)[:, None]
+    rows = x.view(np.uint8).reshape(n, B)
+    masks, bitvals = [], []
+    for k in range(n_seg):
+        m, v = O.build_metadata(rows[k * per:(k + 1) * per], 0.8)
+        masks.append(m), bitvals.append(v)
+    assert len({m.tobytes() for m in masks}) > 4
+    empty = set(range(3, n_seg, 17))
+    seg_row = [k * per for k in range(n_seg)]
+    seg_count = [0 if k in empty else per for k in range(n_seg)]
+    store = torch.full((n * S,), 0x5A, dtype=torch.int8, device="cuda")
+    part = torch.zeros((n * ibp.num_chunks(B, C) + 31) // 32, dtype=torch.int32, device="cuda")
+    lengths = torch.zeros(n, dtype=torch.int32, device="cuda")
+    G.log(f"[parity] {n_seg} compress segments, B={B} C={C}")
+    ibp.compress_segments(G.dev(rows), B, seg_row, seg_row, seg_count, n, B, C,
+                          G.dev(np.concatenate(masks)), G.dev(np.concatenate(bitvals)), store, S,
+                          part, lengths)
+    torch.cuda.synchronize()
+    full = [k for k in range(n_seg) if k not in empty]
+    o_parts = {}
+    for k in full:
+        o_store, o_part, o_len = G.check_store(rows[k * per:(k + 1) * per], masks[k], bitvals[k], C,
+                                               S, store, part, lengths, first=k * per, n_tensors=n)
+        o_parts[k] = (o_store, o_part)
+    # the empty segments' tensors were not written
+    g_len = G.host(lengths).view(np.uint32)
+    for k in empty:
+        assert not g_len[k * per:(k + 1) * per].any()
+    # gather: segment k takes ids of its own tensors (with repeats and an invalid id)
+    ids, seg_ids, m_all, v_all, want = [], [0], [], [], []
+    for k in range(n_seg):
+        cnt = 0 if k in empty else int(rng.integers(1, 40))
+        x = rng.integers(k * per, (k + 1) * per, cnt)
+        if cnt > 2:
+            x[1] = -1
+        ids.append(x)
+        seg_ids.append(seg_ids[-1] + cnt)
+        m_all.append(masks[k]), v_all.append(bitvals[k])
+        if cnt:
+            o_store, o_part = o_parts[k]
+            want.append(O.gather_decompress(o_store, o_part, n, x, B, C, masks[k], bitvals[k],
+                                            slot_bytes=S))
+    ids = np.concatenate(ids).astype(np.int64)
+    want = np.concatenate(want)
+    assert (want == G.expected_rows(rows, ids)).all()
+    d_ids, d_m, d_v = G.dev(ids), G.dev(np.concatenate(m_all)), G.dev(np.concatenate(v_all))
+    offsets = torch.zeros(n + 1, dtype=torch.int64, device="cuda")
+    ibp.compact_offsets(lengths, n, offsets)
+    total = int(offsets[-1].item())
+    cache = torch.zeros(max(total, 16), dtype=torch.uint8, device="cuda")
+    ibp.compact(store, S, n, offsets, cache, total)
+    for name, src, nbytes, slot, offs, flags in (
+            ("slots", store, n * S, S, None, 0), ("slots routed", store, n * S, S, None, G.ROUTE),
+            ("cache", cache, total, 0, offsets, 0)):
+        G.log(f"[parity] {n_seg} gather segments, B={B}: {name}")
+        out = torch.full((len(ids) * B,), -1, dtype=torch.int8, device="cuda")
+        ibp.gather_decompress_segments(src, nbytes, slot, offs, part, n, d_ids, seg_ids, B, C, d_m,
+                                       d_v, out, flags)
+        got = G.host(out).view(np.uint8).reshape(len(ids), B)
+        assert (got == want).all(), f"{n_seg} segments, B={B}: {name} differs from the oracle"
+
+
+@pytest.mark.parametrize("n", [64, 1000])
+def test_metadata_ties_at_half(n):
+    """T = 0.5 with an even sample count: bit positions where exactly half the
+    samples are 1 reach the cutoff (Mask 1) and take Bitval 0; positions one
+    sample away from the tie take the majority value."""
+    rng = np.random.default_rng(n)
+    B = 512
+    rows = np.zeros((n, B), np.uint8)
+    half = n // 2
+    bits = np.unpackbits(rows, axis=1, bitorder="little")
+    kind = rng.integers(0, 4, 8 * B)   # 0: exact tie, 1: tie + 1 one, 2: tie - 1, 3: random
+    for i in range(8 * B):
+        ones = {0: half, 1: half + 1, 2: half - 1, 3: int(rng.integers(0, n + 1))}[int(kind[i])]
+        col = np.zeros(n, np.uint8)
+        col[rng.choice(n, ones, replace=False)] = 1
+        bits[:, i] = col
+    rows = np.packbits(bits, axis=1, bitorder="little")
+    mask, bitval = G.check_metadata(rows, 0.5)
+    mb = np.unpackbits(mask.view(np.uint8), bitorder="little")
+    vb = np.unpackbits(bitval.view(np.uint8), bitorder="little")
+    assert mb.all(), "at T = 0.5 the majority (or a tie) always reaches the cutoff"
+    assert not vb[kind == 0].any(), "ties give Bitval 0"
+    assert vb[kind == 1].all() and not vb[kind == 2].any()
