@@ -44,8 +44,16 @@
  *              transfer compression); slot bytes [len_t, slot_bytes) are
  *              don't-care (the compressor writes zeros up to the next 16 B).
  *   cache      compacted layout: payload of t at cache + offsets[t],
- *              offsets[0] = 0, offsets[t+1] = offsets[t] + roundup(len_t, 16)
+ *              offsets[0] = 0, offsets[t+1] = offsets[t] + roundup(len_t, A)
+ *              with entry alignment A = 16 (ibp_compact_offsets) or a power
+ *              of two up to 4096 (ibp_compact_offsets_aligned; A = 128 puts
+ *              each entry on the fewest 128 B lines its length allows)
  *              ([G-EN] System Integration, cache compression).
+ *   index      for a cache of one-chunk tensors: one uint64 per 32 tensors,
+ *              index[w] = (participating tensors in bitmap words < w) << 32
+ *              | bitmap word w.  Every entry then has one of two sizes, so
+ *              its offset follows from the index word alone
+ *              (ibp_gather_decompress_indexed).
  *
  * -------------------------------------------------------------- CONVENTIONS
  *   - Every function returns IBP_OK (0) or a negative ibp_status.  Arguments

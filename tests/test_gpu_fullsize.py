@@ -5,7 +5,8 @@ At these sizes the oracle cannot redo everything, so each test checks:
   - Mask/Bitval of the GPU against the oracle's on the same sample (exact);
   - compressed bytes, participation bits and lengths of a random sample of
     tensors against the oracle compressing those tensors (exact);
-  - the cache offsets against the 16 B-rounded running sum of the lengths;
+  - the cache offsets against the 16 B-rounded running sum of the lengths, and
+    the 128 B-aligned offsets and the rank index against the oracle's;
   - every gathered row against the original row (the method is lossless),
     and a sample of gathered rows against the oracle's gather.
 """
@@ -138,6 +139,61 @@ def test_fullsize_hbm_cache(key):
     check_gather(t, W.batch_ids(w, 0), cache, total, offsets, rng, "workload batch")
     big = np.concatenate([W.batch_ids(w, k) for k in range((1 << 20) // w.batch)])
     check_gather(t, big, cache, total, offsets, rng, "1M ids")
+    t["raw"].free()
+
+
+def check_indexed_gather(t, ids, cache, total, align, index, rng, label):
+    """ibp_gather_decompress_indexed: every row lossless; SAMPLE rows equal to
+    the oracle's gather."""
+    w = t["w"]
+    N, B, C, S = w.n_tensors, w.tensor_bytes, w.chunk_bytes, w.slot_bytes
+    nb = len(ids)
+    out = torch.empty(nb * B, dtype=torch.uint8, device="cuda")
+    G.log(f"[fullsize] {w.key}: indexed gather {nb} ids ({label}, entries of {align} B)")
+    ibp.gather_decompress_indexed(cache, total, align, index, N, G.dev(ids), nb, B, C,
+                                  t["d_mask"], t["d_bitval"], out)
+    got = G.host(out).reshape(nb, B)
+    assert (got == t["view"][ids]).all(), f"{label}: gathered rows are not the original rows"
+    pick = rng.choice(nb, min(SAMPLE, nb), replace=False)
+    uniq, inv = np.unique(ids[pick], return_inverse=True)
+    rows = np.ascontiguousarray(t["view"][uniq])
+    o_store, o_part, _ = O.compress(rows, t["mask"], t["bitval"], C, slot_bytes=S)
+    want = O.gather_decompress(o_store, o_part, len(uniq), inv, B, C, t["mask"], t["bitval"],
+                               slot_bytes=S)
+    assert (got[pick] == want).all(), f"{label}: gather differs from the oracle"
+
+
+@pytest.mark.parametrize("key", ["dense_gnn", "dlrm_1k"])
+def test_fullsize_indexed_cache(key):
+    """The HBM cache as the benchmark lays it out and times it: entries rounded
+    to 128 B lines (ibp_compact_offsets_aligned, ibp_cache_fill) and found
+    through the rank index (ibp_cache_index), gathered with the workload's
+    batch, 1M Zipf ids and 1M distinct ids."""
+    rng = np.random.default_rng(303)
+    w = W.WORKLOADS[key]
+    N, S, A = w.n_tensors, w.slot_bytes, 128
+    t = build_table(w, "hbm")
+    check_sampled_store(t, rng)
+    offsets = torch.zeros(N + 1, dtype=torch.int64, device="cuda")
+    ibp.compact_offsets_aligned(t["lengths"], N, A, offsets)
+    g_off = G.host(offsets).view(np.uint64)
+    g_len = G.host(t["lengths"]).view(np.uint32)
+    o_off, _ = O.compact_aligned(None, S, g_len, A, with_cache=False)
+    assert (g_off == o_off).all(), "aligned offsets differ from the oracle's"
+    total = int(g_off[-1])
+    cache = torch.empty(total, dtype=torch.uint8, device="cuda")
+    ibp.cache_fill(t["store"], S, t["lengths"], N, offsets, cache, total)
+    index = torch.zeros((N + 31) // 32, dtype=torch.int64, device="cuda")
+    ibp.cache_index(t["part"], N, index)
+    o_idx = O.cache_index(G.host(t["part"]).view(np.uint32), N)
+    assert (G.host(index).view(np.uint64) == o_idx).all(), "rank index differs from the oracle's"
+    del t["store"], offsets
+    torch.cuda.empty_cache()
+    check_indexed_gather(t, W.batch_ids(w, 0), cache, total, A, index, rng, "workload batch")
+    big = np.concatenate([W.batch_ids(w, k) for k in range((1 << 20) // w.batch)])
+    check_indexed_gather(t, big, cache, total, A, index, rng, "1M Zipf ids")
+    distinct = rng.permutation(N)[:1 << 20].astype(np.int64)
+    check_indexed_gather(t, distinct, cache, total, A, index, rng, "1M distinct ids")
     t["raw"].free()
 
 
