@@ -64,9 +64,9 @@ HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E
 # still hash to GATHER_SOURCES_SHA256, else traffic is null.
 GATHER_SOURCES = ("host_transfer_amd/csrc/gather.hip", "host_transfer_amd/csrc/ibp_plan.h",
                   "host_transfer_amd/csrc/ibp_device.h")
-GATHER_SOURCES_SHA256 = "097c9a51496424eb6d8f62f48259248eb101f057aa5c4df73a099b1f54f285e7"
-HEADLINE_COUNTERS = {"link_read": 10632448, "hbm_read": 1695341, "hbm_write": 49653440,
-                     "fetch_size_kib": 6168.5, "write_size_kib": 48480.7}
+GATHER_SOURCES_SHA256 = "d66b445c81d7a1dc6755b07db88e47d90a5be0001a2d733d3b5ea3f51d7a8676"
+HEADLINE_COUNTERS = {"link_read": 10632453, "hbm_read": 1694318, "hbm_write": 49656767,
+                     "fetch_size_kib": 6191.5, "write_size_kib": 48484.5}
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 # HBM bytes (read, written) per 1M-id cache launch, from the same runs (the
 # summary in profiles/k_gather_cache__dense_gnn_dlrm_1k_hbm.md), for the code

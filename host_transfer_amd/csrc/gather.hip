@@ -291,6 +291,22 @@ __device__ __forceinline__ void gather_group_body(GatherArgs& a, uint32_t block,
   load_plan_counts(run, a.sh, s_pref, s_kc, s_wsum);
 
   if (row0 >= a.n_ids) return;  // uniform per group; no workgroup barrier follows for it
+
+  // The first tensor's payload is at least ceil(K / 8) bytes (K = kept bits
+  // of the Mask: every chunk packed), so in slot mode its first ceil(K / 128)
+  // units are requested as soon as its id is known, before its participation
+  // word and chunk scan; the rest follows the scan.
+  uint32_t spec = 0;
+  uint4 s0, s1;
+  {
+    const uint64_t so = m0.t * a.slot_bytes;
+    const uint64_t avail = so < a.store_bytes ? (a.store_bytes - so) >> 4 : 0ull;
+    if (a.offsets == nullptr && a.store != nullptr && m0.valid)
+      spec = (uint32_t)min((uint64_t)((s_pref[W] + 127u) >> 7), avail);
+    const uint4* src = (const uint4*)((const uint8_t*)a.store + so);
+    s0 = load_global(gl < spec ? src + gl : &g_zero16);
+    s1 = load_global(gl + G < spec ? src + gl + G : &g_zero16);
+  }
   if (first_wave) scan_row(a, m0, gl, s_kc, &hdrs[0], obufs);
   group_sync(single);
 
@@ -301,11 +317,13 @@ __device__ __forceinline__ void gather_group_body(GatherArgs& a, uint32_t block,
     const GroupHdr h = hdrs[0];
     const uint32_t n16 = payload_units(a, h);
     const uint4* src = (const uint4*)h.addr;
-    v0 = load_global(gl < n16 ? src + gl : &g_zero16);
-    v1 = load_global(gl + G < n16 ? src + gl + G : &g_zero16);
+    v0 = load_global(gl < n16 && gl >= spec ? src + gl : &g_zero16);
+    v1 = load_global(gl + G < n16 && gl + G >= spec ? src + gl + G : &g_zero16);
   }
 
   load_plan_words<J>(a.sh, s_pref, gl, R);
+  if (gl < spec) v0 = s0;
+  if (gl + G < spec) v1 = s1;
 
   uint32_t cur = 0;
   for (uint64_t row = row0; row < a.n_ids; row += step, cur ^= 1u) {
