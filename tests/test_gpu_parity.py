@@ -125,6 +125,34 @@ def test_geometry_sweep(B, C):
                                                                 np.array([n - 1])])
 
 
+@pytest.mark.parametrize("B,C,pinned", [(1028, 256, False), (2052, 1024, False),
+                                         (5732, 1024, True), (16384, 4096, True)])
+def test_group_first_payload_prefix(B, C, pinned):
+    """Group kernel, slot mode: each group requests its first tensor's
+    guaranteed payload prefix (ceil(K / 128) units, K = kept bits) before the
+    chunk scan and the rest after it.  Batches shorter than the number of
+    groups make every row a group's first row.  Tensors with every chunk
+    packed, one chunk whole, every chunk whole, and invalid ids; K is not a
+    multiple of 128 except for B = 16384."""
+    rng = np.random.default_rng(B + C)
+    n, W = 240, B // 4
+    # bits 23..31 equal in every word (a fixed top byte, bit 23 clear): K = 23 W
+    x = rng.integers(0, 1 << 23, (n, W), dtype=np.uint32) | np.uint32(0x3F000000)
+    wpc = C // 4
+    x[1:5, min(wpc, W - 1)] ^= np.uint32(1 << 30)   # one chunk whole
+    for c in range(0, W, wpc):                      # every chunk whole
+        x[5:9, c] ^= np.uint32(1 << 30)
+    rows = x.view(np.uint8)
+    first = np.array([-1, 5, 1, 0, n, 6, 2, 10, 3, 7, 11, 4, 8, 12, 1 << 40, 239])
+    mixed = rng.integers(-3, n + 3, 3000)
+    mask, _, lens = full_roundtrip(f"first payload B={B} C={C}", rows, C, 0.9, pinned=pinned,
+                                   batches=[mixed, first, np.array([5, 6, 7, 8])])
+    K = 32 * W - int(np.unpackbits(mask.view(np.uint8)).sum())
+    assert K == 23 * W, "the Mask should keep bits 0..22 of every word"
+    n_c = -(-B // C)
+    assert lens[0] == -(-K // 8) and lens[5] == B and (lens[1] > lens[0]) and (lens[1] < B or n_c == 1)
+
+
 @pytest.mark.parametrize("case", range(12))
 def test_random_shapes(case):
     """Seeded random shapes across the kernel choices: tensor size (tile,
