@@ -73,7 +73,7 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 # of gather_cache.hip they were measured on (CACHE_SOURCES_SHA256).
 CACHE_SOURCES = ("host_transfer_amd/csrc/gather_cache.hip", "host_transfer_amd/csrc/ibp_plan.h",
                  "host_transfer_amd/csrc/ibp_device.h")
-CACHE_SOURCES_SHA256 = "8b0747f508c8b869821d2c6e13105203611541ec050690e868556990da092725"
+CACHE_SOURCES_SHA256 = "59032c9ceb436f04b68b6d261a8affcc39e819dccd6e87102417bd69fb160d6c"
 HBM_COUNTERS = {
     ("dense_gnn", "zipf"): {"index_128B": (184.05e6, 536.87e6), "index_16B": (222.36e6, 536.87e6),
                             "table_16B": (261.42e6, 536.87e6), "raw": (178.79e6, 536.87e6)},

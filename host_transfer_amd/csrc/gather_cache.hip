@@ -478,6 +478,8 @@ hipError_t launch_gather_cache_index(const Geometry& g, const uint8_t* cache, ui
                                      const uint32_t* mask, const uint32_t* bitval, uint32_t* out,
                                      hipStream_t s) {
   if (n_ids == 0) return hipSuccess;
+  // no tensors (and an empty index): every id is out of range, every row zero
+  if (n_tensors == 0) return launch_fill_u32(out, n_ids * (uint64_t)g.W, 0u, s);
   CacheArgs a = cache_args(g, cache, cache_bytes, ids, n_ids, n_tensors, mask, bitval, out);
   a.index = index;
   a.align = entry_align;

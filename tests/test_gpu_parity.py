@@ -753,6 +753,12 @@ def test_indexed_cache(key, B, C, n, law):
         want = G.expected_rows(rows, ids)
         want[~inside & (units > 0)] = 0
         assert (got == want).all(), f"{key} {law} A={A}: cut cache"
+    # no tensors at all (an empty index): every row is zero, nothing is read
+    ids = np.array([0, 1, -1, 5])
+    out = torch.full((len(ids) * B,), -1, dtype=torch.int8, device="cuda")
+    ibp.gather_decompress_indexed(cache, total, 128, index, 0, G.dev(ids), len(ids), B, C,
+                                  G.dev(mask), G.dev(bitval), out)
+    assert not G.host(out).any(), "rows of a gather over no tensors must be zero"
 
 
 @pytest.mark.parametrize("n_seg", [80, 130, 256])
