@@ -248,6 +248,31 @@ __device__ __forceinline__ void decode_store(uint8_t* lds, uint32_t slot, uint32
   __builtin_nontemporal_store(row, (u32x4*)orow);
 }
 
+// This lane's per-word decode constants (words u + L q) once the kept-bit
+// prefix is in LDS.  Returns whether the kept bits of every word form at most
+// two runs (the same answer in every lane of the wave).
+template <int J>
+__device__ __forceinline__ bool word_constants(WordDec (&dw)[4], const uint32_t* s_pref,
+                                               uint32_t slot, uint32_t u) {
+  constexpr uint32_t L = CacheGeo<J>::L;
+  bool runs_ok = true;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    WordDec& d = dw[q];
+    const uint32_t pre = s_pref[u + L * q];
+    d.bv &= d.mk;
+    d.ap = slot + 4u * (pre >> 5);
+    d.sp = pre & 31u;
+    runs_ok = two_runs(~d.mk, d.c) && runs_ok;
+  }
+  const bool runs = __ballot(!runs_ok) == 0ull;
+  if (!runs) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) move_masks(~dw[q].mk, dw[q].c);
+  }
+  return runs;
+}
+
 // One block of `br` rows (rows row0 .. row0 + br - 1, the last block possibly
 // short): SPB = br / TPS steps, payloads D steps ahead, the next block's
 // entries resolved half-way.
@@ -349,21 +374,7 @@ __global__ __launch_bounds__(256) void k_gather_cache(CacheArgs a, uint32_t br) 
   }
 
   // per-word constants (while those payloads are in flight)
-  bool runs_ok = true;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    WordDec& d = dw[q];
-    const uint32_t pre = s_pref[u + L * q];
-    d.bv &= d.mk;
-    d.ap = slot + 4u * (pre >> 5);
-    d.sp = pre & 31u;
-    runs_ok = two_runs(~d.mk, d.c) && runs_ok;
-  }
-  const bool runs = __ballot(!runs_ok) == 0ull;
-  if (!runs) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) move_masks(~dw[q].mk, dw[q].c);
-  }
+  const bool runs = word_constants<J>(dw, s_pref, slot, u);
 
   RowMeta m_n = m_c;
   for (uint64_t b = b0; b < n_blocks; b += waves) {
@@ -391,6 +402,79 @@ __global__ __launch_bounds__(256) void k_gather_cache(CacheArgs a, uint32_t br) 
   }
 }
 
+// Short batches (every wave's rows fit one round of resident waves): wave w
+// takes S steps' rows, w * S * TPS onwards, resolves their entries and
+// requests all S payloads at once, then decodes them step by step.  No
+// pipeline across blocks, so a launch's critical path is one chain:
+// id -> entry -> payload -> decode -> store.
+template <int J, bool INDEXED, uint32_t S>
+__global__ __launch_bounds__(256) void k_gather_cache_short(CacheArgs a) {
+  using G = CacheGeo<J>;
+  constexpr uint32_t L = G::L, TPS = G::TPS, kW = G::kW;
+  constexpr uint32_t R = S * TPS;  // rows per wave
+  static_assert(R <= (uint32_t)kWave, "one row per lane at most");
+  __shared__ __align__(16) CacheLds<J> s_lds;
+  uint8_t* lds = s_lds.b;
+  uint32_t* s_pref = (uint32_t*)(s_lds.b + G::pref);
+  uint32_t* s_kc = (uint32_t*)(s_lds.b + G::kc);
+  uint32_t* s_wsum = (uint32_t*)(s_lds.b + G::wsum);
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  const uint32_t lane = threadIdx.x % kWave;
+  const uint32_t g = lane / L, u = lane % L;
+  const uint32_t slot = G::slots + (wave * TPS + g) * G::kSlot;
+  const uint64_t row0 = ((uint64_t)blockIdx.x * kCacheWaves + wave) * R;
+
+  // this wave's ids and their entries, the Mask/Bitval words, then the
+  // kept-bit prefix (a workgroup scan)
+  const int64_t id = row_id(a, row0 + (lane < R ? lane : R - 1u));
+  PlanRun run;
+  load_plan_run(a.mask, a.sh, run);
+  WordDec dw[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    dw[q].mk = ld_u32(a.mask + u + L * q);
+    dw[q].bv = ld_u32(a.bitval + u + L * q);
+  }
+  const RowRaw rr = row_raw<INDEXED>(a, id);
+  load_plan_counts(run, a.sh, s_pref, s_kc, s_wsum);
+  if (row0 >= a.n_ids) return;  // per wave; no workgroup barrier follows
+
+  const uint32_t K = s_pref[kW];
+  const uint32_t n16p = (K + 127u) >> 7;
+  const uint64_t amask = (uint64_t)a.align - 1u;
+  const uint64_t s_p = (((uint64_t)K + 7u) / 8u + amask) & ~amask;
+  const uint64_t s_r = ((uint64_t)(4u * kW) + amask) & ~amask;
+  const RowMeta m = row_resolve<INDEXED>(a, rr, n16p, L, s_p, s_r);
+
+  uint4 v[S];
+  uint32_t pk[S];
+#pragma unroll
+  for (uint32_t d = 0; d < S; ++d) {
+    const uint32_t i = d * TPS + g;
+    const uint32_t lo = (uint32_t)__shfl((int)m.lo, (int)i, kWave);
+    const uint32_t hi = (uint32_t)__shfl((int)m.hi, (int)i, kWave);
+    const uint32_t un = min(u, (hi >> 16) & 63u);
+    v[d] = load_global((const uint4*)((((uint64_t)(hi & 0xFFFFu) << 32) | lo) + 16ull * un));
+    pk[d] = hi >> 24;
+  }
+  const bool runs = word_constants<J>(dw, s_pref, slot, u);
+
+  uint32_t* orow = a.out + (row0 + g) * kW + 4u * u;
+#pragma unroll
+  for (uint32_t d = 0; d < S; ++d) {
+    *(uint4*)(lds + slot + 16u * u) = v[d];
+    wave_sync();
+    if (row0 + d * TPS + g < a.n_ids) {
+      if (runs)
+        decode_store<J, true>(lds, slot, u, dw, pk[d] != 0u, orow);
+      else
+        decode_store<J, false>(lds, slot, u, dw, pk[d] != 0u, orow);
+    }
+    orow += TPS * kW;
+    wave_sync();
+  }
+}
+
 // Rows per block: 64 while the batch still gives every SIMD a few waves of
 // such blocks, fewer on short batches (down to 2 D steps' worth), so that
 // short launches spread over the whole GPU.
@@ -403,11 +487,35 @@ uint32_t cache_rows_per_block(uint64_t n_ids, int cus) {
   return br < min_br ? min_br : br;
 }
 
+// The short kernel with S steps per wave, if its waves for this batch fit one
+// round of resident waves (*done set); hipSuccess with *done clear otherwise.
+template <int J, bool INDEXED, uint32_t S>
+hipError_t try_cache_short(const CacheArgs& a, int cus, bool* done, hipStream_t s) {
+  constexpr uint32_t R = S * CacheGeo<J>::TPS;
+  int per_cu = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      &per_cu, k_gather_cache_short<J, INDEXED, S>, kCacheWaves * kWave, 0);
+  if (e != hipSuccess) return e;
+  const uint64_t waves = (a.n_ids + R - 1) / R;
+  const uint64_t resident = (uint64_t)per_cu * (uint64_t)cus * kCacheWaves;
+  *done = waves <= resident;
+  if (!*done) return hipSuccess;
+  const uint64_t blocks = (waves + kCacheWaves - 1) / kCacheWaves;
+  hipLaunchKernelGGL((k_gather_cache_short<J, INDEXED, S>), dim3((uint32_t)blocks),
+                     dim3(kCacheWaves * kWave), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int J, bool INDEXED>
 hipError_t launch_cache_j(const CacheArgs& a, hipStream_t s) {
   DeviceInfo di;
   hipError_t e = device_info(&di);
   if (e != hipSuccess) return e;
+  // short batches: the fewest steps per wave whose waves fit one round
+  bool done = false;
+  if ((e = try_cache_short<J, INDEXED, 1>(a, di.cus, &done, s)) != hipSuccess || done) return e;
+  if ((e = try_cache_short<J, INDEXED, 2>(a, di.cus, &done, s)) != hipSuccess || done) return e;
+  if ((e = try_cache_short<J, INDEXED, 4>(a, di.cus, &done, s)) != hipSuccess || done) return e;
   int per_cu = 0;
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gather_cache<J, INDEXED>,
                                                    kCacheWaves * kWave, 0);
