@@ -19,15 +19,17 @@
 //          tensor; with A = 128 every entry starts on a 128 B line and
 //          occupies the fewest lines its length allows.
 //
-// Launch shape: a wave takes blocks of br consecutive rows (grid stride; br =
-// 32, fewer on short batches so that they still spread over every CU).
-// Lane r of the wave resolves row r's entry (address, 16 B units to read,
-// packed or not) once per block.  A step moves TPS = 64 / L tensors, each
-// with L = 16 J lanes loading one 16 B unit each (a plain row copy's shape);
-// the payloads of the next D steps are in flight in registers while the
-// current one is decoded from LDS.  Lane u of a tensor decodes words
-// u + L q, q < 4, so consecutive lanes read consecutive LDS words and store
-// consecutive output words.
+// Launch shape: a wave takes S steps' rows, S * TPS consecutive rows.  A step
+// moves TPS = 64 / L tensors, each with L = 16 J lanes loading one 16 B unit
+// each (a plain row copy's shape).  Lane r of the wave resolves row r's entry
+// (address, 16 B units to read, packed or not), then the wave requests all S
+// payloads at once and decodes them step by step from LDS.  Lane u of a
+// tensor decodes words u + L q, q < 4, so consecutive lanes read consecutive
+// LDS words and store consecutive output words.  A batch whose waves fit one
+// round of resident waves takes the fewest steps per wave that fit (S = 1, 2
+// or 4; eight waves per SIMD for S <= 2); a longer batch takes S = 4 with a
+// grid-stride loop over blocks, the next block's ids requested while the
+// current payloads are in flight.
 //
 // Decode of one word w of a packed tensor: a 64-bit window of the payload at
 // the word's kept-bit offset pre_w (two LDS words, v_alignbit), then the kept
@@ -39,13 +41,6 @@
 // word.  Every select is a per-lane select, with no divergent branch.
 #include "ibp_internal.h"
 #include "ibp_plan.h"
-
-#ifndef IBP_CACHE_BR_MAX
-#define IBP_CACHE_BR_MAX 32  // rows per block at most
-#endif
-#ifndef IBP_CACHE_DEPTH
-#define IBP_CACHE_DEPTH 4  // steps of payload in flight per wave
-#endif
 
 namespace ibp {
 
@@ -195,13 +190,6 @@ struct CacheGeo {
   static constexpr uint32_t TPS = (uint32_t)kWave / L;   // tensors per step
   static constexpr uint32_t kW = 4u * L;                 // words per tensor
   static constexpr uint32_t kSlot = 16u * L + 16u;       // LDS bytes per tensor + the word a window reads past
-  static constexpr uint32_t D = IBP_CACHE_DEPTH;
-  // blocks hold a power-of-two number of steps >= 2 D (cache_rows_per_block),
-  // so D steps divide every block
-  static_assert(D >= 1 && (D & (D - 1)) == 0, "pipeline depth: a power of two");
-  static_assert(2u * D * TPS <= (uint32_t)kWave, "a block of at most 64 rows holds 2 D steps");
-  static_assert(IBP_CACHE_BR_MAX <= 64 && (IBP_CACHE_BR_MAX & (IBP_CACHE_BR_MAX - 1)) == 0,
-                "rows per block: a power of two, at most one per lane");
   // LDS: kept-bit prefix (W + 1 words, padded), chunk sums, scan scratch, slots
   static constexpr uint32_t pref = 0;
   static constexpr uint32_t kc = ((4u * (kW + 1u)) + 15u) & ~15u;
@@ -273,142 +261,14 @@ __device__ __forceinline__ bool word_constants(WordDec (&dw)[4], const uint32_t*
   return runs;
 }
 
-// One block of `br` rows (rows row0 .. row0 + br - 1, the last block possibly
-// short): SPB = br / TPS steps, payloads D steps ahead, the next block's
-// entries resolved half-way.
-template <int J, bool INDEXED, bool RUNS, bool FULL>
-__device__ __forceinline__ void cache_block(const CacheArgs& a, uint8_t* lds,
-                                            uint32_t slot, uint32_t g,
-                                            uint32_t u, uint32_t spb, uint64_t row0,
-                                            const WordDec (&dw)[4], uint4 (&v)[CacheGeo<J>::D],
-                                            uint32_t (&pk)[CacheGeo<J>::D], const RowMeta& m_c,
-                                            RowMeta& m_n, const RowRaw& r_n, uint32_t n16p,
-                                            uint64_t s_p, uint64_t s_r) {
-  using G = CacheGeo<J>;
-  constexpr uint32_t L = G::L, TPS = G::TPS, kW = G::kW, D = G::D;
-  uint32_t* orow = a.out + (row0 + g) * kW + 4u * u;
-  const uint32_t left = (uint32_t)min((uint64_t)spb * TPS, a.n_ids - row0);
-  for (uint32_t k0 = 0; k0 < spb; k0 += D) {
-#pragma unroll
-    for (uint32_t d = 0; d < D; ++d) {
-      const uint32_t k = k0 + d;
-      // a. this step's payload -> LDS
-      *(uint4*)(lds + slot + 16u * u) = v[d];
-      const bool packed = pk[d] != 0u;
-      wave_sync();
-      // b. the next block's entries, loaded half a block ago
-      if (k == spb / 2) m_n = row_resolve<INDEXED>(a, r_n, n16p, L, s_p, s_r);
-      // c. the payload D steps ahead (in the next block near the end)
-      {
-        const bool wrap = k + D >= spb;
-        const uint32_t i = (wrap ? k + D - spb : k + D) * TPS + g;
-        const uint32_t lo = (uint32_t)__shfl((int)(wrap ? m_n.lo : m_c.lo), (int)i, kWave);
-        const uint32_t hi = (uint32_t)__shfl((int)(wrap ? m_n.hi : m_c.hi), (int)i, kWave);
-        const uint32_t un = min(u, (hi >> 16) & 63u);
-        v[d] = load_global((const uint4*)((((uint64_t)(hi & 0xFFFFu) << 32) | lo) + 16ull * un));
-        pk[d] = hi >> 24;
-      }
-      // d. decode and store row k * TPS + g
-      if (FULL || k * TPS + g < left) decode_store<J, RUNS>(lds, slot, u, dw, packed, orow);
-      orow += TPS * kW;
-      wave_sync();
-    }
-  }
-}
-
-template <int J, bool INDEXED>
-__global__ __launch_bounds__(256) void k_gather_cache(CacheArgs a, uint32_t br) {
-  using G = CacheGeo<J>;
-  constexpr uint32_t L = G::L, TPS = G::TPS, kW = G::kW, D = G::D;
-  __shared__ __align__(16) CacheLds<J> s_lds;
-  uint8_t* lds = s_lds.b;
-  uint32_t* s_pref = (uint32_t*)(s_lds.b + G::pref);
-  uint32_t* s_kc = (uint32_t*)(s_lds.b + G::kc);
-  uint32_t* s_wsum = (uint32_t*)(s_lds.b + G::wsum);
-  const uint32_t wave = uniform(threadIdx.x / kWave);
-  const uint32_t lane = threadIdx.x % kWave;
-  const uint32_t g = lane / L, u = lane % L;
-  const uint32_t slot = G::slots + (wave * TPS + g) * G::kSlot;
-  const uint32_t spb = br / TPS;  // steps per block
-
-  const uint64_t n_blocks = (a.n_ids + br - 1u) / br;
-  const uint64_t waves = (uint64_t)gridDim.x * kCacheWaves;
-  const uint64_t b0 = (uint64_t)blockIdx.x * kCacheWaves + wave;
-
-  // ids of the first two blocks, this lane's Mask/Bitval words, the first
-  // block's entries, then the kept-bit prefix (a workgroup scan)
-  const uint32_t r = lane < br ? lane : br - 1u;
-  const int64_t id0 = row_id(a, b0 * br + r);
-  int64_t id_n = row_id(a, (b0 + waves) * br + r);
-  PlanRun run;
-  load_plan_run(a.mask, a.sh, run);
-  WordDec dw[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    dw[q].mk = ld_u32(a.mask + u + L * q);
-    dw[q].bv = ld_u32(a.bitval + u + L * q);
-  }
-  const RowRaw r0 = row_raw<INDEXED>(a, id0);
-  load_plan_counts(run, a.sh, s_pref, s_kc, s_wsum);
-  if (b0 >= n_blocks) return;  // per wave; no workgroup barrier follows
-
-  // packed payload: K bits -> ceil(K / 128) units; entry sizes (index mode)
-  const uint32_t K = s_pref[kW];
-  const uint32_t n16p = (K + 127u) >> 7;
-  const uint64_t amask = (uint64_t)a.align - 1u;
-  const uint64_t s_p = (((uint64_t)K + 7u) / 8u + amask) & ~amask;
-  const uint64_t s_r = ((uint64_t)(4u * kW) + amask) & ~amask;
-  RowMeta m_c = row_resolve<INDEXED>(a, r0, n16p, L, s_p, s_r);
-
-  // payloads of the first D steps (a block of br rows has br / TPS >= D steps)
-  uint4 v[D];
-  uint32_t pk[D];
-#pragma unroll
-  for (uint32_t d = 0; d < D; ++d) {
-    const uint32_t i = d * TPS + g;
-    const uint32_t lo = (uint32_t)__shfl((int)m_c.lo, (int)i, kWave);
-    const uint32_t hi = (uint32_t)__shfl((int)m_c.hi, (int)i, kWave);
-    const uint32_t un = min(u, (hi >> 16) & 63u);
-    v[d] = load_global((const uint4*)((((uint64_t)(hi & 0xFFFFu) << 32) | lo) + 16ull * un));
-    pk[d] = hi >> 24;
-  }
-
-  // per-word constants (while those payloads are in flight)
-  const bool runs = word_constants<J>(dw, s_pref, slot, u);
-
-  RowMeta m_n = m_c;
-  for (uint64_t b = b0; b < n_blocks; b += waves) {
-    // next block's entries; ids two blocks ahead
-    const RowRaw r_n = row_raw<INDEXED>(a, id_n);
-    id_n = row_id(a, (b + 2u * waves) * br + r);
-    const uint64_t row0 = b * br;
-    const bool full = row0 + br <= a.n_ids;
-    if (runs) {
-      if (full)
-        cache_block<J, INDEXED, true, true>(a, lds, slot, g, u, spb, row0, dw, v, pk,
-                                            m_c, m_n, r_n, n16p, s_p, s_r);
-      else
-        cache_block<J, INDEXED, true, false>(a, lds, slot, g, u, spb, row0, dw, v, pk,
-                                             m_c, m_n, r_n, n16p, s_p, s_r);
-    } else {
-      if (full)
-        cache_block<J, INDEXED, false, true>(a, lds, slot, g, u, spb, row0, dw, v, pk,
-                                             m_c, m_n, r_n, n16p, s_p, s_r);
-      else
-        cache_block<J, INDEXED, false, false>(a, lds, slot, g, u, spb, row0, dw, v, pk,
-                                              m_c, m_n, r_n, n16p, s_p, s_r);
-    }
-    m_c = m_n;
-  }
-}
-
-// Short batches (every wave's rows fit one round of resident waves): wave w
-// takes S steps' rows, w * S * TPS onwards, resolves their entries and
-// requests all S payloads at once, then decodes them step by step.  No
-// pipeline across blocks, so a launch's critical path is one chain:
-// id -> entry -> payload -> decode -> store.
-template <int J, bool INDEXED, uint32_t S>
-__global__ __launch_bounds__(256) void k_gather_cache_short(CacheArgs a) {
+// Wave w takes S steps' rows, w * S * TPS onwards, resolves their entries,
+// requests all S payloads at once, then decodes them step by step.  Without
+// LOOP the grid covers the batch once, so a launch's critical path is one
+// chain: id -> entry -> payload -> decode -> store.  With LOOP the waves walk
+// the batch with a grid stride, each block's ids requested while the previous
+// block's payloads are in flight.
+template <int J, bool INDEXED, uint32_t S, bool LOOP>
+__global__ __launch_bounds__(256) void k_gather_cache(CacheArgs a) {
   using G = CacheGeo<J>;
   constexpr uint32_t L = G::L, TPS = G::TPS, kW = G::kW;
   constexpr uint32_t R = S * TPS;  // rows per wave
@@ -422,11 +282,12 @@ __global__ __launch_bounds__(256) void k_gather_cache_short(CacheArgs a) {
   const uint32_t lane = threadIdx.x % kWave;
   const uint32_t g = lane / L, u = lane % L;
   const uint32_t slot = G::slots + (wave * TPS + g) * G::kSlot;
-  const uint64_t row0 = ((uint64_t)blockIdx.x * kCacheWaves + wave) * R;
+  uint64_t row0 = ((uint64_t)blockIdx.x * kCacheWaves + wave) * R;
+  const uint64_t stride = (uint64_t)gridDim.x * kCacheWaves * R;
 
   // this wave's ids and their entries, the Mask/Bitval words, then the
   // kept-bit prefix (a workgroup scan)
-  const int64_t id = row_id(a, row0 + (lane < R ? lane : R - 1u));
+  int64_t id = row_id(a, row0 + (lane < R ? lane : R - 1u));
   PlanRun run;
   load_plan_run(a.mask, a.sh, run);
   WordDec dw[4];
@@ -435,7 +296,7 @@ __global__ __launch_bounds__(256) void k_gather_cache_short(CacheArgs a) {
     dw[q].mk = ld_u32(a.mask + u + L * q);
     dw[q].bv = ld_u32(a.bitval + u + L * q);
   }
-  const RowRaw rr = row_raw<INDEXED>(a, id);
+  RowRaw rr = row_raw<INDEXED>(a, id);
   load_plan_counts(run, a.sh, s_pref, s_kc, s_wsum);
   if (row0 >= a.n_ids) return;  // per wave; no workgroup barrier follows
 
@@ -444,64 +305,71 @@ __global__ __launch_bounds__(256) void k_gather_cache_short(CacheArgs a) {
   const uint64_t amask = (uint64_t)a.align - 1u;
   const uint64_t s_p = (((uint64_t)K + 7u) / 8u + amask) & ~amask;
   const uint64_t s_r = ((uint64_t)(4u * kW) + amask) & ~amask;
-  const RowMeta m = row_resolve<INDEXED>(a, rr, n16p, L, s_p, s_r);
-
-  uint4 v[S];
-  uint32_t pk[S];
+  bool runs = true, planned = false;
+  for (;;) {
+    const RowMeta m = row_resolve<INDEXED>(a, rr, n16p, L, s_p, s_r);
+    uint4 v[S];
+    uint32_t pk[S];
 #pragma unroll
-  for (uint32_t d = 0; d < S; ++d) {
-    const uint32_t i = d * TPS + g;
-    const uint32_t lo = (uint32_t)__shfl((int)m.lo, (int)i, kWave);
-    const uint32_t hi = (uint32_t)__shfl((int)m.hi, (int)i, kWave);
-    const uint32_t un = min(u, (hi >> 16) & 63u);
-    v[d] = load_global((const uint4*)((((uint64_t)(hi & 0xFFFFu) << 32) | lo) + 16ull * un));
-    pk[d] = hi >> 24;
-  }
-  const bool runs = word_constants<J>(dw, s_pref, slot, u);
-
-  uint32_t* orow = a.out + (row0 + g) * kW + 4u * u;
-#pragma unroll
-  for (uint32_t d = 0; d < S; ++d) {
-    *(uint4*)(lds + slot + 16u * u) = v[d];
-    wave_sync();
-    if (row0 + d * TPS + g < a.n_ids) {
-      if (runs)
-        decode_store<J, true>(lds, slot, u, dw, pk[d] != 0u, orow);
-      else
-        decode_store<J, false>(lds, slot, u, dw, pk[d] != 0u, orow);
+    for (uint32_t d = 0; d < S; ++d) {
+      const uint32_t i = d * TPS + g;
+      const uint32_t lo = (uint32_t)__shfl((int)m.lo, (int)i, kWave);
+      const uint32_t hi = (uint32_t)__shfl((int)m.hi, (int)i, kWave);
+      const uint32_t un = min(u, (hi >> 16) & 63u);
+      v[d] = load_global((const uint4*)((((uint64_t)(hi & 0xFFFFu) << 32) | lo) + 16ull * un));
+      pk[d] = hi >> 24;
     }
-    orow += TPS * kW;
-    wave_sync();
+    // the next block's ids (clamped, unconditional) while these payloads fly
+    const uint64_t next = row0 + stride;
+    if (LOOP) id = row_id(a, next + (lane < R ? lane : R - 1u));
+    if (!planned) {
+      runs = word_constants<J>(dw, s_pref, slot, u);
+      planned = true;
+    }
+    uint32_t* orow = a.out + (row0 + g) * kW + 4u * u;
+#pragma unroll
+    for (uint32_t d = 0; d < S; ++d) {
+      *(uint4*)(lds + slot + 16u * u) = v[d];
+      wave_sync();
+      if (row0 + d * TPS + g < a.n_ids) {
+        if (runs)
+          decode_store<J, true>(lds, slot, u, dw, pk[d] != 0u, orow);
+        else
+          decode_store<J, false>(lds, slot, u, dw, pk[d] != 0u, orow);
+      }
+      orow += TPS * kW;
+      wave_sync();
+    }
+    if (!LOOP || next >= a.n_ids) break;
+    row0 = next;
+    rr = row_raw<INDEXED>(a, id);
   }
 }
 
-// Rows per block: 64 while the batch still gives every SIMD a few waves of
-// such blocks, fewer on short batches (down to 2 D steps' worth), so that
-// short launches spread over the whole GPU.
-template <int J>
-uint32_t cache_rows_per_block(uint64_t n_ids, int cus) {
-  using G = CacheGeo<J>;
-  uint32_t br = IBP_CACHE_BR_MAX;
-  const uint32_t min_br = 2u * G::D * G::TPS;
-  while (br > min_br && n_ids / br < (uint64_t)cus * 16u) br /= 2;
-  return br < min_br ? min_br : br;
+// Resident waves of one k_gather_cache instance on the current device.
+template <int J, bool INDEXED, uint32_t S, bool LOOP>
+hipError_t resident_waves(int cus, uint64_t* waves) {
+  int per_cu = 0;
+  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      &per_cu, k_gather_cache<J, INDEXED, S, LOOP>, kCacheWaves * kWave, 0);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1) return hipErrorInvalidConfiguration;
+  *waves = (uint64_t)per_cu * (uint64_t)cus * kCacheWaves;
+  return hipSuccess;
 }
 
-// The short kernel with S steps per wave, if its waves for this batch fit one
-// round of resident waves (*done set); hipSuccess with *done clear otherwise.
+// One round with S steps per wave if the batch's waves fit (*done set).
 template <int J, bool INDEXED, uint32_t S>
-hipError_t try_cache_short(const CacheArgs& a, int cus, bool* done, hipStream_t s) {
-  constexpr uint32_t R = S * CacheGeo<J>::TPS;
-  int per_cu = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &per_cu, k_gather_cache_short<J, INDEXED, S>, kCacheWaves * kWave, 0);
+hipError_t try_one_round(const CacheArgs& a, int cus, bool* done, hipStream_t s) {
+  constexpr uint64_t R = S * CacheGeo<J>::TPS;
+  uint64_t resident = 0;
+  hipError_t e = resident_waves<J, INDEXED, S, false>(cus, &resident);
   if (e != hipSuccess) return e;
   const uint64_t waves = (a.n_ids + R - 1) / R;
-  const uint64_t resident = (uint64_t)per_cu * (uint64_t)cus * kCacheWaves;
   *done = waves <= resident;
   if (!*done) return hipSuccess;
-  const uint64_t blocks = (waves + kCacheWaves - 1) / kCacheWaves;
-  hipLaunchKernelGGL((k_gather_cache_short<J, INDEXED, S>), dim3((uint32_t)blocks),
+  hipLaunchKernelGGL((k_gather_cache<J, INDEXED, S, false>),
+                     dim3((uint32_t)((waves + kCacheWaves - 1) / kCacheWaves)),
                      dim3(kCacheWaves * kWave), 0, s, a);
   return hipGetLastError();
 }
@@ -511,24 +379,16 @@ hipError_t launch_cache_j(const CacheArgs& a, hipStream_t s) {
   DeviceInfo di;
   hipError_t e = device_info(&di);
   if (e != hipSuccess) return e;
-  // short batches: the fewest steps per wave whose waves fit one round
+  // the fewest steps per wave whose waves fit one round
   bool done = false;
-  if ((e = try_cache_short<J, INDEXED, 1>(a, di.cus, &done, s)) != hipSuccess || done) return e;
-  if ((e = try_cache_short<J, INDEXED, 2>(a, di.cus, &done, s)) != hipSuccess || done) return e;
-  if ((e = try_cache_short<J, INDEXED, 4>(a, di.cus, &done, s)) != hipSuccess || done) return e;
-  int per_cu = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gather_cache<J, INDEXED>,
-                                                   kCacheWaves * kWave, 0);
-  if (e != hipSuccess) return e;
-  if (per_cu < 1) return hipErrorInvalidConfiguration;
-  const uint32_t br = cache_rows_per_block<J>(a.n_ids, di.cus);
-  const uint64_t n_blocks = (a.n_ids + br - 1) / br;
-  const uint64_t cap = (uint64_t)per_cu * (uint64_t)di.cus;
-  // as many workgroups as fit, but each wave gets the same number of blocks
-  const uint64_t per_wave = (n_blocks + cap * kCacheWaves - 1) / (cap * kCacheWaves);
-  const uint64_t want = (n_blocks + per_wave * kCacheWaves - 1) / (per_wave * kCacheWaves);
-  hipLaunchKernelGGL((k_gather_cache<J, INDEXED>), dim3((uint32_t)want), dim3(kCacheWaves * kWave),
-                     0, s, a, br);
+  if ((e = try_one_round<J, INDEXED, 1>(a, di.cus, &done, s)) != hipSuccess || done) return e;
+  if ((e = try_one_round<J, INDEXED, 2>(a, di.cus, &done, s)) != hipSuccess || done) return e;
+  if ((e = try_one_round<J, INDEXED, 4>(a, di.cus, &done, s)) != hipSuccess || done) return e;
+  // longer batches: four steps per wave, every resident wave, grid stride
+  uint64_t resident = 0;
+  if ((e = resident_waves<J, INDEXED, 4, true>(di.cus, &resident)) != hipSuccess) return e;
+  hipLaunchKernelGGL((k_gather_cache<J, INDEXED, 4, true>),
+                     dim3((uint32_t)(resident / kCacheWaves)), dim3(kCacheWaves * kWave), 0, s, a);
   return hipGetLastError();
 }
 
