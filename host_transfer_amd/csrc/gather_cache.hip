@@ -384,8 +384,9 @@ hipError_t launch_cache_j(const CacheArgs& a, hipStream_t s) {
   if ((e = try_one_round<J, INDEXED, 1>(a, di.cus, &done, s)) != hipSuccess || done) return e;
   if ((e = try_one_round<J, INDEXED, 2>(a, di.cus, &done, s)) != hipSuccess || done) return e;
   if ((e = try_one_round<J, INDEXED, 4>(a, di.cus, &done, s)) != hipSuccess || done) return e;
-  // longer batches: four steps per wave, every resident wave, grid stride (two
-  // or three steps kept too few payloads in flight, six or eight cost waves)
+  // longer batches: four steps per wave, every resident wave, grid stride (one
+  // or two steps per wave, and six or eight at fewer waves per SIMD, measured
+  // slower)
   constexpr uint32_t SL = 4;
   uint64_t resident = 0;
   if ((e = resident_waves<J, INDEXED, SL, true>(di.cus, &resident)) != hipSuccess) return e;
