@@ -73,18 +73,18 @@ FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 # of gather_cache.hip they were measured on (CACHE_SOURCES_SHA256).
 CACHE_SOURCES = ("host_transfer_amd/csrc/gather_cache.hip", "host_transfer_amd/csrc/ibp_plan.h",
                  "host_transfer_amd/csrc/ibp_device.h")
-CACHE_SOURCES_SHA256 = "59032c9ceb436f04b68b6d261a8affcc39e819dccd6e87102417bd69fb160d6c"
+CACHE_SOURCES_SHA256 = "ebe2dc8d87093948edff1033623b266d90e81e8626f06c23a5b9e8820395672e"
 HBM_COUNTERS = {
-    ("dense_gnn", "zipf"): {"index_128B": (184.05e6, 536.87e6), "index_16B": (222.36e6, 536.87e6),
-                            "table_16B": (261.42e6, 536.87e6), "raw": (178.79e6, 536.87e6)},
-    ("dense_gnn", "distinct"): {"index_128B": (579.23e6, 536.87e6),
-                                "index_16B": (684.54e6, 536.87e6),
-                                "table_16B": (793.85e6, 536.87e6), "raw": (553.66e6, 536.88e6)},
-    ("dlrm_1k", "zipf"): {"index_128B": (509.97e6, 1073.74e6), "index_16B": (510.41e6, 1073.74e6),
-                          "table_16B": (571.11e6, 1073.74e6), "raw": (542.20e6, 1073.74e6)},
-    ("dlrm_1k", "distinct"): {"index_128B": (1063.59e6, 1073.75e6),
-                              "index_16B": (1063.62e6, 1073.76e6),
-                              "table_16B": (1180.57e6, 1073.76e6), "raw": (1107.31e6, 1073.75e6)},
+    ("dense_gnn", "zipf"): {"index_128B": (184.30e6, 536.87e6), "index_16B": (222.75e6, 536.87e6),
+                            "table_16B": (262.52e6, 536.87e6), "raw": (179.09e6, 536.87e6)},
+    ("dense_gnn", "distinct"): {"index_128B": (577.20e6, 536.87e6),
+                                "index_16B": (685.03e6, 536.87e6),
+                                "table_16B": (794.37e6, 536.87e6), "raw": (553.66e6, 536.87e6)},
+    ("dlrm_1k", "zipf"): {"index_128B": (512.87e6, 1073.74e6), "index_16B": (513.04e6, 1073.74e6),
+                          "table_16B": (575.65e6, 1073.74e6), "raw": (542.21e6, 1073.74e6)},
+    ("dlrm_1k", "distinct"): {"index_128B": (1075.96e6, 1073.75e6),
+                              "index_16B": (1075.98e6, 1073.75e6),
+                              "table_16B": (1192.30e6, 1073.74e6), "raw": (1107.31e6, 1073.75e6)},
 }
 
 
@@ -668,6 +668,10 @@ def measure_pinned(torch, ibp, W, key, flags, args, pr):
     # the GPU's caches, not over the link, so this is the link-side count
     uniq = statistics.mean(float(table.len_host[np.unique(i)].sum())
                            for i in m["ids_host"][args.warmup:])
+    # the same tensors in the whole 128 B lines that cross the link (slots
+    # start on a line; a payload of len bytes is read as ceil(len / 128) lines)
+    uniq_lines = statistics.mean(lines_bytes(table.len_host[np.unique(i)])
+                                 for i in m["ids_host"][args.warmup:])
     link = max(pr["h2d_dma_GBps"], pr["h2d_zero_copy_read_GBps"])
     km, rm = m["kernel_ms"], m["raw_kernel_ms"]
     achieved = comp / (km * 1e-3) / 1e9
@@ -681,6 +685,7 @@ def measure_pinned(torch, ibp, W, key, flags, args, pr):
            "unique_payload_GBps_over_link": round(achieved_u, 2),
            "unique_frac_of_measured": round(achieved_u / link, 4),
            "unique_frac_of_zero_copy_read": round(achieved_u / pr["h2d_zero_copy_read_GBps"], 4),
+           "unique_line_frac_of_measured": round(uniq_lines / (km * 1e-3) / 1e9 / link, 4),
            "batch_payload_over_dense": round(comp / (w.batch * w.tensor_bytes), 5),
            "raw_gather_us": round(rm * 1e3, 2),
            "transfer_speedup_vs_raw_gpu_gather": round(rm / km, 3),
@@ -700,10 +705,12 @@ def measure_pinned(torch, ibp, W, key, flags, args, pr):
     ms16, _ = region_launches(torch, lambda k: table.gather(ibp, d16[k % len(d16)], nb16, out16,
                                                             flags16), 2, 6)
     u16 = statistics.mean(float(table.len_host[np.unique(i[:nb16])].sum()) for i in ids16)
+    l16 = statistics.mean(lines_bytes(table.len_host[np.unique(i[:nb16])]) for i in ids16)
     res["one_launch_16_batches"] = {
         "ids": nb16, "kernel_us": round(ms16 * 1e3, 2),
         "unique_payload_GBps_over_link": round(u16 / (ms16 * 1e-3) / 1e9, 2),
-        "unique_frac_of_measured": round(u16 / (ms16 * 1e-3) / 1e9 / link, 4)}
+        "unique_frac_of_measured": round(u16 / (ms16 * 1e-3) / 1e9 / link, 4),
+        "unique_line_frac_of_measured": round(l16 / (ms16 * 1e-3) / 1e9 / link, 4)}
     del out16, d16
     log(f"{key} pinned: {res}")
     return res, table
