@@ -40,7 +40,7 @@
 // ibp_device.h.  A whole (non-participating) tensor's word is its payload
 // word.  Every select is a per-lane select, with no divergent branch.
 #include "ibp_internal.h"
-#include "ibp_plan.h"
+#include "ibp_device.h"
 
 namespace ibp {
 
@@ -64,7 +64,6 @@ struct CacheArgs {
   const uint32_t* mask;
   const uint32_t* bitval;
   uint32_t* out;
-  Shape sh;
   uint32_t align;            // index mode: entry alignment (power of two)
 };
 
@@ -190,11 +189,8 @@ struct CacheGeo {
   static constexpr uint32_t TPS = (uint32_t)kWave / L;   // tensors per step
   static constexpr uint32_t kW = 4u * L;                 // words per tensor
   static constexpr uint32_t kSlot = 16u * L + 16u;       // LDS bytes per tensor + the word a window reads past
-  // LDS: kept-bit prefix (W + 1 words, padded), chunk sums, scan scratch, slots
-  static constexpr uint32_t pref = 0;
-  static constexpr uint32_t kc = ((4u * (kW + 1u)) + 15u) & ~15u;
-  static constexpr uint32_t wsum = kc + 256u;
-  static constexpr uint32_t slots = wsum + 64u;
+  // LDS: one payload slot per tensor of a step, per wave
+  static constexpr uint32_t slots = 0;
   static constexpr uint32_t bytes = slots + kCacheWaves * TPS * kSlot;
 };
 
@@ -204,53 +200,75 @@ struct CacheLds {
   uint8_t b[CacheGeo<J>::bytes];
 };
 
-// Decodes row `orow` of a packed tensor in its LDS slot (this lane's words
-// u + L q, from the windows at their kept-bit offsets) and writes the words
-// back over the slot, then stores the row 16 B per lane from the slot.  A whole
-// tensor's slot already holds its words in order.  Consecutive lanes read and
-// write consecutive LDS words (no bank conflicts), and each lane stores 16
-// contiguous bytes, so a row leaves in whole-line 16 B stores like a plain copy.
+// Decodes a packed tensor in its LDS slot (this lane's words u + L q, from
+// the windows at their kept-bit offsets) and writes the words back over the
+// slot.  A whole tensor's slot already holds its words in order.
+// Consecutive lanes read and write consecutive LDS words (no bank conflicts).
 template <int J, bool RUNS>
-__device__ __forceinline__ void decode_store(uint8_t* lds, uint32_t slot, uint32_t u,
-                                             const WordDec (&dw)[4], bool packed,
-                                             uint32_t* orow) {
+__device__ __forceinline__ void decode_in_slot(uint8_t* lds, uint32_t slot, uint32_t u,
+                                               const WordDec (&dw)[4]) {
   constexpr uint32_t L = CacheGeo<J>::L;
-  if (packed) {
-    uint32_t z[4];
+  uint32_t z[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const WordDec& d = dw[q];
-      const uint32_t d0 = *(const uint32_t*)(lds + d.ap);
-      const uint32_t d1 = *(const uint32_t*)(lds + d.ap + 4u);
-      const uint32_t p = __builtin_amdgcn_alignbit(d1, d0, d.sp);
-      z[q] = bfi_op(d.mk, d.bv, spread<RUNS>(p, d));
-    }
-    // every window of the slot has been read (LDS accesses of a wave run in
-    // order) before the words overwrite it
-#pragma unroll
-    for (int q = 0; q < 4; ++q) *(uint32_t*)(lds + slot + 4u * (u + L * q)) = z[q];
+  for (int q = 0; q < 4; ++q) {
+    const WordDec& d = dw[q];
+    const uint32_t d0 = *(const uint32_t*)(lds + d.ap);
+    const uint32_t d1 = *(const uint32_t*)(lds + d.ap + 4u);
+    const uint32_t p = __builtin_amdgcn_alignbit(d1, d0, d.sp);
+    z[q] = bfi_op(d.mk, d.bv, spread<RUNS>(p, d));
   }
-  wave_sync();
+  // every window of the slot has been read (LDS accesses of a wave run in
+  // order) before the words overwrite it
+#pragma unroll
+  for (int q = 0; q < 4; ++q) *(uint32_t*)(lds + slot + 4u * (u + L * q)) = z[q];
+}
+
+// Stores the row in its LDS slot 16 B per lane, so a row leaves in
+// whole-line 16 B streaming stores like a plain copy (one store site per
+// step: the streaming hint stays on every store).
+__device__ __forceinline__ void store_row(const uint8_t* lds, uint32_t slot, uint32_t u,
+                                          uint32_t* orow) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   const u32x4 row = *(const u32x4*)(lds + slot + 16u * u);
   __builtin_nontemporal_store(row, (u32x4*)orow);
 }
 
-// This lane's per-word decode constants (words u + L q) once the kept-bit
-// prefix is in LDS.  Returns whether the kept bits of every word form at most
-// two runs (the same answer in every lane of the wave).
+// Kept-bit prefix of this lane's words u + L q (the kept bits of all words
+// before each) and K, the kept bits of the whole Mask, from the wave's own
+// Mask words: the L lanes of a tensor hold every word once, so a scan over
+// each group of L lanes per q gives the prefixes, with no workgroup barrier.
 template <int J>
-__device__ __forceinline__ bool word_constants(WordDec (&dw)[4], const uint32_t* s_pref,
-                                               uint32_t slot, uint32_t u) {
+__device__ __forceinline__ uint32_t kept_prefix(const WordDec (&dw)[4], uint32_t u,
+                                                uint32_t (&pre)[4]) {
   constexpr uint32_t L = CacheGeo<J>::L;
+  uint32_t base = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t x = (uint32_t)__popc(~dw[q].mk);
+    uint32_t incl = x;
+#pragma unroll
+    for (uint32_t d = 1; d < L; d <<= 1) {
+      const uint32_t y = (uint32_t)__shfl_up((int)incl, d, (int)L);
+      if (u >= d) incl += y;
+    }
+    pre[q] = base + incl - x;
+    base += (uint32_t)__shfl((int)incl, (int)(L - 1u), (int)L);  // the group's total
+  }
+  return base;
+}
+
+// This lane's per-word decode constants (words u + L q) from their kept-bit
+// prefixes.  Returns whether the kept bits of every word form at most two
+// runs (the same answer in every lane of the wave).
+__device__ __forceinline__ bool word_constants(WordDec (&dw)[4], const uint32_t (&pre)[4],
+                                               uint32_t slot) {
   bool runs_ok = true;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     WordDec& d = dw[q];
-    const uint32_t pre = s_pref[u + L * q];
     d.bv &= d.mk;
-    d.ap = slot + 4u * (pre >> 5);
-    d.sp = pre & 31u;
+    d.ap = slot + 4u * (pre[q] >> 5);
+    d.sp = pre[q] & 31u;
     runs_ok = two_runs(~d.mk, d.c) && runs_ok;
   }
   const bool runs = __ballot(!runs_ok) == 0ull;
@@ -275,9 +293,6 @@ __global__ __launch_bounds__(256) void k_gather_cache(CacheArgs a) {
   static_assert(R <= (uint32_t)kWave, "one row per lane at most");
   __shared__ __align__(16) CacheLds<J> s_lds;
   uint8_t* lds = s_lds.b;
-  uint32_t* s_pref = (uint32_t*)(s_lds.b + G::pref);
-  uint32_t* s_kc = (uint32_t*)(s_lds.b + G::kc);
-  uint32_t* s_wsum = (uint32_t*)(s_lds.b + G::wsum);
   const uint32_t wave = uniform(threadIdx.x / kWave);
   const uint32_t lane = threadIdx.x % kWave;
   const uint32_t g = lane / L, u = lane % L;
@@ -285,11 +300,12 @@ __global__ __launch_bounds__(256) void k_gather_cache(CacheArgs a) {
   uint64_t row0 = ((uint64_t)blockIdx.x * kCacheWaves + wave) * R;
   const uint64_t stride = (uint64_t)gridDim.x * kCacheWaves * R;
 
+  // one round: per wave (that form has no workgroup barrier)
+  if (!LOOP && row0 >= a.n_ids) return;
+
   // this wave's ids and their entries, the Mask/Bitval words, then the
-  // kept-bit prefix (a workgroup scan)
+  // kept-bit prefix of this lane's words (a scan within the wave)
   int64_t id = row_id(a, row0 + (lane < R ? lane : R - 1u));
-  PlanRun run;
-  load_plan_run(a.mask, a.sh, run);
   WordDec dw[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -297,10 +313,14 @@ __global__ __launch_bounds__(256) void k_gather_cache(CacheArgs a) {
     dw[q].bv = ld_u32(a.bitval + u + L * q);
   }
   RowRaw rr = row_raw<INDEXED>(a, id);
-  load_plan_counts(run, a.sh, s_pref, s_kc, s_wsum);
-  if (row0 >= a.n_ids) return;  // per wave; no workgroup barrier follows
-
-  const uint32_t K = s_pref[kW];
+  uint32_t pre[4];
+  const uint32_t K = kept_prefix<J>(dw, u, pre);
+  if (LOOP) {
+    // the grid-stride form starts its waves together: without this barrier
+    // the 1M-id Zipf launches ran 6 % slower (dense_gnn, 170 against 160 us)
+    __syncthreads();
+    if (row0 >= a.n_ids) return;  // per wave; no workgroup barrier follows
+  }
   const uint32_t n16p = (K + 127u) >> 7;
   const uint64_t amask = (uint64_t)a.align - 1u;
   const uint64_t s_p = (((uint64_t)K + 7u) / 8u + amask) & ~amask;
@@ -323,7 +343,7 @@ __global__ __launch_bounds__(256) void k_gather_cache(CacheArgs a) {
     const uint64_t next = row0 + stride;
     if (LOOP) id = row_id(a, next + (lane < R ? lane : R - 1u));
     if (!planned) {
-      runs = word_constants<J>(dw, s_pref, slot, u);
+      runs = word_constants(dw, pre, slot);
       planned = true;
     }
     uint32_t* orow = a.out + (row0 + g) * kW + 4u * u;
@@ -331,12 +351,15 @@ __global__ __launch_bounds__(256) void k_gather_cache(CacheArgs a) {
     for (uint32_t d = 0; d < S; ++d) {
       *(uint4*)(lds + slot + 16u * u) = v[d];
       wave_sync();
-      if (row0 + d * TPS + g < a.n_ids) {
+      const bool in = row0 + d * TPS + g < a.n_ids;
+      if (in && pk[d] != 0u) {
         if (runs)
-          decode_store<J, true>(lds, slot, u, dw, pk[d] != 0u, orow);
+          decode_in_slot<J, true>(lds, slot, u, dw);
         else
-          decode_store<J, false>(lds, slot, u, dw, pk[d] != 0u, orow);
+          decode_in_slot<J, false>(lds, slot, u, dw);
       }
+      wave_sync();
+      if (in) store_row(lds, slot, u, orow);
       orow += TPS * kW;
       wave_sync();
     }
@@ -420,7 +443,6 @@ CacheArgs cache_args(const Geometry& g, const uint8_t* cache, uint64_t cache_byt
   a.mask = mask;
   a.bitval = bitval;
   a.out = out;
-  a.sh = Shape{g.W, g.n_c, g.wpc_log2, g.last_bits, kCacheWaves * kWave};
   a.align = 16;
   return a;
 }
