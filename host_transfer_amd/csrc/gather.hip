@@ -848,7 +848,7 @@ __device__ __forceinline__ void tile_body(GatherArgs& a, uint32_t block, uint32_
         for (int j = 0; j < J; ++j) {
           const uint32_t w = lane + kWave * j;
           const uint32_t val = tile_word<J>(a, R, j, pb32, pm, o1, o2, o3);
-          if (FULL || w < W) orow[w] = valid ? val : 0u;
+          if (FULL || w < W) store_out(orow + w, valid ? val : 0u);
         }
       }
     } else {
@@ -866,7 +866,7 @@ __device__ __forceinline__ void tile_body(GatherArgs& a, uint32_t block, uint32_
         for (int j = 0; j < J; ++j) {
           const uint32_t w = lane + kWave * j;
           const uint32_t val = tile_word<J>(a, R, j, pb32, pm, o1, o2, o3);
-          if (w < W) orow[w] = valid ? val : 0u;
+          if (w < W) store_out(orow + w, valid ? val : 0u);
         }
       }
       break;  // it is the last tile
