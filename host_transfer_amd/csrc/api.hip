@@ -651,4 +651,20 @@ int ibp_stream_read(const void* src, uint64_t bytes, uint32_t never, uint32_t* s
   return ok();
 }
 
+int ibp_stream_copy(const void* src, void* dst, uint64_t bytes, void* stream) {
+  if (!src || !dst) return fail(IBP_ERR_NULL, "ibp_stream_copy: src and dst are required");
+  if (bytes % 16 != 0) return fail(IBP_ERR_SIZE, "ibp_stream_copy: bytes must be %% 16");
+  if (!aligned(src, 16) || !aligned(dst, 16))
+    return fail(IBP_ERR_ALIGN, "ibp_stream_copy: misaligned pointer");
+  const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+  if (bytes && s0 < d0 + bytes && d0 < s0 + bytes)
+    return fail(IBP_ERR_SIZE, "ibp_stream_copy: src and dst overlap");
+  int r;
+  if ((r = require_device("ibp_stream_copy"))) return r;
+  hipError_t e = ibp::launch_stream_copy((const uint8_t*)src, (uint8_t*)dst, bytes,
+                                         (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "ibp_stream_copy");
+  return ok();
+}
+
 }  // extern "C"

@@ -102,6 +102,7 @@ hipError_t launch_raw_gather(const uint8_t* src, uint64_t row_stride, uint64_t n
                              const int64_t* ids, uint64_t n_ids, uint32_t row_bytes, uint8_t* out,
                              bool route, hipStream_t s);
 
+hipError_t launch_stream_copy(const uint8_t* src, uint8_t* dst, uint64_t bytes, hipStream_t s);
 hipError_t launch_stream_read(const uint8_t* src, uint64_t bytes, uint32_t never, uint32_t* sink,
                               hipStream_t s);
 

@@ -2,7 +2,9 @@
 //   k_raw_gather   uncompressed GPU-initiated gather of the same rows (what
 //                  the compressed gather is compared against);
 //   k_stream_read  streaming 16 B loads over a buffer (host-mapped: the rate
-//                  of GPU-initiated reads over the host link; device: HBM).
+//                  of GPU-initiated reads over the host link; device: HBM);
+//   k_stream_copy  a 16 B-per-lane copy (in HBM: the read + write rate a
+//                  gather is compared against).
 #include "ibp_internal.h"
 #include "ibp_device.h"
 
@@ -107,11 +109,8 @@ __global__ __launch_bounds__(256) void k_stream_read(const uint4* __restrict__ s
   const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
   uint32_t acc = 0;
   uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^
-           d.z ^ d.w;
-  }
+  // one load per step: four strided loads per step read HBM 12 % slower (more
+  // DRAM pages open at once) and the host link no faster
   for (; i < n16; i += stride) {
     const uint4 a = src[i];
     acc ^= a.x ^ a.y ^ a.z ^ a.w;
@@ -151,6 +150,19 @@ hipError_t launch_raw_gather(const uint8_t* src, uint64_t row_stride, uint64_t n
   return hipGetLastError();
 }
 
+// dst[i] = src[i], 16 B per lane with streaming stores: the copy rate that
+// a gather's reads and writes are compared against.
+__global__ __launch_bounds__(256) void k_stream_copy(const uint4* __restrict__ src,
+                                                      uint4* __restrict__ dst, uint64_t n16) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
+    const uint4 a = src[i];
+    const u32x4 v = {a.x, a.y, a.z, a.w};
+    __builtin_nontemporal_store(v, (u32x4*)dst + i);
+  }
+}
+
 hipError_t launch_stream_read(const uint8_t* src, uint64_t bytes, uint32_t never, uint32_t* sink,
                               hipStream_t s) {
   const uint64_t n16 = bytes / 16;
@@ -162,6 +174,21 @@ hipError_t launch_stream_read(const uint8_t* src, uint64_t bytes, uint32_t never
   const uint64_t cap = (uint64_t)di.cus * 8;
   hipLaunchKernelGGL(k_stream_read, dim3((uint32_t)(want < cap ? want : cap)), dim3(256), 0, s,
                      (const uint4*)src, n16, never, sink);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_copy(const uint8_t* src, uint8_t* dst, uint64_t bytes, hipStream_t s) {
+  const uint64_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  DeviceInfo di;
+  hipError_t e = device_info(&di);
+  if (e != hipSuccess) return e;
+  // four workgroups per CU: in HBM a copy moved 5.6 TB/s (read + write) at
+  // three or four, 4.6-4.8 at eight or sixteen (fewer rows written at once)
+  const uint64_t want = (n16 + 255) / 256;
+  const uint64_t cap = (uint64_t)di.cus * 4;
+  hipLaunchKernelGGL(k_stream_copy, dim3((uint32_t)(want < cap ? want : cap)), dim3(256), 0, s,
+                     (const uint4*)src, (uint4*)dst, n16);
   return hipGetLastError();
 }
 

@@ -67,6 +67,7 @@ _SIGS = {
     "ibp_host_free": [_vp],
     "ibp_raw_gather": [_vp, _u64, _u64, _vp, _u64, _u32, _vp, ctypes.c_uint, _vp],
     "ibp_stream_read": [_vp, _u64, _u32, _vp, _vp],
+    "ibp_stream_copy": [_vp, _vp, _u64, _vp],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -249,6 +250,10 @@ def raw_gather(src, row_stride, n_rows, ids, n_ids, row_bytes, out, flags=0, str
 
 def stream_read(src, nbytes, never, sink, stream=None):
     _check(_lib.ibp_stream_read(_ptr(src), nbytes, never, _ptr(sink), _stream(stream)))
+
+
+def stream_copy(src, dst, nbytes, stream=None):
+    _check(_lib.ibp_stream_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
 
 
 def host_alloc(nbytes, flags=HOST_DEFAULT) -> int:

@@ -422,8 +422,9 @@ int ibp_host_free(void *ptr);
 
 /* ------------------------------------------------------------ measurement
  * Baselines the pages compare against ([JH] Table 1 and Figure 5
- * discussions): an uncompressed GPU-initiated gather of the same rows, and a
- * streaming read that measures the link or HBM read rate. */
+ * discussions): an uncompressed GPU-initiated gather of the same rows, a
+ * streaming read that measures the link or HBM read rate, and a streaming
+ * copy that measures the HBM read + write rate. */
 
 /* out row r = row_bytes bytes at src + ids[r]*row_stride.  Ids outside
  * [0, n_rows) give zero rows.  src device or host-mapped; row_bytes,
@@ -446,6 +447,13 @@ int ibp_raw_gather(const void *src, uint64_t row_stride, uint64_t n_rows,
  * `never` (so the reads cannot be optimised away).  src 16 B aligned. */
 int ibp_stream_read(const void *src, uint64_t bytes, uint32_t never,
                     uint32_t *sink, void *stream);
+
+/* Copies bytes (a multiple of 16) from src to dst with 16 B loads and
+ * streaming 16 B stores spread over the whole GPU: in HBM, the read + write
+ * rate a gather's traffic is compared against.  src and dst device or
+ * host-mapped, 16 B aligned, not overlapping.  Errors: NULL pointers, bytes
+ * not a multiple of 16, alignment, overlap. */
+int ibp_stream_copy(const void *src, void *dst, uint64_t bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported(ibp):
     names = declared_functions()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     out = subprocess.run(["nm", "-D", "--defined-only", ibp.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (ibp_\w+)$", out, flags=re.M))
@@ -175,6 +175,13 @@ def test_other_validation(ibp):
     _expect(ibp, ibp.ERR_SIZE, ibp.raw_gather, P, 512, 10, P, 1 << 32, 512, P,
             ibp.RAW_ROUTE_XCD)
     _expect(ibp, ibp.ERR_SIZE, ibp.stream_read, P, 100, 0, P)
+    _expect(ibp, ibp.ERR_NULL, ibp.stream_copy, 0, P, 1024)
+    _expect(ibp, ibp.ERR_NULL, ibp.stream_copy, P, 0, 1024)
+    _expect(ibp, ibp.ERR_SIZE, ibp.stream_copy, P, P + 4096, 100)
+    _expect(ibp, ibp.ERR_ALIGN, ibp.stream_copy, P + 8, P + 4096, 1024)
+    _expect(ibp, ibp.ERR_ALIGN, ibp.stream_copy, P, P + 4104, 1024)
+    _expect(ibp, ibp.ERR_SIZE, ibp.stream_copy, P, P + 512, 1024)   # overlap
+    _expect(ibp, ibp.ERR_SIZE, ibp.stream_copy, P + 512, P, 1024)   # overlap
     with pytest.raises(ibp.IbpError) as e:
         ibp.host_alloc(1024, 7)
     assert e.value.code == ibp.ERR_FLAGS
@@ -261,6 +268,7 @@ def test_valid_call_without_a_device_reports_hip_error(ibp):
         (ibp.gather_decompress, (P, 10 * 512, 512, None, P, 10, P, 0, 512, 256, P, P, P)),
         (ibp.raw_gather, (P, 512, 10, P, 0, 512, P)),
         (ibp.stream_read, (P, 0, 0, P)),
+        (ibp.stream_copy, (P, P + 4096, 0)),
     ]
     for fn, a in calls:
         if has_device:

@@ -605,6 +605,32 @@ def test_raw_gather_and_stream_read(B, stride, shift, m, flags):
     hb.free()
 
 
+@pytest.mark.parametrize("nbytes", [0, 16, 4096, 1 << 20, (77 << 20) + 48])
+def test_stream_copy(nbytes):
+    """The copy probe copies every byte (device to device, and from pinned
+    host memory), with a ragged tail of 16 B units past whole grid strides."""
+    from host_transfer_amd import ibp
+    rng = np.random.default_rng(nbytes % 1000 + 3)
+    src_h = rng.integers(0, 256, nbytes, dtype=np.uint8)
+    G.log(f"[parity] stream copy {nbytes} B")
+    src = torch.zeros(max(nbytes, 16), dtype=torch.int8, device="cuda")
+    src[:nbytes] = torch.from_numpy(src_h.view(np.int8)).cuda()
+    dst = torch.full((nbytes + 32,), 7, dtype=torch.int8, device="cuda")
+    ibp.stream_copy(src, dst, nbytes)
+    got = G.host(dst).view(np.uint8)
+    assert (got[:nbytes] == src_h).all()
+    assert (got[nbytes:] == 7).all(), "bytes past the copy are untouched"
+    if nbytes:
+        hb = ibp.HostBuffer(nbytes)
+        hb.array[:] = src_h[::-1]
+        dst.fill_(7)
+        ibp.stream_copy(hb, dst, nbytes)
+        got = G.host(dst).view(np.uint8)
+        assert (got[:nbytes] == src_h[::-1]).all()
+        assert (got[nbytes:] == 7).all()
+        hb.free()
+
+
 # ------------------------------------------------------------ cache + store (hybrid)
 
 @pytest.mark.parametrize("key,n", [("dense_gnn", 5000), ("sparse_gnn", 1500)])
