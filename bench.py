@@ -58,15 +58,15 @@ HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E
 # transfer of known size in the same run: host-link reads
 # (TCC_EA0_RDREQ_IO_32B x 32 B, a 1 GiB zero-copy read reads as 1.000), HBM reads
 # and writes (TCC_EA0_RDREQ_DRAM_32B and TCC_EA0_WRREQ_WRITE_DRAM_32B x 32 B, a 4
-# GiB read and a 1 GiB fill read as 1.000), and FETCH_SIZE / WRITE_SIZE in KiB
+# GiB read and a 2 GiB HBM copy read as 1.000), and FETCH_SIZE / WRITE_SIZE in KiB
 # (factors 2.000 / 1.000).  Valid only for the gather code they were measured
 # on: bench.py reports them while the sources (comments and spacing aside)
 # still hash to GATHER_SOURCES_SHA256, else traffic is null.
 GATHER_SOURCES = ("host_transfer_amd/csrc/gather.hip", "host_transfer_amd/csrc/ibp_plan.h",
                   "host_transfer_amd/csrc/ibp_device.h")
 GATHER_SOURCES_SHA256 = "470bd05ffa9d23b09395737559715907ac362081fa8a67c568a0b60209e244d9"
-HEADLINE_COUNTERS = {"link_read": 10632453, "hbm_read": 1694326, "hbm_write": 49654042,
-                     "fetch_size_kib": 6191.5, "write_size_kib": 48489.9}
+HEADLINE_COUNTERS = {"link_read": 10632453, "hbm_read": 1694321, "hbm_write": 49659224,
+                     "fetch_size_kib": 6191.5, "write_size_kib": 48504.2}
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 # HBM bytes (read, written) per 1M-id cache launch, from the same runs (the
 # summary in profiles/k_gather_cache__dense_gnn_dlrm_1k_hbm.md), for the code
@@ -75,16 +75,16 @@ CACHE_SOURCES = ("host_transfer_amd/csrc/gather_cache.hip", "host_transfer_amd/c
                  "host_transfer_amd/csrc/ibp_device.h")
 CACHE_SOURCES_SHA256 = "5c308ec71d79b392e854cd4eb737040c2b075363083ed2549e5975c6759b62c9"
 HBM_COUNTERS = {
-    ("dense_gnn", "zipf"): {"index_128B": (183.85e6, 536.87e6), "index_16B": (222.36e6, 536.87e6),
-                            "table_16B": (262.50e6, 536.87e6), "raw": (179.10e6, 536.87e6)},
-    ("dense_gnn", "distinct"): {"index_128B": (577.39e6, 536.89e6),
-                                "index_16B": (685.25e6, 536.88e6),
-                                "table_16B": (794.39e6, 536.87e6), "raw": (553.66e6, 536.87e6)},
-    ("dlrm_1k", "zipf"): {"index_128B": (512.98e6, 1073.74e6), "index_16B": (513.04e6, 1073.74e6),
-                          "table_16B": (575.63e6, 1073.74e6), "raw": (542.28e6, 1073.74e6)},
-    ("dlrm_1k", "distinct"): {"index_128B": (1076.03e6, 1073.76e6),
-                              "index_16B": (1076.02e6, 1073.75e6),
-                              "table_16B": (1192.39e6, 1073.75e6), "raw": (1107.31e6, 1073.75e6)},
+    ("dense_gnn", "zipf"): {"index_128B": (184.10e6, 536.87e6), "index_16B": (222.73e6, 536.87e6),
+                            "table_16B": (262.34e6, 536.87e6), "raw": (179.09e6, 536.87e6)},
+    ("dense_gnn", "distinct"): {"index_128B": (577.23e6, 536.89e6),
+                                "index_16B": (685.07e6, 536.88e6),
+                                "table_16B": (794.24e6, 536.87e6), "raw": (553.66e6, 536.88e6)},
+    ("dlrm_1k", "zipf"): {"index_128B": (512.92e6, 1073.74e6), "index_16B": (513.02e6, 1073.74e6),
+                          "table_16B": (575.74e6, 1073.74e6), "raw": (542.20e6, 1073.74e6)},
+    ("dlrm_1k", "distinct"): {"index_128B": (1075.98e6, 1073.75e6),
+                              "index_16B": (1075.97e6, 1073.75e6),
+                              "table_16B": (1192.30e6, 1073.74e6), "raw": (1107.31e6, 1073.75e6)},
 }
 
 
