@@ -23,9 +23,11 @@
 // moves TPS = 64 / L tensors, each with L = 16 J lanes loading one 16 B unit
 // each (a plain row copy's shape).  Lane r of the wave resolves row r's entry
 // (address, 16 B units to read, packed or not), then the wave requests all S
-// payloads at once and decodes them step by step from LDS.  Lane u of a
-// tensor decodes words u + L q, q < 4, so consecutive lanes read consecutive
-// LDS words and store consecutive output words.  A batch whose waves fit one
+// payloads at once and decodes them step by step.  Lane u of a tensor owns
+// words 4u..4u+3, the 16 B it loads for a whole tensor and stores in every
+// case: a packed tensor's payload goes through an LDS slot, from which the
+// lane reads its words' windows and decodes them in registers; a whole
+// tensor's unit is already its words.  A batch whose waves fit one
 // round of resident waves takes the fewest steps per wave that fit (S = 1, 2
 // or 4; eight waves per SIMD for S <= 2); a longer batch takes S = 4 with a
 // grid-stride loop over blocks, the next block's ids requested while the
@@ -200,15 +202,11 @@ struct CacheLds {
   uint8_t b[CacheGeo<J>::bytes];
 };
 
-// Decodes a packed tensor in its LDS slot (this lane's words u + L q, from
-// the windows at their kept-bit offsets) and writes the words back over the
-// slot.  A whole tensor's slot already holds its words in order.
-// Consecutive lanes read and write consecutive LDS words (no bank conflicts).
-template <int J, bool RUNS>
-__device__ __forceinline__ void decode_in_slot(uint8_t* lds, uint32_t slot, uint32_t u,
-                                               const WordDec (&dw)[4]) {
-  constexpr uint32_t L = CacheGeo<J>::L;
-  uint32_t z[4];
+// Decodes this lane's words 4u..4u+3 of a packed tensor, from the windows at
+// their kept-bit offsets in the LDS slot, into registers.
+template <bool RUNS>
+__device__ __forceinline__ void decode_regs(const uint8_t* lds, const WordDec (&dw)[4],
+                                            uint32_t (&z)[4]) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const WordDec& d = dw[q];
@@ -217,47 +215,39 @@ __device__ __forceinline__ void decode_in_slot(uint8_t* lds, uint32_t slot, uint
     const uint32_t p = __builtin_amdgcn_alignbit(d1, d0, d.sp);
     z[q] = bfi_op(d.mk, d.bv, spread<RUNS>(p, d));
   }
-  // every window of the slot has been read (LDS accesses of a wave run in
-  // order) before the words overwrite it
-#pragma unroll
-  for (int q = 0; q < 4; ++q) *(uint32_t*)(lds + slot + 4u * (u + L * q)) = z[q];
 }
 
-// Stores the row in its LDS slot 16 B per lane, so a row leaves in
-// whole-line 16 B streaming stores like a plain copy (one store site per
-// step: the streaming hint stays on every store).
-__device__ __forceinline__ void store_row(const uint8_t* lds, uint32_t slot, uint32_t u,
-                                          uint32_t* orow) {
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 row = *(const u32x4*)(lds + slot + 16u * u);
-  __builtin_nontemporal_store(row, (u32x4*)orow);
-}
-
-// Kept-bit prefix of this lane's words u + L q (the kept bits of all words
+// Kept-bit prefix of this lane's words 4u..4u+3 (the kept bits of all words
 // before each) and K, the kept bits of the whole Mask, from the wave's own
-// Mask words: the L lanes of a tensor hold every word once, so a scan over
-// each group of L lanes per q gives the prefixes, with no workgroup barrier.
+// Mask words: the L lanes of a tensor hold every word once, so one scan of
+// the lanes' kept-bit totals over each group of L lanes gives the prefixes,
+// with no workgroup barrier.
 template <int J>
 __device__ __forceinline__ uint32_t kept_prefix(const WordDec (&dw)[4], uint32_t u,
                                                 uint32_t (&pre)[4]) {
   constexpr uint32_t L = CacheGeo<J>::L;
-  uint32_t base = 0;
+  uint32_t x[4], t = 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const uint32_t x = (uint32_t)__popc(~dw[q].mk);
-    uint32_t incl = x;
-#pragma unroll
-    for (uint32_t d = 1; d < L; d <<= 1) {
-      const uint32_t y = (uint32_t)__shfl_up((int)incl, d, (int)L);
-      if (u >= d) incl += y;
-    }
-    pre[q] = base + incl - x;
-    base += (uint32_t)__shfl((int)incl, (int)(L - 1u), (int)L);  // the group's total
+    x[q] = (uint32_t)__popc(~dw[q].mk);
+    t += x[q];
   }
-  return base;
+  uint32_t incl = t;
+#pragma unroll
+  for (uint32_t d = 1; d < L; d <<= 1) {
+    const uint32_t y = (uint32_t)__shfl_up((int)incl, d, (int)L);
+    if (u >= d) incl += y;
+  }
+  uint32_t run = incl - t;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    pre[q] = run;
+    run += x[q];
+  }
+  return (uint32_t)__shfl((int)incl, (int)(L - 1u), (int)L);
 }
 
-// This lane's per-word decode constants (words u + L q) from their kept-bit
+// This lane's per-word decode constants (words 4u..4u+3) from their kept-bit
 // prefixes.  Returns whether the kept bits of every word form at most two
 // runs (the same answer in every lane of the wave).
 __device__ __forceinline__ bool word_constants(WordDec (&dw)[4], const uint32_t (&pre)[4],
@@ -309,8 +299,8 @@ __global__ __launch_bounds__(256) void k_gather_cache(CacheArgs a) {
   WordDec dw[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    dw[q].mk = ld_u32(a.mask + u + L * q);
-    dw[q].bv = ld_u32(a.bitval + u + L * q);
+    dw[q].mk = ld_u32(a.mask + 4u * u + q);
+    dw[q].bv = ld_u32(a.bitval + 4u * u + q);
   }
   RowRaw rr = row_raw<INDEXED>(a, id);
   uint32_t pre[4];
@@ -349,19 +339,26 @@ __global__ __launch_bounds__(256) void k_gather_cache(CacheArgs a) {
     uint32_t* orow = a.out + (row0 + g) * kW + 4u * u;
 #pragma unroll
     for (uint32_t d = 0; d < S; ++d) {
-      *(uint4*)(lds + slot + 16u * u) = v[d];
+      *(uint4*)(lds + slot + 16u * u) = v[d];  // the windows of a packed payload
       wave_sync();
       const bool in = row0 + d * TPS + g < a.n_ids;
+      // a whole tensor's unit is its words 4u..4u+3; a packed one's words
+      // are decoded from the windows in the slot
+      uint32_t z[4] = {v[d].x, v[d].y, v[d].z, v[d].w};
       if (in && pk[d] != 0u) {
         if (runs)
-          decode_in_slot<J, true>(lds, slot, u, dw);
+          decode_regs<true>(lds, dw, z);
         else
-          decode_in_slot<J, false>(lds, slot, u, dw);
+          decode_regs<false>(lds, dw, z);
       }
-      wave_sync();
-      if (in) store_row(lds, slot, u, orow);
+      if (in) {
+        // one store site per step, so the streaming hint stays on every store
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 row = {z[0], z[1], z[2], z[3]};
+        __builtin_nontemporal_store(row, (u32x4*)orow);
+      }
       orow += TPS * kW;
-      wave_sync();
+      wave_sync();  // every window read before the next step's payload lands
     }
     if (!LOOP || next >= a.n_ids) break;
     row0 = next;
