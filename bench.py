@@ -65,8 +65,8 @@ HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E
 GATHER_SOURCES = ("host_transfer_amd/csrc/gather.hip", "host_transfer_amd/csrc/ibp_plan.h",
                   "host_transfer_amd/csrc/ibp_device.h")
 GATHER_SOURCES_SHA256 = "470bd05ffa9d23b09395737559715907ac362081fa8a67c568a0b60209e244d9"
-HEADLINE_COUNTERS = {"link_read": 10632453, "hbm_read": 1694305, "hbm_write": 49663110,
-                     "fetch_size_kib": 6191.5, "write_size_kib": 48486.3}
+HEADLINE_COUNTERS = {"link_read": 10632453, "hbm_read": 1694317, "hbm_write": 49649810,
+                     "fetch_size_kib": 6191.5, "write_size_kib": 48511.6}
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 # HBM bytes (read, written) per 1M-id cache launch, from the same runs (the
 # summary in profiles/k_gather_cache__dense_gnn_dlrm_1k_hbm.md), for the code
@@ -75,14 +75,14 @@ CACHE_SOURCES = ("host_transfer_amd/csrc/gather_cache.hip", "host_transfer_amd/c
                  "host_transfer_amd/csrc/ibp_device.h")
 CACHE_SOURCES_SHA256 = "b685aa934fc992145b138a565a900cad876ad4772c99020426b89da4a5ac9a92"
 HBM_COUNTERS = {
-    ("dense_gnn", "zipf"): {"index_128B": (184.20e6, 536.87e6), "index_16B": (222.99e6, 536.87e6),
-                            "table_16B": (262.44e6, 536.87e6), "raw": (179.07e6, 536.87e6)},
+    ("dense_gnn", "zipf"): {"index_128B": (184.20e6, 536.87e6), "index_16B": (222.95e6, 536.87e6),
+                            "table_16B": (262.47e6, 536.87e6), "raw": (179.09e6, 536.87e6)},
     ("dense_gnn", "distinct"): {"index_128B": (577.12e6, 536.87e6),
-                                "index_16B": (684.96e6, 536.87e6),
-                                "table_16B": (794.25e6, 536.87e6), "raw": (553.66e6, 536.88e6)},
-    ("dlrm_1k", "zipf"): {"index_128B": (512.91e6, 1073.74e6), "index_16B": (513.04e6, 1073.74e6),
-                          "table_16B": (575.50e6, 1073.74e6), "raw": (542.21e6, 1073.74e6)},
-    ("dlrm_1k", "distinct"): {"index_128B": (1075.98e6, 1073.75e6),
+                                "index_16B": (684.97e6, 536.87e6),
+                                "table_16B": (794.26e6, 536.87e6), "raw": (553.66e6, 536.88e6)},
+    ("dlrm_1k", "zipf"): {"index_128B": (512.94e6, 1073.74e6), "index_16B": (512.96e6, 1073.74e6),
+                          "table_16B": (575.51e6, 1073.74e6), "raw": (542.20e6, 1073.74e6)},
+    ("dlrm_1k", "distinct"): {"index_128B": (1075.99e6, 1073.75e6),
                               "index_16B": (1075.99e6, 1073.75e6),
                               "table_16B": (1192.33e6, 1073.74e6), "raw": (1107.31e6, 1073.75e6)},
 }
