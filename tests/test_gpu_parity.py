@@ -408,6 +408,50 @@ def test_side_stream_and_graph_replay():
             del graph
 
 
+def test_two_streams_at_once():
+    """Gathers of different batches launched alternately on two streams, so
+    that consecutive launches run at the same time (the library keeps no
+    state a launch writes): group and tile kernels from pinned slots, and the
+    indexed cache gather; every output checked against the original rows."""
+    from host_transfer_amd import ibp
+    rng = np.random.default_rng(23)
+    for key, n in (("sparse_gnn", 1500), ("dense_gnn", 3000)):
+        w = W.WORKLOADS[key].scaled(n)
+        rows = W.rows(w)
+        B, C, slot = w.tensor_bytes, w.chunk_bytes, w.slot_bytes
+        G.log(f"[parity] two streams at once: {key}")
+        mask, bitval = G.check_metadata(rows, w.threshold)
+        store, part, lens = G.gpu_compress(rows, mask, bitval, C, slot, pinned=True)
+        d_mask, d_bitval = G.dev(mask), G.dev(bitval)
+        launches = [("slots", lambda ids, nb, dst: ibp.gather_decompress(
+            store, n * slot, slot, None, part, n, ids, nb, B, C, d_mask, d_bitval, dst))]
+        if C >= B:  # one-chunk tensors: also the indexed cache
+            offsets = torch.zeros(n + 1, dtype=torch.int64, device="cuda")
+            ibp.compact_offsets_aligned(lens, n, 128, offsets)
+            total = int(offsets[-1].item())
+            cache = torch.zeros(max(total, 16), dtype=torch.uint8, device="cuda")
+            ibp.cache_fill(store, slot, lens, n, offsets, cache, total)
+            index = torch.zeros((n + 31) // 32, dtype=torch.int64, device="cuda")
+            ibp.cache_index(part, n, index)
+            launches.append(("indexed cache", lambda ids, nb, dst: ibp.gather_decompress_indexed(
+                cache, total, 128, index, n, ids, nb, B, C, d_mask, d_bitval, dst)))
+        streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+        for name, launch in launches:
+            nb = 4096
+            batches = [rng.integers(-1, n + 1, nb) for _ in range(8)]
+            d_ids = [torch.from_numpy(b).cuda() for b in batches]
+            outs = [torch.full((nb * B,), 0x5A, dtype=torch.uint8, device="cuda") for _ in range(8)]
+            torch.cuda.synchronize()
+            for k in range(8):
+                with torch.cuda.stream(streams[k % 2]):
+                    launch(d_ids[k], nb, outs[k])
+            torch.cuda.synchronize()
+            for k in range(8):
+                got = G.host(outs[k]).reshape(nb, B)
+                assert (got == G.expected_rows(rows, batches[k])).all(), (key, name, k)
+        store.free()
+
+
 def _segment_case(rows, masks, bitvals, parts, B, C, S, n, rng, mode, per_seg=300, flags=0,
                   hot=0):
     """One segmented gather over `parts` = [(first, count) of the tensors
